@@ -1,0 +1,139 @@
+/*
+ * ssd.h -- C ABI of libssd.so, the MI355X (gfx950) SSD chunked-scan library.
+ *
+ * The operation is the selective state-space recurrence evaluated chunk-wise
+ * ("Structured State Space Duality" concept page, sections "The recurrence as
+ * one matrix" and "The chunked algorithm takes both"):
+ *
+ *     h_t = a_t * h_{t-1} + x_t B_t^T        (per head: state P x N)
+ *     y_t = h_t C_t + D_h * x_t
+ *
+ * with a scalar decay per head and token, a_t = exp(dt_t * A_h), or -- for the
+ * diagonal variant ("What the duality gives up" on the same page; "Diagonal
+ * Equivalence in State Space Models", abstract) -- one decay per state
+ * dimension, a_{t,n} = exp(dt_t * A_{h,n}).  h0 is the state before token 0; the
+ * final state h_T is the state after the last token.  The sequence is split into
+ * chunks of `chunk` tokens: a masked matmul on each diagonal block, and one state
+ * step per chunk across blocks; the result does not depend on the chunk size
+ * beyond floating-point rounding.
+ *
+ * Layouts (row-major, contiguous, no strides):
+ *     x, y   [batch, seqlen, nheads, headdim]        dtype of the problem
+ *     dt     [batch, seqlen, nheads]                 float32
+ *     A      [nheads] (scalar) / [nheads, dstate]    float32
+ *     B, C   [batch, seqlen, ngroups, dstate]        dtype of the problem
+ *     D      [nheads]                                float32 (may be NULL = 0)
+ *     h0, hT [batch, nheads, headdim, dstate]        float32 (h0 NULL = 0; hT NULL = not written)
+ * Head h reads B/C group floor(h * ngroups / nheads) (contiguous blocks of heads).
+ *
+ * Precision: decay sums, exponentials and states are float32; x, B, C (and the
+ * masked scores and entering states fed to the matrix cores) are in the problem
+ * dtype; accumulation is float32; y is rounded once to the problem dtype.
+ * Accuracy is stated for A <= 0 (decays in (0, 1]); NaN inputs propagate.
+ *
+ * Ownership and ordering: every pointer is a device pointer owned by the caller.
+ * The library allocates nothing and keeps no global mutable state; calls are
+ * thread-safe.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without synchronising: inputs and the workspace
+ * must stay alive until the stream has passed this work.  Outputs must not
+ * overlap any input or the workspace.  Two calls that share a workspace must be
+ * ordered on one stream.
+ *
+ * Errors: every entry point validates on the host, before any HIP call, and
+ * returns an ssd_status; nothing is enqueued on failure.  SSD_ERR_HIP reports a
+ * launch failure (hipGetLastError after enqueueing).
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_VERSION 100 /* 1.0.0 */
+
+typedef enum {
+    SSD_F32 = 0,  /* x, B, C, y are float32 */
+    SSD_BF16 = 1  /* x, B, C, y are bfloat16 */
+} ssd_dtype;
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = 2,       /* a dimension is negative/zero where it must not be, or nheads % ngroups != 0 */
+    SSD_ERR_UNSUPPORTED = 3, /* chunk, headdim, dstate or dtype outside the supported set */
+    SSD_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than ssd_workspace_bytes() */
+    SSD_ERR_ALIGN = 5,       /* x/B/C/y/h0/hT not 16-byte aligned, dt/A/D not 4-byte, workspace not 256-byte */
+    SSD_ERR_ALIAS = 6,       /* y or hT overlaps an input, the other output or the workspace */
+    SSD_ERR_HIP = 7          /* a kernel launch failed */
+} ssd_status;
+
+/* Problem descriptor.  Supported: chunk in {64, 128, 256}; headdim in {16, 32, 64, 128};
+ * dstate in {16, 32, 64, 128, 256}; any seqlen >= 0 (a ragged last chunk is allowed);
+ * batch >= 0; nheads >= 1; ngroups >= 1 dividing nheads. */
+typedef struct {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+    int32_t dtype;  /* ssd_dtype */
+    int32_t flags;  /* 0 = the whole forward; see SSD_STAGE_* */
+} ssd_problem;
+
+/* Diagnostics only (per-kernel timing and per-stage inspection).  A nonzero `flags`
+ * is a mask of the kernels to enqueue; the others are skipped and their results are
+ * read from the workspace, which a previous call with flags = 0 on the same problem,
+ * inputs and workspace must have filled.  Any other bit is SSD_ERR_UNSUPPORTED. */
+#define SSD_STAGE_CUMSUM 0x01 /* chunk-local cumulative sum of dt      -> ws cdt     */
+#define SSD_STAGE_CB 0x02     /* C_c B_c^T per chunk (scalar decay)    -> ws cb      */
+#define SSD_STAGE_STATE 0x04  /* chunk states S_c                      -> ws states  */
+#define SSD_STAGE_SCAN 0x08   /* inter-chunk state scan                -> ws hin, hT */
+#define SSD_STAGE_OUT 0x10    /* diagonal blocks + state output + D    -> y          */
+#define SSD_STAGE_ALL 0x1f
+
+/* Bytes of device workspace that ssd_scan_fwd (diag = 0) or ssd_diag_scan_fwd
+ * (diag = 1) needs for this problem; 0 if the problem is invalid or empty.
+ * Pure host function. */
+size_t ssd_workspace_bytes(const ssd_problem* p, int diag);
+
+/* Where each intermediate lives inside the workspace (byte offsets, each 256-aligned;
+ * a size of 0 means "absent"), for inspection after a call has completed:
+ *   cdt  float32 [batch, nheads, nchunks, chunk]  chunk-local cumulative sum of dt
+ *        (positions past seqlen repeat the chunk total)
+ *   cb   dtype   [batch, nchunks, ngroups, chunk, chunk]  C_c B_c^T, blocks on and below
+ *        the diagonal (scalar decay only)
+ *   states float32 [batch, nheads, nchunks, headdim, dstate]  chunk states S_c
+ *   hin  dtype   [batch, nheads, nchunks, headdim, dstate]  state entering chunk c
+ * Returns an ssd_status.  Pure host function. */
+typedef struct {
+    size_t cdt_off, cdt_bytes;
+    size_t cb_off, cb_bytes;
+    size_t states_off, states_bytes;
+    size_t hin_off, hin_bytes;
+    size_t total_bytes;
+} ssd_workspace_layout;
+int ssd_get_workspace_layout(const ssd_problem* p, int diag, ssd_workspace_layout* out);
+
+/* Scalar-decay SSD forward: A is [nheads].  Writes y (and hT if non-NULL).
+ * `ws` must hold ssd_workspace_bytes(p, 0) bytes. */
+int ssd_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const float* A,
+                 const void* B, const void* C, const float* D, const float* h0,
+                 void* y, float* hT, void* ws, size_t ws_bytes, void* stream);
+
+/* Diagonal-decay SSD forward: A is [nheads, dstate].  Same conventions;
+ * `ws` must hold ssd_workspace_bytes(p, 1) bytes. */
+int ssd_diag_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const float* A,
+                      const void* B, const void* C, const float* D, const float* h0,
+                      void* y, float* hT, void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* ssd_status_string(int status);
+
+/* SSD_VERSION of the built library. */
+int ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

@@ -1,0 +1,171 @@
+"""MI355X-native SSD chunked scan (the Mamba-2 core layer), forward pass.
+
+Thin Python binding over ``libssd.so`` (C ABI in ``include/ssd.h``): argument
+marshalling only -- every step of the scan runs in the library's HIP kernels.
+PyTorch supplies device memory and the stream.  If the library is missing or fails
+to load, every call raises: there is no fallback path.
+
+    y, hT = scan_fwd(x, dt, A, B, C, D=None, h0=None, chunk=256)
+    y, hT = diag_scan_fwd(x, dt, A, B, C, D=None, h0=None, chunk=128)
+
+Layouts: x [b,T,H,P]; dt [b,T,H] f32; A [H] (scalar decay) or [H,N] (diagonal
+decay) f32; B, C [b,T,G,N]; D [H] f32; h0 [b,H,P,N] f32.  x/B/C share one dtype,
+bfloat16 or float32; y has that dtype, hT is float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["scan_fwd", "diag_scan_fwd", "scan_fwd_into", "Problem", "workspace_bytes",
+           "workspace_layout", "status_string", "version", "library_path", "SSDError"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libssd.so")
+_lib = None
+
+SSD_F32, SSD_BF16 = 0, 1
+STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
+          4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_ALIGN", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_HIP"}
+EXPORTS = ("ssd_workspace_bytes", "ssd_get_workspace_layout", "ssd_scan_fwd", "ssd_diag_scan_fwd",
+           "ssd_status_string", "ssd_version")
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("cdt_off", "cdt_bytes", "cb_off", "cb_bytes", "states_off", "states_bytes",
+                 "hin_off", "hin_bytes", "total_bytes")]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"libssd.so not built ({_LIB_PATH}); run `python -m ssd_chunked_scan_03_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp, fp, sz, ci = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.ssd_workspace_bytes.argtypes = [P, ci]
+    lib.ssd_workspace_bytes.restype = sz
+    lib.ssd_get_workspace_layout.argtypes = [P, ci, ctypes.POINTER(WorkspaceLayout)]
+    lib.ssd_get_workspace_layout.restype = ci
+    for f in (lib.ssd_scan_fwd, lib.ssd_diag_scan_fwd):
+        f.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp]
+        f.restype = ci
+    lib.ssd_status_string.argtypes = [ci]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_version.argtypes = []
+    lib.ssd_version.restype = ci
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return _load().ssd_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(_load().ssd_version())
+
+
+STAGE_CUMSUM, STAGE_CB, STAGE_STATE, STAGE_SCAN, STAGE_OUT = 0x01, 0x02, 0x04, 0x08, 0x10
+STAGES = {"k_cumsum": STAGE_CUMSUM, "k_cb": STAGE_CB, "k_state": STAGE_STATE, "k_scan": STAGE_SCAN,
+          "k_out": STAGE_OUT}
+
+
+def make_problem(b, T, H, P, N, G, chunk, dtype, flags=0) -> Problem:
+    """flags = 0 runs the whole forward; a mask of STAGE_* bits runs only those kernels
+    (diagnostics: earlier stages are read from a workspace a full call filled)."""
+    return Problem(int(b), int(T), int(H), int(P), int(N), int(G), int(chunk), int(dtype), int(flags))
+
+
+def workspace_bytes(prob: Problem, diag: bool = False) -> int:
+    return int(_load().ssd_workspace_bytes(ctypes.byref(prob), int(bool(diag))))
+
+
+def workspace_layout(prob: Problem, diag: bool = False) -> dict:
+    lay = WorkspaceLayout()
+    st = _load().ssd_get_workspace_layout(ctypes.byref(prob), int(bool(diag)), ctypes.byref(lay))
+    if st:
+        raise SSDError(st, "ssd_get_workspace_layout")
+    return {n: int(getattr(lay, n)) for n, _ in WorkspaceLayout._fields_}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def scan_fwd_into(prob: Problem, diag: bool, x, dt, A, B, C, D, h0, y, hT, ws, stream=None) -> None:
+    """Enqueue one forward into caller-provided outputs and workspace (no allocation)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    lib = _load()
+    fn = lib.ssd_diag_scan_fwd if diag else lib.ssd_scan_fwd
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = fn(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+            _ptr(y), _ptr(hT), _ptr(ws), nbytes, ctypes.c_void_p(int(stream)))
+    if st:
+        raise SSDError(st, "ssd_diag_scan_fwd" if diag else "ssd_scan_fwd")
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    if t.dtype == torch.float32:
+        return SSD_F32
+    raise TypeError(f"x/B/C must be bfloat16 or float32, got {t.dtype}")
+
+
+def _forward(diag, x, dt, A, B, C, D, h0, chunk, return_final_state, ws):
+    import torch
+    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D), ("h0", h0)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if not (x.dtype == B.dtype == C.dtype):
+        raise TypeError("x, B and C must share one dtype")
+    for name, t in (("dt", dt), ("A", A), ("D", D), ("h0", h0)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if B.shape != (b, T, G, N) or C.shape != B.shape or dt.shape != (b, T, H):
+        raise ValueError("shape mismatch among x, dt, B, C")
+    if A.shape != ((H, N) if diag else (H,)):
+        raise ValueError(f"A must be {'[H, N]' if diag else '[H]'}")
+    prob = make_problem(b, T, H, P, N, G, chunk, _dtype_code(x))
+    y = torch.empty_like(x)
+    hT = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device) if return_final_state else None
+    need = workspace_bytes(prob, diag)
+    if ws is None or ws.numel() * ws.element_size() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    scan_fwd_into(prob, diag, x, dt, A, B, C, D, h0, y, hT, ws)
+    return y, hT
+
+
+def scan_fwd(x, dt, A, B, C, D=None, h0=None, chunk=256, return_final_state=True, workspace=None):
+    """Scalar-decay SSD forward (a_t = exp(dt_t A_h)). Returns (y, hT)."""
+    return _forward(False, x, dt, A, B, C, D, h0, chunk, return_final_state, workspace)
+
+
+def diag_scan_fwd(x, dt, A, B, C, D=None, h0=None, chunk=128, return_final_state=True, workspace=None):
+    """Diagonal-decay SSD forward (a_{t,n} = exp(dt_t A_{h,n})). Returns (y, hT)."""
+    return _forward(True, x, dt, A, B, C, D, h0, chunk, return_final_state, workspace)

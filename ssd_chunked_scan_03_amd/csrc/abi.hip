@@ -1,0 +1,187 @@
+// abi.hip -- the C ABI of libssd.so (declared in include/ssd.h): host-side
+// validation, workspace layout and launch sequencing.  No allocation, no global
+// mutable state; every check happens before the first HIP call.
+#include <string.h>
+
+#include "launch.hpp"
+#include "ssd.h"
+
+namespace {
+
+// hT = h0 (or 0) for an empty sequence: a fill kernel, not a memset, so that the
+// call stays safe under stream capture.
+__global__ void k_copy_state(const float* __restrict__ h0, float* __restrict__ hT, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) hT[i] = h0 ? h0[i] : 0.f;
+}
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool pn_supported(int64_t P, int64_t N) {
+    const bool p = P == 16 || P == 32 || P == 64 || P == 128;
+    const bool n = N == 16 || N == 32 || N == 64 || N == 128 || N == 256;
+    return p && n;
+}
+
+size_t esize(int32_t dtype) { return dtype == SSD_BF16 ? 2 : 4; }
+
+// Shape checks shared by every entry point.
+int check_problem(const ssd_problem* p) {
+    if (!p) return SSD_ERR_NULL;
+    if (p->batch < 0 || p->seqlen < 0 || p->nheads <= 0 || p->headdim <= 0 || p->dstate <= 0 ||
+        p->ngroups <= 0 || p->chunk <= 0)
+        return SSD_ERR_SHAPE;
+    if (p->nheads % p->ngroups != 0) return SSD_ERR_SHAPE;
+    if (p->dtype != SSD_F32 && p->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (p->chunk != 64 && p->chunk != 128 && p->chunk != 256) return SSD_ERR_UNSUPPORTED;
+    if (!pn_supported(p->headdim, p->dstate)) return SSD_ERR_UNSUPPORTED;
+    if (p->flags & ~SSD_STAGE_ALL) return SSD_ERR_UNSUPPORTED;
+    // launch-grid limits: blocks per launch and the batch / group grid dimensions
+    const int64_t nc = (p->seqlen + p->chunk - 1) / p->chunk;
+    if (p->batch > 65535 || p->batch * p->ngroups > 65535) return SSD_ERR_UNSUPPORTED;
+    if (p->nheads > (int64_t)1 << 20 || nc > (int64_t)1 << 24) return SSD_ERR_UNSUPPORTED;
+    if (p->batch * p->nheads * (nc > 0 ? nc : 1) > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+ssd_workspace_layout layout_of(const ssd_problem* p, int diag) {
+    ssd_workspace_layout L;
+    memset(&L, 0, sizeof(L));
+    const int64_t nc = (p->seqlen + p->chunk - 1) / p->chunk;
+    const size_t bhc = (size_t)(p->batch * p->nheads * nc);
+    const size_t es = esize(p->dtype);
+    size_t off = 0;
+    L.cdt_off = off;
+    L.cdt_bytes = bhc * (size_t)p->chunk * 4;
+    off += align_up(L.cdt_bytes);
+    L.cb_off = off;
+    L.cb_bytes = diag ? 0 : (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->chunk * p->chunk) * es;
+    off += align_up(L.cb_bytes);
+    L.states_off = off;
+    L.states_bytes = bhc * (size_t)(p->headdim * p->dstate) * 4;
+    off += align_up(L.states_bytes);
+    L.hin_off = off;
+    L.hin_bytes = bhc * (size_t)(p->headdim * p->dstate) * es;
+    off += align_up(L.hin_bytes);
+    L.total_bytes = (p->batch == 0 || p->seqlen == 0) ? 0 : off;
+    return L;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+struct Range {
+    const void* p;
+    size_t n;
+};
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const float* A,
+         const void* B, const void* C, const float* D, const float* h0, void* y, float* hT,
+         void* ws, size_t ws_bytes, void* stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    const int64_t b = p->batch, T = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate,
+                  G = p->ngroups, Q = p->chunk;
+    const size_t es = esize(p->dtype);
+    const size_t state_bytes = (size_t)(b * H * P * N) * 4;
+    if (b == 0) return SSD_OK;
+    if (!A) return SSD_ERR_NULL;
+    if (!aligned(A, 4) || (D && !aligned(D, 4)) || (h0 && !aligned(h0, 16)) || (hT && !aligned(hT, 16)))
+        return SSD_ERR_ALIGN;
+    if (T == 0) {
+        // empty sequence: hT = h0 (or 0); y is empty
+        if (!hT) return SSD_OK;
+        if (overlap({hT, state_bytes}, {h0, state_bytes})) return SSD_ERR_ALIAS;
+        const int64_t n = b * H * P * N;
+        k_copy_state<<<(unsigned)((n + 255) / 256), 256, 0, (hipStream_t)stream>>>(h0, hT, n);
+        return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    }
+    if (!x || !dt || !B || !C || !y) return SSD_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(dt, 4))
+        return SSD_ERR_ALIGN;
+    const ssd_workspace_layout L = layout_of(p, diag);
+    if (!ws || ws_bytes < L.total_bytes) return SSD_ERR_WORKSPACE;
+    if (!aligned(ws, kAlign)) return SSD_ERR_ALIGN;
+
+    const size_t xb = (size_t)(b * T * H * P) * es;
+    const Range ins[] = {{x, xb},
+                         {dt, (size_t)(b * T * H) * 4},
+                         {A, (size_t)(diag ? H * N : H) * 4},
+                         {B, (size_t)(b * T * G * N) * es},
+                         {C, (size_t)(b * T * G * N) * es},
+                         {D, D ? (size_t)H * 4 : 0},
+                         {h0, h0 ? state_bytes : 0},
+                         {ws, L.total_bytes}};
+    const Range ry = {y, xb}, rh = {hT, hT ? state_bytes : 0};
+    for (const Range& r : ins)
+        if (overlap(ry, r) || overlap(rh, r)) return SSD_ERR_ALIAS;
+    if (overlap(ry, rh)) return SSD_ERR_ALIAS;
+
+    ssd::RunArgs a;
+    a.b = b; a.T = T; a.H = H; a.P = P; a.N = N; a.G = G; a.Q = Q;
+    a.nc = (T + Q - 1) / Q;
+    a.diag = diag;
+    a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.h0 = h0;
+    a.y = y; a.hT = hT;
+    char* w = static_cast<char*>(ws);
+    a.cdt = reinterpret_cast<float*>(w + L.cdt_off);
+    a.cb = diag ? nullptr : static_cast<void*>(w + L.cb_off);
+    a.states = reinterpret_cast<float*>(w + L.states_off);
+    a.hin = static_cast<void*>(w + L.hin_off);
+    a.stream = (hipStream_t)stream;
+    a.stages = p->flags ? p->flags : SSD_STAGE_ALL;
+    return p->dtype == SSD_BF16 ? ssd::run_bf16(a) : ssd::run_f32(a);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_workspace_bytes(const ssd_problem* p, int diag) {
+    if (check_problem(p)) return 0;
+    return layout_of(p, diag ? 1 : 0).total_bytes;
+}
+
+int ssd_get_workspace_layout(const ssd_problem* p, int diag, ssd_workspace_layout* out) {
+    if (!out) return SSD_ERR_NULL;
+    const int st = check_problem(p);
+    if (st) return st;
+    *out = layout_of(p, diag ? 1 : 0);
+    return SSD_OK;
+}
+
+int ssd_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const float* A,
+                 const void* B, const void* C, const float* D, const float* h0, void* y,
+                 float* hT, void* ws, size_t ws_bytes, void* stream) {
+    return scan(p, 0, x, dt, A, B, C, D, h0, y, hT, ws, ws_bytes, stream);
+}
+
+int ssd_diag_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const float* A,
+                      const void* B, const void* C, const float* D, const float* h0, void* y,
+                      float* hT, void* ws, size_t ws_bytes, void* stream) {
+    return scan(p, 1, x, dt, A, B, C, D, h0, y, hT, ws, ws_bytes, stream);
+}
+
+const char* ssd_status_string(int status) {
+    switch (status) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL: return "a required pointer is NULL";
+        case SSD_ERR_SHAPE: return "invalid shape (negative/zero dimension or nheads % ngroups != 0)";
+        case SSD_ERR_UNSUPPORTED: return "unsupported chunk, headdim, dstate, dtype, flags or size";
+        case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+        case SSD_ERR_ALIGN: return "pointer misaligned (16 B for tensors, 4 B for dt/A/D, 256 B for workspace)";
+        case SSD_ERR_ALIAS: return "an output overlaps an input, the workspace or the other output";
+        case SSD_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int ssd_version(void) { return SSD_VERSION; }
+
+}  // extern "C"

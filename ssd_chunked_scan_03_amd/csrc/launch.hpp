@@ -1,0 +1,91 @@
+// launch.hpp -- enqueue the kernel sequence of one SSD forward on a stream.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace ssd {
+
+// Everything one launch sequence needs; validated by the C ABI beforehand.
+struct RunArgs {
+    int64_t b, T, H, P, N, G, Q, nc;
+    int diag;
+    const void* x;
+    const float* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* h0;
+    void* y;
+    float* hT;
+    float* cdt;     // [b,H,nc,Q]
+    void* cb;       // [b,nc,G,Q,Q]  (scalar decay only)
+    float* states;  // [b,H,nc,P,N]
+    void* hin;      // [b,H,nc,P,N]
+    hipStream_t stream;
+    int stages;     // mask of kernels to enqueue (1 cumsum, 2 cb, 4 state, 8 scan, 16 out)
+};
+
+template <typename T, int P, int N>
+int run(const RunArgs& a) {
+    const int Q = (int)a.Q, nc = (int)a.nc, H = (int)a.H, G = (int)a.G;
+    hipStream_t s = a.stream;
+    const T* x = static_cast<const T*>(a.x);
+    const T* Bm = static_cast<const T*>(a.B);
+    const T* Cm = static_cast<const T*>(a.C);
+    T* cb = static_cast<T*>(a.cb);
+    T* hin = static_cast<T*>(a.hin);
+    T* y = static_cast<T*>(a.y);
+
+    // the output kernel's LDS must fit one CU (160 KiB); checked before any launch
+    const size_t smem = a.diag ? OutSmem<T, P, N, true>::bytes(Q) : OutSmem<T, P, N, false>::bytes(Q);
+    if (smem > 160 * 1024) return 3;
+
+    const dim3 g1(nc, (unsigned)a.b, (H + 15) / 16);
+    if (a.stages & 1) switch (Q) {
+        case 64: k_cumsum<64><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, a.T, H, nc); break;
+        case 128: k_cumsum<128><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, a.T, H, nc); break;
+        case 256: k_cumsum<256><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, a.T, H, nc); break;
+        default: return 3;
+    }
+    if (!a.diag && (a.stages & 2)) {
+        const int nb = Q / 64;
+        const dim3 g2(nb * (nb + 1) / 2, nc, (unsigned)(a.b * G));
+        k_cb<T, N><<<g2, kThreads, 0, s>>>(Bm, Cm, cb, a.T, G, Q, nc);
+    }
+    const dim3 g3((unsigned)(a.b * H * nc));
+    if (!(a.stages & 4)) {
+    } else if (a.diag)
+        k_state<T, P, N, true><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
+    else
+        k_state<T, P, N, false><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
+
+    const int per_head = (P * N / 4 + kThreads - 1) / kThreads;
+    const dim3 g4((unsigned)(a.b * H * per_head));
+    if (!(a.stages & 8)) {
+    } else if (a.diag)
+        k_scan<T, true><<<g4, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, H, P * N, N, Q, nc, per_head);
+    else
+        k_scan<T, false><<<g4, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, H, P * N, N, Q, nc, per_head);
+
+    if (!(a.stages & 16)) {
+    } else if (a.diag) {
+        hipFuncSetAttribute((const void*)k_out<T, P, N, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        k_out<T, P, N, true><<<g3, kThreads, smem, s>>>(x, Bm, Cm, nullptr, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);
+    } else {
+        hipFuncSetAttribute((const void*)k_out<T, P, N, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        k_out<T, P, N, false><<<g3, kThreads, smem, s>>>(x, Bm, Cm, cb, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+int run_bf16(const RunArgs& a);
+int run_f32(const RunArgs& a);
+
+// The (headdim, dstate) pairs with compiled kernels.
+#define SSD_FOR_EACH_PN(X)                                                              \
+    X(16, 16) X(16, 32) X(16, 64) X(16, 128) X(16, 256) X(32, 16) X(32, 32) X(32, 64)   \
+    X(32, 128) X(32, 256) X(64, 16) X(64, 32) X(64, 64) X(64, 128) X(64, 256)           \
+    X(128, 16) X(128, 32) X(128, 64) X(128, 128) X(128, 256)
+
+}  // namespace ssd

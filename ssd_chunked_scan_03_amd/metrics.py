@@ -1,0 +1,62 @@
+"""Algorithmic work of one SSD forward: matrix-core flops and minimal HBM bytes.
+
+Flops use the causal convention: a Q x Q block product counts only the L(L+1)/2
+entries on or below the diagonal (L = tokens in the chunk); C B^T counts once per
+(batch, group, chunk) for the scalar decay and once per (batch, head, chunk) for the
+diagonal decay (it is formed per head there); the chunk-state and state-output
+contractions count 2 L P N each.  Exponentials, masks, the state scan and the skip
+term are not counted.
+
+Bytes are per kernel of the split schedule, each operand that kernel must touch
+counted once (es = bytes of the x/B/C dtype):
+  k_cumsum  dt read + cdt write
+  k_cb      B + C read + C B^T blocks (64 x 64, on/below the diagonal) write
+  k_state   x + B + cdt read + fp32 chunk states write
+  k_scan    fp32 chunk states + chunk-end cdt + h0 read, entering states (es) + hT write
+  k_out     x + C + cdt + C B^T blocks + entering states read, y write
+The path minimum is x + y + B + C + dt + h0 + hT, each touched once.
+"""
+from __future__ import annotations
+
+
+def _chunks(T, Q):
+    full, rem = divmod(T, Q)
+    return [Q] * full + ([rem] if rem else [])
+
+
+def flops(b, T, H, P, N, G, Q, diag=False) -> dict:
+    tri = sum(L * (L + 1) // 2 for L in _chunks(T, Q))
+    tok = T
+    out = {
+        "diag_block": b * H * tri * 2 * P,
+        "cb": b * (H if diag else G) * tri * 2 * N,
+        "chunk_state": b * H * tok * 2 * P * N,
+        "state_output": b * H * tok * 2 * P * N,
+    }
+    out["total"] = sum(out.values())
+    return out
+
+
+def kernel_bytes(b, T, H, P, N, G, Q, es, diag=False, h0=True) -> dict:
+    nc = -(-T // Q)
+    nb = Q // 64
+    x = b * T * H * P * es
+    bc = b * T * G * N * es
+    dt = b * T * H * 4
+    cdt = b * H * nc * Q * 4
+    cbb = 0 if diag else b * nc * G * (nb * (nb + 1) // 2) * 64 * 64 * es
+    st32 = b * H * nc * P * N * 4
+    stx = b * H * nc * P * N * es
+    hstate = b * H * P * N * 4
+    return {
+        "k_cumsum": dt + cdt,
+        "k_cb": 0 if diag else 2 * bc + cbb,
+        "k_state": x + bc + cdt + st32,
+        "k_scan": st32 + b * H * nc * 4 + (hstate if h0 else 0) + stx + hstate,
+        "k_out": x + bc * (2 if diag else 1) + cdt + cbb + stx + x,
+    }
+
+
+def path_min_bytes(b, T, H, P, N, G, es, h0=True) -> int:
+    return 2 * b * T * H * P * es + 2 * b * T * G * N * es + b * T * H * 4 + \
+        (2 if h0 else 1) * b * H * P * N * 4
