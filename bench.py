@@ -27,7 +27,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, published
 FP32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix cores, published
 KERNEL_SOURCES = ["ssd_chunked_scan_03_amd/csrc/kernels.hpp", "ssd_chunked_scan_03_amd/csrc/device.hpp",
-                  "ssd_chunked_scan_03_amd/csrc/launch.hpp"]
+                  "ssd_chunked_scan_03_amd/csrc/fused.hpp", "ssd_chunked_scan_03_amd/csrc/launch.hpp"]
 
 
 def kernel_source_hash() -> str:
@@ -148,7 +148,10 @@ def main():
     kb = metrics.kernel_bytes(b, T, H, P, N, G, Q, 2 if w.dtype == "bf16" else 4, w.diag, h0 is not None)
     ksteps = args.kernel_steps or max(10, args.steps)
     kernels = {}
-    for name, bit in ssd.STAGES.items():
+    schedule = ssd.schedule_of(prob, w.diag)
+    names = ssd.FUSED_KERNELS if schedule == "fused" else ssd.SPLIT_KERNELS
+    for name in names:
+        bit = ssd.STAGES[name]
         if w.diag and name == "k_cb":
             continue
         pk = ssd.make_problem(b, T, H, P, N, G, Q, dcode, flags=bit)
@@ -192,7 +195,7 @@ def main():
         "data": "synthetic (seeded; Mamba-2 layer-shaped value distributions)",
         "config": {"workload": w.name, "batch": b, "seqlen": T, "nheads": H, "headdim": P, "dstate": N,
                    "ngroups": G, "chunk": Q, "decay": "diagonal" if w.diag else "scalar",
-                   "h0": h0 is not None},
+                   "h0": h0 is not None, "schedule": schedule},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak, 4),
         "path_min_bytes": min_bytes,

@@ -80,16 +80,31 @@ typedef struct {
     int32_t flags;  /* 0 = the whole forward; see SSD_STAGE_* */
 } ssd_problem;
 
-/* Diagnostics only (per-kernel timing and per-stage inspection).  A nonzero `flags`
- * is a mask of the kernels to enqueue; the others are skipped and their results are
- * read from the workspace, which a previous call with flags = 0 on the same problem,
- * inputs and workspace must have filled.  Any other bit is SSD_ERR_UNSUPPORTED. */
+/* Schedules.  The library runs one of two kernel sequences:
+ *   fused  k_cumsum, k_cb, k_bt, then k_fused: one work-group per (batch, head) walks its
+ *          chunks in order with the state held on chip (scalar decay, bf16, headdim 64,
+ *          dstate 64 or 128, and at least 512 (batch, head) pairs to fill the GPU);
+ *   split  k_cumsum, k_cb (scalar decay), k_state, k_scan, k_out: every stage is a
+ *          separate chunk-parallel launch and chunk states go through the workspace.
+ * flags = 0 picks fused where it applies, else split.  SSD_SCHEDULE_SPLIT forces split
+ * (every intermediate then lands in the workspace); SSD_SCHEDULE_FUSED forces fused
+ * regardless of the (batch, head) count, and is SSD_ERR_UNSUPPORTED where the fused
+ * kernel does not exist (other dtype, decay, headdim or dstate).
+ *
+ * Diagnostics only (per-kernel timing and per-stage inspection): a nonzero stage mask
+ * in the low byte of `flags` enqueues just those kernels; their inputs are read from the
+ * workspace, which a previous full call on the same problem, inputs and workspace must
+ * have filled.  Any other bit is SSD_ERR_UNSUPPORTED. */
 #define SSD_STAGE_CUMSUM 0x01 /* chunk-local cumulative sum of dt      -> ws cdt     */
 #define SSD_STAGE_CB 0x02     /* C_c B_c^T per chunk (scalar decay)    -> ws cb      */
 #define SSD_STAGE_STATE 0x04  /* chunk states S_c                      -> ws states  */
 #define SSD_STAGE_SCAN 0x08   /* inter-chunk state scan                -> ws hin, hT */
 #define SSD_STAGE_OUT 0x10    /* diagonal blocks + state output + D    -> y          */
-#define SSD_STAGE_ALL 0x1f
+#define SSD_STAGE_BT 0x20     /* per-chunk B with tokens contiguous    -> ws bt      */
+#define SSD_STAGE_FUSED 0x40  /* fused per-(batch, head) scan          -> y, hT      */
+#define SSD_STAGE_ALL 0x7f
+#define SSD_SCHEDULE_SPLIT 0x100
+#define SSD_SCHEDULE_FUSED 0x200
 
 /* Bytes of device workspace that ssd_scan_fwd (diag = 0) or ssd_diag_scan_fwd
  * (diag = 1) needs for this problem; 0 if the problem is invalid or empty.
@@ -104,12 +119,16 @@ size_t ssd_workspace_bytes(const ssd_problem* p, int diag);
  *        the diagonal (scalar decay only)
  *   states float32 [batch, nheads, nchunks, headdim, dstate]  chunk states S_c
  *   hin  dtype   [batch, nheads, nchunks, headdim, dstate]  state entering chunk c
+ *   bt   dtype   [batch, nchunks, ngroups, dstate, chunk]  B of each chunk, tokens contiguous
+ *        (scalar decay)
+ * The split schedule fills cdt, cb, states and hin; the fused one fills cdt, cb and bt.
  * Returns an ssd_status.  Pure host function. */
 typedef struct {
     size_t cdt_off, cdt_bytes;
     size_t cb_off, cb_bytes;
     size_t states_off, states_bytes;
     size_t hin_off, hin_bytes;
+    size_t bt_off, bt_bytes;
     size_t total_bytes;
 } ssd_workspace_layout;
 int ssd_get_workspace_layout(const ssd_problem* p, int diag, ssd_workspace_layout* out);

@@ -46,7 +46,7 @@ class Problem(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("cdt_off", "cdt_bytes", "cb_off", "cb_bytes", "states_off", "states_bytes",
-                 "hin_off", "hin_bytes", "total_bytes")]
+                 "hin_off", "hin_bytes", "bt_off", "bt_bytes", "total_bytes")]
 
 
 def library_path() -> str:
@@ -86,8 +86,27 @@ def version() -> int:
 
 
 STAGE_CUMSUM, STAGE_CB, STAGE_STATE, STAGE_SCAN, STAGE_OUT = 0x01, 0x02, 0x04, 0x08, 0x10
+STAGE_BT, STAGE_FUSED = 0x20, 0x40
+SCHEDULE_SPLIT, SCHEDULE_FUSED = 0x100, 0x200
 STAGES = {"k_cumsum": STAGE_CUMSUM, "k_cb": STAGE_CB, "k_state": STAGE_STATE, "k_scan": STAGE_SCAN,
-          "k_out": STAGE_OUT}
+          "k_out": STAGE_OUT, "k_bt": STAGE_BT, "k_fused": STAGE_FUSED}
+SPLIT_KERNELS = ("k_cumsum", "k_cb", "k_state", "k_scan", "k_out")
+FUSED_KERNELS = ("k_cumsum", "k_cb", "k_bt", "k_fused")
+
+
+def fused_supported(dtype_code, diag, P, N) -> bool:
+    """Whether the fused per-(batch, head) kernel exists for this problem."""
+    return dtype_code == SSD_BF16 and not diag and P == 64 and N in (64, 128)
+
+
+def schedule_of(prob: "Problem", diag: bool) -> str:
+    """The schedule the library runs for flags without a stage mask."""
+    if prob.flags & SCHEDULE_SPLIT:
+        return "split"
+    ok = fused_supported(prob.dtype, diag, prob.headdim, prob.dstate)
+    if prob.flags & SCHEDULE_FUSED:
+        return "fused" if ok else "unsupported"
+    return "fused" if ok and prob.batch * prob.nheads >= 512 else "split"
 
 
 def make_problem(b, T, H, P, N, G, chunk, dtype, flags=0) -> Problem:

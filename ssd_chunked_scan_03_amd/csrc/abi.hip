@@ -37,7 +37,8 @@ int check_problem(const ssd_problem* p) {
     if (p->dtype != SSD_F32 && p->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
     if (p->chunk != 64 && p->chunk != 128 && p->chunk != 256) return SSD_ERR_UNSUPPORTED;
     if (!pn_supported(p->headdim, p->dstate)) return SSD_ERR_UNSUPPORTED;
-    if (p->flags & ~SSD_STAGE_ALL) return SSD_ERR_UNSUPPORTED;
+    if (p->flags & ~(SSD_STAGE_ALL | SSD_SCHEDULE_SPLIT | SSD_SCHEDULE_FUSED)) return SSD_ERR_UNSUPPORTED;
+    if ((p->flags & SSD_SCHEDULE_SPLIT) && (p->flags & SSD_SCHEDULE_FUSED)) return SSD_ERR_UNSUPPORTED;
     // launch-grid limits: blocks per launch and the batch / group grid dimensions
     const int64_t nc = (p->seqlen + p->chunk - 1) / p->chunk;
     if (p->batch > 65535 || p->batch * p->ngroups > 65535) return SSD_ERR_UNSUPPORTED;
@@ -65,6 +66,9 @@ ssd_workspace_layout layout_of(const ssd_problem* p, int diag) {
     L.hin_off = off;
     L.hin_bytes = bhc * (size_t)(p->headdim * p->dstate) * es;
     off += align_up(L.hin_bytes);
+    L.bt_off = off;
+    L.bt_bytes = diag ? 0 : (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->dstate * p->chunk) * es;
+    off += align_up(L.bt_bytes);
     L.total_bytes = (p->batch == 0 || p->seqlen == 0) ? 0 : off;
     return L;
 }
@@ -134,8 +138,11 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     a.cb = diag ? nullptr : static_cast<void*>(w + L.cb_off);
     a.states = reinterpret_cast<float*>(w + L.states_off);
     a.hin = static_cast<void*>(w + L.hin_off);
+    a.bt = diag ? nullptr : static_cast<void*>(w + L.bt_off);
     a.stream = (hipStream_t)stream;
-    a.stages = p->flags ? p->flags : SSD_STAGE_ALL;
+    a.stages = p->flags & SSD_STAGE_ALL;
+    a.force_split = (p->flags & SSD_SCHEDULE_SPLIT) != 0;
+    a.force_fused = (p->flags & SSD_SCHEDULE_FUSED) != 0;
     return p->dtype == SSD_BF16 ? ssd::run_bf16(a) : ssd::run_f32(a);
 }
 

@@ -144,13 +144,62 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
 }
 
 // ---------------------------------------------------------------------------
+// k_bt: Bt[b,c,g][n][j] = B[b, cQ+j, g, n] (0 past T): each chunk's B with tokens
+// contiguous, the layout the fused kernel reads its chunk-state A operand from.
+// Grid (nc * Q/64, b*G): one 64-token slab per work-group, transposed through LDS.
+// ---------------------------------------------------------------------------
+template <typename T, int N>
+__global__ __launch_bounds__(kThreads) void k_bt(const T* __restrict__ Bm, T* __restrict__ Bt, int64_t Tn,
+                                                 int G, int Q, int nc) {
+    typedef typename V8<T>::type v8;
+    constexpr int JB = 64, LD = JB + 8;
+    __shared__ __attribute__((aligned(16))) T s[N * LD];
+    const int slabs = Q / JB;
+    const int c = blockIdx.x / slabs, j0 = (blockIdx.x - c * slabs) * JB;
+    const int64_t bg = blockIdx.y;
+    const int64_t bi = bg / G;
+    const int g = (int)(bg - bi * G);
+    const int64_t tok0 = (int64_t)c * Q + j0;
+    for (int v = threadIdx.x; v < JB * N / 8; v += kThreads) {
+        const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
+        const v8 val = (tok0 + jj < Tn) ? ld8(Bm + ((bi * Tn + tok0 + jj) * G + g) * N + n0) : zero8<T>();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[(n0 + e) * LD + jj] = val[e];
+    }
+    __syncthreads();
+    T* out = Bt + ((bi * nc + c) * G + g) * (int64_t)N * Q + j0;
+    for (int v = threadIdx.x; v < N * JB / 8; v += kThreads) {
+        const int n = v / (JB / 8), jv = (v - n * (JB / 8)) * 8;
+        st8(out + (int64_t)n * Q + jv, ld8(&s[n * LD + jv]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wave tiling of a [N/16] x [P/16] grid of 16x16 output tiles over 4 waves: each
+// wave owns WN x WP tiles starting at (n-tile n0, p-tile p0) (or none).
+// ---------------------------------------------------------------------------
+template <int P, int N>
+struct StateTiling {
+    static constexpr int NTN = N / 16, NTP = P / 16;
+    static constexpr int WN = NTN >= 4 ? NTN / 4 : (NTP >= 4 ? NTN : 1);
+    static constexpr int WP = NTN >= 4 ? NTP : (NTP >= 4 ? NTP / 4 : 1);
+    __device__ static bool active(int w) { return NTN >= 4 || NTP >= 4 || w < NTN * NTP; }
+    __device__ static int n0(int w) { return NTN >= 4 ? w * WN : (NTP >= 4 ? 0 : w / NTP); }
+    __device__ static int p0(int w) { return NTN >= 4 ? 0 : (NTP >= 4 ? w * WP : w % NTP); }
+};
+
+// ---------------------------------------------------------------------------
 // k_state: the chunk input projection decayed to the chunk end,
 //   S_c[p][n] = sum_{j in chunk} x_j[p] * B_j[n] * exp(A (cdt_last - cdt_j))
 // (A = A_h, or A_{h,n} for the diagonal decay).  One work-group per (b, h, c).
-// The contraction runs over tokens j, which are the strided dimension of x and B in
-// memory, so 64-token slabs of x and of the decay-weighted B are transposed into LDS
-// ([p][j] and [n][j], token-contiguous) and fed to the matrix cores from there.  The
-// wave computes S^T tiles [n][p] so that each lane stores 4 consecutive n.
+// The contraction runs over tokens j, the strided dimension of x and B in memory, so
+// 64-token slabs of x and B are staged row-major in LDS (16-byte coalesced loads and
+// stores) and read back as token-contiguous fragments with the LDS transpose read.
+// The decay weight multiplies the smaller operand once per element while staging: x
+// rows (one weight per token) for the scalar decay, B elements for the diagonal decay.
+// The next slab's global loads are issued into registers before the current slab's
+// matrix-core work.  Waves compute S^T tiles [n][p], so each lane stores 4
+// consecutive n.
 // ---------------------------------------------------------------------------
 template <typename T, int P, int N, bool DIAG>
 __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, const T* __restrict__ Bm,
@@ -159,11 +208,14 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
                                                     float* __restrict__ S, int64_t Tn, int H, int G,
                                                     int Q, int nc) {
     typedef typename V8<T>::type v8;
-    constexpr int JB = 64, LDJ = JB + 8;
-    constexpr int NT = (N / 16) * (P / 16), TPW = (NT + 3) / 4;
-    __shared__ __attribute__((aligned(16))) T Xt[P * LDJ];
-    __shared__ __attribute__((aligned(16))) T Bt[N * LDJ];
+    typedef StateTiling<P, N> TL;
+    constexpr int JB = 64, LDX = P + 8, LDB = N + 8;
+    constexpr int XV = JB * P / 8, BV = JB * N / 8;                       // 8-element vectors per slab
+    constexpr int XR = (XV + kThreads - 1) / kThreads, BR = (BV + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) T Xs[JB * LDX];
+    __shared__ __attribute__((aligned(16))) T Bs[JB * LDB];
     __shared__ float cds[256];
+    __shared__ float an2[DIAG ? N : 1];
     const int64_t blk = blockIdx.x;
     const int c = (int)(blk % nc);
     const int64_t bh = blk / nc;
@@ -175,65 +227,96 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
     const int len = (int)((Tn - tok0) < Q ? (Tn - tok0) : Q);
     const float* cd = cdt + (bh * nc + c) * (int64_t)Q;
     for (int i = tid; i < Q; i += kThreads) cds[i] = cd[i];
-    __syncthreads();
-    const float last = cds[Q - 1];
-    const float Ah = DIAG ? 0.f : A[h];
-    f32x4 acc[TPW];
+    if (DIAG)
+        for (int n = tid; n < N; n += kThreads) an2[n] = A[h * N + n] * 1.4426950408889634f;
+    const float ah2 = DIAG ? 0.f : A[h] * 1.4426950408889634f;
+    const T* xb = x + ((bi * Tn + tok0) * H + h) * P;   // row j at xb + j * H * P
+    const T* bb = Bm + ((bi * Tn + tok0) * G + g) * N;  // row j at bb + j * G * N
+
+    v8 xv[XR], bv[BR];
+    auto prefetch = [&](int j0) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < XR; ++r) {
+            const int v = tid + r * kThreads;
+            const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
+            const int jr = j0 + jj < len ? j0 + jj : len - 1;
+            xv[r] = sel8(v < XV && j0 + jj < len, ld8(xb + (int64_t)jr * H * P + p0));
+        }
+#pragma unroll
+        for (int r = 0; r < BR; ++r) {
+            const int v = tid + r * kThreads;
+            const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
+            const int jr = j0 + jj < len ? j0 + jj : len - 1;
+            bv[r] = sel8(v < BV && j0 + jj < len, ld8(bb + (int64_t)jr * G * N + n0));
+        }
+    };
+    prefetch(0);
+    __syncthreads();  // cds, an2
+    const float last = cds[Q - 1];
+
+    f32x4 acc[TL::WN][TL::WP];
+#pragma unroll
+    for (int a = 0; a < TL::WN; ++a)
+#pragma unroll
+        for (int b = 0; b < TL::WP; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool wact = TL::active(w);
+    const int wn0 = TL::n0(w), wp0 = TL::p0(w);
 
     for (int j0 = 0; j0 < len; j0 += JB) {
-        for (int v = tid; v < JB * P / 8; v += kThreads) {
-            const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
-            const int j = j0 + jj;
-            const v8 val = (j < len) ? ld8(x + ((bi * Tn + tok0 + j) * H + h) * P + p0) : zero8<T>();
+        // slab j0 -> LDS, decay weight applied once per element
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Xt[(p0 + e) * LDJ + jj] = val[e];
-        }
-        for (int v = tid; v < JB * N / 8; v += kThreads) {
-            const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
-            const int j = j0 + jj;
-            if (j < len) {
-                const v8 val = ld8(Bm + ((bi * Tn + tok0 + j) * G + g) * N + n0);
-                const float dc = last - cds[j];
+        for (int r = 0; r < XR; ++r) {
+            const int v = tid + r * kThreads;
+            if (v < XV) {
+                const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
+                v8 o = xv[r];
                 if (!DIAG) {
-                    const float wj = exp_f(Ah * dc);
+                    const float wj = exp2f_fast(ah2 * (last - cds[j0 + jj]));
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) Bt[(n0 + e) * LDJ + jj] = from_f<T>(to_f(val[e]) * wj);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        Bt[(n0 + e) * LDJ + jj] = from_f<T>(to_f(val[e]) * exp_f(A[h * N + n0 + e] * dc));
+                    for (int e = 0; e < 8; ++e) o[e] = from_f<T>(to_f(o[e]) * wj);
                 }
-            } else {
+                st8(&Xs[jj * LDX + p0], o);
+            }
+        }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) Bt[(n0 + e) * LDJ + jj] = from_f<T>(0.f);
+        for (int r = 0; r < BR; ++r) {
+            const int v = tid + r * kThreads;
+            if (v < BV) {
+                const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
+                v8 o = bv[r];
+                if (DIAG) {
+                    const float dc = last - cds[j0 + jj];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] = from_f<T>(to_f(o[e]) * exp2f_fast(an2[n0 + e] * dc));
+                }
+                st8(&Bs[jj * LDB + n0], o);
             }
         }
         __syncthreads();
+        if (j0 + JB < len) prefetch(j0 + JB);
+        if (wact) {
 #pragma unroll
-        for (int kk = 0; kk < JB; kk += 32) {
+            for (int kk = 0; kk < JB; kk += 32) {
+                v8 bf[TL::WP];
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int tile = w + 4 * t;
-                if (tile < NT) {
-                    const int nt = tile / (P / 16), pt = tile - nt * (P / 16);
-                    const v8 a = ld8(&Bt[(nt * 16 + l16) * LDJ + kk + 8 * q]);
-                    const v8 b = ld8(&Xt[(pt * 16 + l16) * LDJ + kk + 8 * q]);
-                    acc[t] = mma(acc[t], a, b);
+                for (int b = 0; b < TL::WP; ++b) bf[b] = frag_rows(Xs, LDX, kk, (wp0 + b) * 16, lane);
+#pragma unroll
+                for (int a = 0; a < TL::WN; ++a) {
+                    const v8 af = frag_rows(Bs, LDB, kk, (wn0 + a) * 16, lane);
+#pragma unroll
+                    for (int b = 0; b < TL::WP; ++b) acc[a][b] = mma(acc[a][b], af, bf[b]);
                 }
             }
         }
         __syncthreads();
     }
-    float* out = S + (bh * nc + c) * (int64_t)(P * N);
+    if (wact) {
+        float* out = S + (bh * nc + c) * (int64_t)(P * N);
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int tile = w + 4 * t;
-        if (tile < NT) {
-            const int nt = tile / (P / 16), pt = tile - nt * (P / 16);
-            st4(out + (pt * 16 + l16) * N + nt * 16 + 4 * q, acc[t]);
-        }
+        for (int a = 0; a < TL::WN; ++a)
+#pragma unroll
+            for (int b = 0; b < TL::WP; ++b)
+                st4(out + ((wp0 + b) * 16 + l16) * N + (wn0 + a) * 16 + 4 * q, acc[a][b]);
     }
 }
 
@@ -296,36 +379,34 @@ __global__ __launch_bounds__(kThreads) void k_scan(const float* __restrict__ S, 
 //   y_i = sum_{j<=i} cb[i][j] exp(A (cdt_i - cdt_j)) x_j        (diagonal block)
 //       + exp(A cdt_i) * sum_n C_i[n] H_c[p][n]                   (off-diagonal blocks)
 //       + D_h x_i
-// The decay mask is formed in registers on the cb fragment (A operand); x is the
-// B operand, read token-contiguous from an LDS transpose; the state term takes the
-// decay-scaled C rows as A operand and H_c (row-major [p][n]) as B operand, so both
-// terms accumulate into one fp32 tile set.  Each wave owns Q/64 row tiles of 16 rows,
-// paired (k, 7-k) within every 128 rows so the causal work is balanced.  The result
-// is staged through LDS (aliasing the x transpose) for 16-byte row stores.
-// Diagonal decay (DIAG): the per-head block G_ij = sum_n C_in B_jn exp(A_n(cdt_i-cdt_j))
-// is formed on the matrix cores from rescaled operands, for every 16 x 16 sub-block
-// pair (I >= J): C~_i = C_i exp(A (cdt_i - cdt_sI)), B~_j = B_j exp(A (cdt_eJ - cdt_j)),
-// times exp(A (cdt_sI - cdt_eJ)) per n (sI = first row of I, eJ = last row of J); all
-// three factors are <= 1 off the diagonal.  A diagonal sub-block whose decay span is
-// too wide for that split (|A| span > 80) is summed directly with per-term exps.
+// Waves compute y^T tiles [p][i] (x^T from the LDS transpose read as A operand, the
+// masked block row as B operand), so a lane ends up with 4 consecutive p of one row.
+// Scalar decay:
+//  * the state term uses raw C and H fragments; its per-row factor exp(A cdt_i)
+//    scales the accumulator afterwards;
+//  * on the block's 32-token k-steps strictly before the row tile, the mask factors
+//    as exp(A (cdt_i - cdt_r)) exp(A (cdt_r - cdt_j)) with r the last token of the
+//    k-step, both <= 1: one exp per lane and k-step, the second factor from LDS;
+//  * the k-step holding the row tile takes direct exps, the causal cut and D_h on
+//    the diagonal (D x_i rides along in the same product).
+// Diagonal decay: the per-head block G_ij = sum_n C_in B_jn exp(A_n(cdt_i-cdt_j)) is
+// formed on the matrix cores from rescaled operands for every 16 x 16 sub-block pair
+// (I >= J): C~_i = C_i exp(A (cdt_i - cdt_sI)), B~_j = B_j exp(A (cdt_eJ - cdt_j)),
+// times exp(A (cdt_sI - cdt_eJ)) per n (sI first row of I, eJ last row of J); the three
+// factors are <= 1 off the diagonal.  A diagonal sub-block whose decay span is too
+// wide for that split (|A| span > 80) is summed directly with per-term exps.
+// Each wave owns Q/64 row tiles of 16 rows, paired (k, 7-k) within every 128 rows so
+// the causal work is balanced.  y is staged through LDS (aliasing x) for row stores.
 // ---------------------------------------------------------------------------
-// Dynamic LDS of k_out for a chunk of Q tokens (element offsets; all 16-byte aligned):
-//   [0, xy)            x transpose Xt[P][Q+8], later the y staging tile Ys[Q][P+8]
-//   [xy, xy+Q*(N+8))   rescaled C rows (diagonal decay only)
-//   [.., +Q*(N+8))     rescaled B rows (diagonal decay only)
-//   then Q floats      cdt of the chunk
 template <typename T, int P, int N, bool DIAG>
 struct OutSmem {
-    static constexpr int LDY = P + 8;
-    static constexpr int LDN = N + 8;
-    __host__ __device__ static int ldq(int Q) { return Q + 8; }
-    __host__ __device__ static int xy(int Q) {
-        const int a = P * (Q + 8), b = Q * LDY;
-        return ((a > b ? a : b) + 7) / 8 * 8;
-    }
+    static constexpr int LDX = P + 8;  // x (then y) rows
+    static constexpr int LDN = N + 8;  // rescaled C / B rows (diagonal decay)
+    __host__ __device__ static int xs(int Q) { return Q * LDX; }
     __host__ __device__ static int diag_elems(int Q) { return DIAG ? 2 * Q * LDN : 0; }
+    __host__ __device__ static int floats(int Q) { return 2 * Q + (DIAG ? N : 0); }
     __host__ __device__ static size_t bytes(int Q) {
-        return (size_t)(xy(Q) + diag_elems(Q)) * sizeof(T) + (size_t)Q * sizeof(float);
+        return (size_t)(xs(Q) + diag_elems(Q)) * sizeof(T) + (size_t)floats(Q) * sizeof(float);
     }
 };
 
@@ -337,17 +418,19 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                                                   const float* __restrict__ cdt, T* __restrict__ y,
                                                   int64_t Tn, int H, int G, int Q, int nc) {
     typedef typename V8<T>::type v8;
+    typedef typename V4<T>::type v4;
     typedef OutSmem<T, P, N, DIAG> SM;
-    constexpr int LDY = SM::LDY, LDN = SM::LDN;
+    constexpr int LDX = SM::LDX, LDN = SM::LDN;
     constexpr int PT = P / 16;
-    const int LDQ = SM::ldq(Q);
+    constexpr float LOG2E = 1.4426950408889634f;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    T* XY = reinterpret_cast<T*>(smem_raw);
-    T* Ct = XY + SM::xy(Q);
+    T* Xs = reinterpret_cast<T*>(smem_raw);
+    T* Ys = Xs;
+    T* Ct = Xs + SM::xs(Q);
     T* Bt = Ct + (DIAG ? Q * LDN : 0);
-    float* cds = reinterpret_cast<float*>(XY + SM::xy(Q) + SM::diag_elems(Q));
-    T* Xt = XY;
-    T* Ys = XY;
+    float* cds = reinterpret_cast<float*>(Xs + SM::xs(Q) + SM::diag_elems(Q));
+    float* u2 = cds + Q;       // scalar: exp(A (cdt_r(j) - cdt_j)), r(j) = j | 31
+    float* an2 = u2 + Q;       // diagonal: A_n log2(e)
 
     const int64_t blk = blockIdx.x;
     const int c = (int)(blk % nc);
@@ -358,31 +441,88 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, q = lane >> 4;
     const int64_t tok0 = (int64_t)c * Q;
     const int len = (int)((Tn - tok0) < Q ? (Tn - tok0) : Q);
+    const int rpw = Q / 64;  // row tiles per wave
+    const T* xb = x + ((bi * Tn + tok0) * H + h) * P;   // row j at xb + j * H * P
+    const T* cbase_rows = Cm + ((bi * Tn + tok0) * G + g) * N;  // row i at + i * G * N
+    const T* hbase = hin + (bh * nc + c) * (int64_t)(P * N);
     const float* cd = cdt + (bh * nc + c) * (int64_t)Q;
-    for (int i = tid; i < Q; i += kThreads) cds[i] = cd[i];
-    // x rows of the chunk, transposed: Xt[p][j]
-    for (int v = tid; v < Q * P / 8; v += kThreads) {
-        const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
-        const v8 val = (jj < len) ? ld8(x + ((bi * Tn + tok0 + jj) * H + h) * P + p0) : zero8<T>();
+    const float ah2 = DIAG ? 0.f : A[h] * LOG2E;
+    const float Dh = D ? D[h] : 0.f;
+
+    auto row_tile = [&](int k) { return (rpw == 1) ? w : ((k & 1) ? 8 * (k >> 1) + 7 - w : 8 * (k >> 1) + w); };
+
+    // 1. x rows of the chunk: issue the loads now, store them to LDS after the state term
+    constexpr int XR = (256 * P / 8 + kThreads - 1) / kThreads;  // enough for Q = 256
+    const int XV = Q * P / 8;
+    v8 xv[XR];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Xt[(p0 + e) * LDQ + jj] = val[e];
+    for (int r = 0; r < XR; ++r) {
+        const int v = tid + r * kThreads;
+        const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
+        const int jr = jj < len ? jj : len - 1;
+        xv[r] = sel8(v < XV && jj < len, ld8(xb + (int64_t)jr * H * P + p0));
     }
+    float cdv = 0.f;
+    if (tid < Q) cdv = cd[tid];
+
+    f32x4 acc[4][PT];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // 2. scalar decay: state term y^T[p][i] += sum_n H[p][n] C[i][n] from raw fragments
+    if (!DIAG) {
+#pragma unroll
+        for (int n0 = 0; n0 < N; n0 += 32) {
+            const int nn = n0 + 8 * q;
+            const bool nv = (N % 32 == 0) || (nn < N);  // N = 16: half the k-step is padding
+            v8 hf[PT], cf[4];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) hf[pt] = sel8(nv, ld8(hbase + (pt * 16 + l16) * N + (nv ? nn : 0)));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = row_tile(k) * 16 + l16;
+                const int ir = i < len ? i : len - 1;
+                cf[k] = sel8(k < rpw && nv && i < len, ld8(cbase_rows + (int64_t)ir * G * N + (nv ? nn : 0)));
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (k < rpw)
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) acc[k][pt] = mma(acc[k][pt], hf[pt], cf[k]);
+        }
+    }
+
+    // 3. x -> LDS (row-major), chunk decay tables
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+        const int v = tid + r * kThreads;
+        if (v < XV) {
+            const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
+            st8(&Xs[jj * LDX + p0], xv[r]);
+        }
+    }
+    if (tid < Q) cds[tid] = cdv;
+    if (DIAG)
+        for (int n = tid; n < N; n += kThreads) an2[n] = A[h * N + n] * LOG2E;
+    __syncthreads();
+    if (!DIAG && tid < Q) u2[tid] = exp2f_fast(ah2 * (cds[tid | 31] - cds[tid]));
     if (DIAG) {
-        __syncthreads();  // cds visible
         // rescaled rows: Ct[i][n] = C_i[n] e^{A_n (cdt_i - cdt_sI)}, Bt[j][n] = B_j[n] e^{A_n (cdt_eJ - cdt_j)}
+        const T* bbase_rows = Bm + ((bi * Tn + tok0) * G + g) * N;
         for (int v = tid; v < Q * N / 8; v += kThreads) {
             const int ii = v / (N / 8), n0 = (v - ii * (N / 8)) * 8;
             v8 cv = zero8<T>(), bv = zero8<T>();
             if (ii < len) {
-                const v8 cr = ld8(Cm + ((bi * Tn + tok0 + ii) * G + g) * N + n0);
-                const v8 br = ld8(Bm + ((bi * Tn + tok0 + ii) * G + g) * N + n0);
+                const v8 cr = ld8(cbase_rows + (int64_t)ii * G * N + n0);
+                const v8 br = ld8(bbase_rows + (int64_t)ii * G * N + n0);
                 const float dcs = cds[ii] - cds[ii & ~15];
                 const float dce = cds[ii | 15] - cds[ii];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float an = A[h * N + n0 + e];
-                    cv[e] = from_f<T>(to_f(cr[e]) * exp_f(an * dcs));
-                    bv[e] = from_f<T>(to_f(br[e]) * exp_f(an * dce));
+                    cv[e] = from_f<T>(to_f(cr[e]) * exp2f_fast(an2[n0 + e] * dcs));
+                    bv[e] = from_f<T>(to_f(br[e]) * exp2f_fast(an2[n0 + e] * dce));
                 }
             }
             st8(&Ct[ii * LDN + n0], cv);
@@ -391,65 +531,78 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
     }
     __syncthreads();
 
-    const float Ah = DIAG ? 0.f : A[h];
-    const float Dh = D ? D[h] : 0.f;
-    const int rpw = Q / 64;  // row tiles per wave
-    f32x4 acc[4][PT];
+    if (!DIAG) {
+        // 4. per-row factor of the state term: this lane's column is row i
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < 4; ++k)
+            if (k < rpw) {
+                const float sc = exp2f_fast(ah2 * cds[row_tile(k) * 16 + l16]);
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const T* hbase = hin + (bh * nc + c) * (int64_t)(P * N);
-    const T* cbase = cb + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
-
+                for (int pt = 0; pt < PT; ++pt) acc[k][pt] *= sc;
+            }
+        // 5. diagonal block
+        const T* cbb = cb + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        if (k < rpw) {
-            const int rt = (rpw == 1) ? w : ((k & 1) ? 8 * (k >> 1) + 7 - w : 8 * (k >> 1) + w);
-            const int i = rt * 16 + l16;  // A-operand row of this lane
-            const float ci = cds[i];
-            if (!DIAG) {
-                // diagonal block: masked C B^T fragment times x
-                const T* cbrow = cbase + (int64_t)i * Q;
-                const int nks = (rt * 16 + 16 + 31) / 32;
-                for (int ks = 0; ks < nks; ++ks) {
-                    const int j0 = ks * 32 + 8 * q;
-                    const v8 gv = ld8(cbrow + j0);
-                    v8 a;
+        for (int k = 0; k < 4; ++k) {
+            if (k < rpw) {
+                const int rt = row_tile(k);
+                const int i = rt * 16 + l16;
+                const T* cbrow = cbb + (int64_t)i * Q;
+                const int nks = rt / 2 + 1;  // k-steps of 32 tokens up to this row tile
+                v8 gf[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int j = j0 + e;
-                        const float m = (j <= i) ? exp_f(Ah * (ci - cds[j])) : 0.f;
-                        a[e] = from_f<T>(to_f(gv[e]) * m);
-                    }
+                for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbrow + (ks < nks ? ks : nks - 1) * 32 + 8 * q);
+                const float ci = cds[i];
 #pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) {
-                        const v8 b = ld8(&Xt[(pt * 16 + l16) * LDQ + j0]);
-                        acc[k][pt] = mma(acc[k][pt], a, b);
+                for (int ks = 0; ks < 8; ++ks) {
+                    if (ks < nks) {
+                        const int j0 = ks * 32 + 8 * q;
+                        v8 mf;
+                        if (ks < nks - 1) {
+                            const float vi = exp2f_fast(ah2 * (ci - cds[ks * 32 + 31]));
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) mf[e] = from_f<T>(to_f(gf[ks][e]) * (u2[j0 + e] * vi));
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const int j = j0 + e;
+                                // exponent clamped to <= 0 so the unused (j > i) slots stay finite
+                                float m = to_f(gf[ks][e]) * exp2f_fast(fminf(ah2 * (ci - cds[j]), 0.f));
+                                m = (j <= i) ? m : 0.f;
+                                m += (j == i) ? Dh : 0.f;
+                                mf[e] = from_f<T>(m);
+                            }
+                        }
+#pragma unroll
+                        for (int pt = 0; pt < PT; ++pt) {
+                            const v8 xf = frag_rows(Xs, LDX, ks * 32, pt * 16, lane);
+                            acc[k][pt] = mma(acc[k][pt], xf, mf);
+                        }
                     }
                 }
-            } else {
-                // per-head block from rescaled operands, 16 x 16 sub-blocks (I = rt, J <= I)
+            }
+        }
+    } else {
+        float amax = 0.f;  // widest per-n decay rate, for the diagonal sub-block split
+        for (int n = 0; n < N; ++n) amax = fmaxf(amax, -an2[n]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (k < rpw) {
+                const int rt = row_tile(k);
                 const int sI = rt * 16;
+                const int i = sI + l16;
                 for (int u = 0; 2 * u <= rt; ++u) {
                     f32x4 gt[2];
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        gt[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        const int J = 2 * u + s;
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        gt[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        const int J = 2 * u + s2;
                         if (J > rt) continue;
                         const int eJ = J * 16 + 15;
-                        bool direct = false;
-                        if (J == rt) {
-                            // widest decay span of this diagonal sub-block over n
-                            float span = 0.f;
-                            for (int n = 0; n < N; ++n) span = fmaxf(span, -A[h * N + n]);
-                            span *= (cds[eJ] - cds[sI]);
-                            direct = !(span <= 80.f);
-                        }
+                        const bool direct = (J == rt) && !(amax * (cds[eJ] - cds[sI]) <= 80.f * LOG2E);
                         if (!direct) {
-                            // gt[s] = (B~_J diag(m) C~_I^T): lane holds G^T[j = 4q + r][i = l16]
+                            // gt = B~_J diag(m) C~_I^T: lane holds G^T[j = 16J + 4q + r][i = sI + l16]
+                            const float dm = cds[sI] - cds[eJ];
 #pragma unroll
                             for (int n0 = 0; n0 < N; n0 += 32) {
                                 const int nn = n0 + 8 * q;
@@ -457,104 +610,92 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                                 v8 a = zero8<T>(), b = zero8<T>();
                                 if (nv) {
                                     a = ld8(&Bt[(J * 16 + l16) * LDN + nn]);
-                                    const float dm = cds[sI] - cds[eJ];
 #pragma unroll
                                     for (int e = 0; e < 8; ++e)
-                                        a[e] = from_f<T>(to_f(a[e]) * exp_f(A[h * N + nn + e] * dm));
+                                        a[e] = from_f<T>(to_f(a[e]) * exp2f_fast(an2[nn + e] * dm));
                                     b = ld8(&Ct[(sI + l16) * LDN + nn]);
                                 }
-                                gt[s] = mma(gt[s], a, b);
+                                gt[s2] = mma(gt[s2], a, b);
                             }
                         } else {
-                            // direct per-term sums for this lane's 4 entries (i = sI + l16, j = sI + 4q + r)
-                            const int ii = sI + l16;
+                            // direct sums for this lane's 4 entries (i, j = sI + 4q + r)
+#pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 const int jj = sI + 4 * q + r;
                                 float sum = 0.f;
-                                if (jj <= ii && ii < len) {
-                                    const T* cr = Cm + ((bi * Tn + tok0 + ii) * G + g) * N;
+                                if (jj <= i && i < len) {
+                                    const T* cr = cbase_rows + (int64_t)i * G * N;
                                     const T* br = Bm + ((bi * Tn + tok0 + jj) * G + g) * N;
-                                    const float dd = cds[ii] - cds[jj];
+                                    const float dd = cds[i] - cds[jj];
                                     for (int n = 0; n < N; ++n)
-                                        sum += to_f(cr[n]) * to_f(br[n]) * exp_f(A[h * N + n] * dd);
+                                        sum += to_f(cr[n]) * to_f(br[n]) * exp2f_fast(an2[n] * dd);
                                 }
-                                gt[s][r] = sum;
+                                gt[s2][r] = sum;
                             }
                         }
                         if (J == rt) {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (4 * q + r > l16) gt[s][r] = 0.f;  // causal: j <= i
+                            for (int r = 0; r < 4; ++r) {
+                                if (4 * q + r > l16) gt[s2][r] = 0.f;       // causal: j <= i
+                                else if (4 * q + r == l16) gt[s2][r] += Dh;  // skip term on the diagonal
+                            }
                         }
                     }
-                    // A operand: row i = l16, k = (s, 4q + r) -> token j = 32u + 16s + 4q + r
-                    v8 a;
+                    // B operand: column i = l16, k = (s2, 4q + r) -> token j = 32u + 16 s2 + 4q + r
+                    v8 mf;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        a[r] = from_f<T>(gt[0][r]);
-                        a[4 + r] = from_f<T>(gt[1][r]);
+                        mf[r] = from_f<T>(gt[0][r]);
+                        mf[4 + r] = from_f<T>(gt[1][r]);
                     }
-                    const int jb = 32 * u + 4 * q;
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) {
-                        const T* xr = &Xt[(pt * 16 + l16) * LDQ + jb];
-                        v8 b;
+                        const v8 xf = frag_rows_split(Xs, LDX, 32 * u + 4 * q, 32 * u + 16 + 4 * q, pt * 16, lane);
+                        acc[k][pt] = mma(acc[k][pt], xf, mf);
+                    }
+                }
+                // state term: y^T[p][i] += sum_n H[p][n] C[i][n] e^{A_n cdt_i}, with
+                // C[i][n] e^{A_n cdt_i} = C~[i][n] e^{A_n cdt_sI}
+                const float csI = cds[sI];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            b[r] = xr[r];
-                            b[4 + r] = xr[16 + r];
-                        }
-                        acc[k][pt] = mma(acc[k][pt], a, b);
+                for (int n0 = 0; n0 < N; n0 += 32) {
+                    const int nn = n0 + 8 * q;
+                    const bool nv = (N % 32 == 0) || (nn < N);
+                    v8 cf = zero8<T>();
+                    if (nv) {
+                        cf = ld8(&Ct[i * LDN + nn]);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) cf[e] = from_f<T>(to_f(cf[e]) * exp2f_fast(an2[nn + e] * csI));
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const v8 hf = nv ? ld8(hbase + (pt * 16 + l16) * N + nn) : zero8<T>();
+                        acc[k][pt] = mma(acc[k][pt], hf, cf);
                     }
                 }
             }
-            // off-diagonal blocks: exp(A cdt_i) C_i . H_c[p]
-            const bool iv = i < len;
-            const T* crow = Cm + ((bi * Tn + tok0 + (iv ? i : 0)) * G + g) * N;
-            const float ei = DIAG ? 0.f : exp_f(Ah * ci);
-#pragma unroll
-            for (int n0 = 0; n0 < N; n0 += 32) {
-                const int nn = n0 + 8 * q;
-                const bool nv = (N % 32 == 0) || (nn < N);  // N = 16: half the k-step is padding
-                v8 a = zero8<T>();
-                if (iv && nv) {
-                    a = ld8(crow + nn);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float sc = DIAG ? exp_f(A[h * N + nn + e] * ci) : ei;
-                        a[e] = from_f<T>(to_f(a[e]) * sc);
-                    }
-                }
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const v8 b = nv ? ld8(hbase + (pt * 16 + l16) * N + nn) : zero8<T>();
-                    acc[k][pt] = mma(acc[k][pt], a, b);
-                }
-            }
-            // skip term D_h x_i: this lane's outputs are rows rt*16 + 4q + r, column pt*16 + l16
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[k][pt][r] += Dh * to_f(Xt[(pt * 16 + l16) * LDQ + rt * 16 + 4 * q + r]);
         }
     }
-    __syncthreads();  // every wave is done with Xt; reuse it as the y staging tile
+
+    // 6. y^T tiles -> LDS rows (4 consecutive p per lane), then 16-byte row stores
+    __syncthreads();  // every wave is done reading Xs
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         if (k < rpw) {
-            const int rt = (rpw == 1) ? w : ((k & 1) ? 8 * (k >> 1) + 7 - w : 8 * (k >> 1) + w);
+            const int i = row_tile(k) * 16 + l16;
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
+            for (int pt = 0; pt < PT; ++pt) {
+                v4 o;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Ys[(rt * 16 + 4 * q + r) * LDY + pt * 16 + l16] = from_f<T>(acc[k][pt][r]);
+                for (int r = 0; r < 4; ++r) o[r] = from_f<T>(acc[k][pt][r]);
+                st4(&Ys[i * LDX + pt * 16 + 4 * q], o);
+            }
         }
     }
     __syncthreads();
     for (int v = tid; v < len * (P / 8); v += kThreads) {
         const int ii = v / (P / 8), p0 = (v - ii * (P / 8)) * 8;
-        st8(y + ((bi * Tn + tok0 + ii) * H + h) * P + p0, ld8(&Ys[ii * LDY + p0]));
+        st8(y + ((bi * Tn + tok0 + ii) * H + h) * P + p0, ld8(&Ys[ii * LDX + p0]));
     }
 }
 

@@ -1,7 +1,7 @@
 // launch.hpp -- enqueue the kernel sequence of one SSD forward on a stream.
 #pragma once
 
-#include "kernels.hpp"
+#include "fused.hpp"
 
 namespace ssd {
 
@@ -22,12 +22,38 @@ struct RunArgs {
     void* cb;       // [b,nc,G,Q,Q]  (scalar decay only)
     float* states;  // [b,H,nc,P,N]
     void* hin;      // [b,H,nc,P,N]
+    void* bt;       // [b,nc,G,N,Q]  (scalar decay only)
     hipStream_t stream;
-    int stages;     // mask of kernels to enqueue (1 cumsum, 2 cb, 4 state, 8 scan, 16 out)
+    int stages;       // 0: the whole schedule; else a mask of kernels to enqueue
+                      // (1 cumsum, 2 cb, 4 state, 8 scan, 16 out, 32 bt, 64 fused)
+    bool force_split;
+    bool force_fused;
 };
+
+// The fused per-(batch, head) schedule: bf16, scalar decay, P = 64, N in {64, 128},
+// and enough (batch, head) chains to occupy every CU several times over.
+inline bool fused_supported(const RunArgs& a, bool bf16_dtype) {
+    return bf16_dtype && !a.diag && a.P == 64 && (a.N == 64 || a.N == 128);
+}
+inline bool fused_applies(const RunArgs& a, bool bf16_dtype) {
+    return fused_supported(a, bf16_dtype) && !a.force_split && (a.force_fused || a.b * a.H >= 512);
+}
+
+template <int Q, int N>
+void launch_fused(const RunArgs& a) {
+    const int BH = (int)(a.b * a.H);
+    k_fused<Q, N><<<BH, kThreads, 0, a.stream>>>(
+        static_cast<const bf16*>(a.x), static_cast<const bf16*>(a.C), static_cast<const bf16*>(a.cb),
+        static_cast<const bf16*>(a.bt), a.A, a.D, a.cdt, a.h0, static_cast<bf16*>(a.y), a.hT, a.T, (int)a.H,
+        (int)a.G, (int)a.nc, BH);
+}
 
 template <typename T, int P, int N>
 int run(const RunArgs& a) {
+    constexpr bool kBF16 = sizeof(T) == 2;
+    if (a.force_fused && !fused_supported(a, kBF16)) return 3;
+    const bool fused = fused_applies(a, kBF16);
+    const int st = a.stages ? a.stages : (fused ? (1 | 2 | 32 | 64) : (1 | 2 | 4 | 8 | 16));
     const int Q = (int)a.Q, nc = (int)a.nc, H = (int)a.H, G = (int)a.G;
     hipStream_t s = a.stream;
     const T* x = static_cast<const T*>(a.x);
@@ -42,19 +68,19 @@ int run(const RunArgs& a) {
     if (smem > 160 * 1024) return 3;
 
     const dim3 g1(nc, (unsigned)a.b, (H + 15) / 16);
-    if (a.stages & 1) switch (Q) {
+    if (st & 1) switch (Q) {
         case 64: k_cumsum<64><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, a.T, H, nc); break;
         case 128: k_cumsum<128><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, a.T, H, nc); break;
         case 256: k_cumsum<256><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, a.T, H, nc); break;
         default: return 3;
     }
-    if (!a.diag && (a.stages & 2)) {
+    if (!a.diag && (st & 2)) {
         const int nb = Q / 64;
         const dim3 g2(nb * (nb + 1) / 2, nc, (unsigned)(a.b * G));
         k_cb<T, N><<<g2, kThreads, 0, s>>>(Bm, Cm, cb, a.T, G, Q, nc);
     }
     const dim3 g3((unsigned)(a.b * H * nc));
-    if (!(a.stages & 4)) {
+    if (!(st & 4)) {
     } else if (a.diag)
         k_state<T, P, N, true><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
     else
@@ -62,19 +88,36 @@ int run(const RunArgs& a) {
 
     const int per_head = (P * N / 4 + kThreads - 1) / kThreads;
     const dim3 g4((unsigned)(a.b * H * per_head));
-    if (!(a.stages & 8)) {
+    if (!(st & 8)) {
     } else if (a.diag)
         k_scan<T, true><<<g4, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, H, P * N, N, Q, nc, per_head);
     else
         k_scan<T, false><<<g4, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, H, P * N, N, Q, nc, per_head);
 
-    if (!(a.stages & 16)) {
+    if (!(st & 16)) {
     } else if (a.diag) {
         hipFuncSetAttribute((const void*)k_out<T, P, N, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         k_out<T, P, N, true><<<g3, kThreads, smem, s>>>(x, Bm, Cm, nullptr, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);
     } else {
         hipFuncSetAttribute((const void*)k_out<T, P, N, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         k_out<T, P, N, false><<<g3, kThreads, smem, s>>>(x, Bm, Cm, cb, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);
+    }
+    if (!a.diag && (st & 32)) {
+        const dim3 g6((unsigned)(nc * (Q / 64)), (unsigned)(a.b * G));
+        k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, static_cast<T*>(a.bt), a.T, G, Q, nc);
+    }
+    if (st & 64) {
+        if constexpr (kBF16 && P == 64 && (N == 64 || N == 128)) {
+            if (a.diag) return 3;
+            switch (Q) {
+                case 64: launch_fused<64, N>(a); break;
+                case 128: launch_fused<128, N>(a); break;
+                case 256: launch_fused<256, N>(a); break;
+                default: return 3;
+            }
+        } else {
+            return 3;
+        }
     }
     return hipGetLastError() == hipSuccess ? 0 : 7;
 }

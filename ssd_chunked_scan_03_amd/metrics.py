@@ -14,6 +14,8 @@ counted once (es = bytes of the x/B/C dtype):
   k_state   x + B + cdt read + fp32 chunk states write
   k_scan    fp32 chunk states + chunk-end cdt + h0 read, entering states (es) + hT write
   k_out     x + C + cdt + C B^T blocks + entering states read, y write
+  k_bt      B read + per-chunk transposed B write
+  k_fused   x + C + transposed B + cdt + C B^T blocks + h0 read, y + hT write
 The path minimum is x + y + B + C + dt + h0 + hT, each touched once.
 """
 from __future__ import annotations
@@ -54,6 +56,8 @@ def kernel_bytes(b, T, H, P, N, G, Q, es, diag=False, h0=True) -> dict:
         "k_state": x + bc + cdt + st32,
         "k_scan": st32 + b * H * nc * 4 + (hstate if h0 else 0) + stx + hstate,
         "k_out": x + bc * (2 if diag else 1) + cdt + cbb + stx + x,
+        "k_bt": 0 if diag else 2 * bc,
+        "k_fused": 2 * x + 2 * bc + cdt + cbb + (2 if h0 else 1) * hstate,
     }
 
 

@@ -26,13 +26,13 @@ def upload(inp, dtype):
     return out
 
 
-def run_gpu(inp, dtype, chunk, diag, poison=True, return_ws=False):
+def run_gpu(inp, dtype, chunk, diag, poison=True, return_ws=False, flags=0):
     """One forward through the C ABI into NaN-poisoned outputs and workspace."""
     d = upload(inp, dtype)
     x, B = d["x"], d["B"]
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    prob = ssd.make_problem(b, T, H, P, N, G, chunk, ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32)
+    prob = ssd.make_problem(b, T, H, P, N, G, chunk, ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32, flags)
     y = torch.empty_like(x)
     hT = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(ssd.workspace_bytes(prob, diag), 1), dtype=torch.uint8, device="cuda")

@@ -48,9 +48,10 @@ def test_workspace_layout_arithmetic():
         assert lay["cb_bytes"] == (0 if diag else 2 * nc * 2 * 128 * 128 * 2)
         assert lay["states_bytes"] == 2 * 4 * nc * 64 * 128 * 4
         assert lay["hin_bytes"] == 2 * 4 * nc * 64 * 128 * 2
-        offs = [lay[k] for k in ("cdt_off", "cb_off", "states_off", "hin_off")]
+        assert lay["bt_bytes"] == (0 if diag else 2 * nc * 2 * 128 * 128 * 2)
+        offs = [lay[k] for k in ("cdt_off", "cb_off", "states_off", "hin_off", "bt_off")]
         assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
-        assert lay["total_bytes"] >= lay["hin_off"] + lay["hin_bytes"]
+        assert lay["total_bytes"] >= lay["bt_off"] + lay["bt_bytes"]
         assert ssd.workspace_bytes(p, diag) == lay["total_bytes"]
     assert ssd.workspace_bytes(prob(T=0)) == 0
     assert ssd.workspace_bytes(prob(b=0)) == 0
@@ -71,8 +72,8 @@ def test_workspace_bytes_rejects_bad_problems(kw, status):
 BASE = 1 << 40  # fake, never dereferenced device addresses
 
 
-def call(p, diag=False, **over):
-    """Call the entry point with fake well-formed pointers, some overridden."""
+def fake_ptrs(p, diag=False):
+    """Disjoint fake device addresses for every argument of problem p (never used)."""
     lay_bytes = max(ssd.workspace_bytes(p, diag), 1)
     b, T, H, P, N, G = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups
     es = 2 if p.dtype == ssd.SSD_BF16 else 4
@@ -83,6 +84,13 @@ def call(p, diag=False, **over):
     for k, n in sizes.items():
         ptrs[k] = cur
         cur += (n + (1 << 20)) // 4096 * 4096 + 4096
+    return ptrs, lay_bytes
+
+
+def call(p, diag=False, **over):
+    """Call the entry point with fake well-formed pointers, some overridden.  Every use
+    below makes the call invalid on purpose, so the host rejects it before any launch."""
+    ptrs, lay_bytes = fake_ptrs(p, diag)
     ptrs.update(over)
     ws_bytes = over.pop("ws_bytes", lay_bytes) if "ws_bytes" in over else lay_bytes
     fn = ssd._load().ssd_diag_scan_fwd if diag else ssd._load().ssd_scan_fwd
@@ -103,7 +111,7 @@ def test_error_paths_return_before_any_launch(diag):
     assert call(p, diag, hT=BASE + 4)[0] == ssd_status("SSD_ERR_ALIGN")
     assert call(p, diag, dt=BASE + 2)[0] == ssd_status("SSD_ERR_ALIGN")
     assert call(p, diag, ws=BASE + 16)[0] == ssd_status("SSD_ERR_ALIGN")
-    _, ptrs = call(prob(), diag)
+    ptrs, _ = fake_ptrs(prob(), diag)
     assert call(p, diag, y=ptrs["x"])[0] == ssd_status("SSD_ERR_ALIAS")
     assert call(p, diag, hT=ptrs["ws"])[0] == ssd_status("SSD_ERR_ALIAS")
     assert call(p, diag, hT=ptrs["y"])[0] == ssd_status("SSD_ERR_ALIAS")
@@ -118,6 +126,27 @@ def test_diag_output_kernel_lds_limit_is_unsupported():
     """The diagonal-decay output kernel keeps rescaled C and B rows of a chunk in LDS;
     a (chunk, dstate) pair that does not fit 160 KiB is reported, not launched."""
     assert call(prob(P=64, N=256, Q=256), True)[0] == ssd_status("SSD_ERR_UNSUPPORTED")
+
+
+def test_schedule_flags_validated():
+    p = prob()
+    p.flags = ssd.SCHEDULE_SPLIT | ssd.SCHEDULE_FUSED
+    assert call(p)[0] == ssd_status("SSD_ERR_UNSUPPORTED")
+    p.flags = 0x400
+    assert call(p)[0] == ssd_status("SSD_ERR_UNSUPPORTED")
+    p = prob(P=32)
+    p.flags = ssd.SCHEDULE_FUSED   # no fused kernel for headdim 32: rejected before any launch
+    assert call(p)[0] == ssd_status("SSD_ERR_UNSUPPORTED")
+    p = prob(dtype=ssd.SSD_F32)
+    p.flags = ssd.SCHEDULE_FUSED
+    assert call(p)[0] == ssd_status("SSD_ERR_UNSUPPORTED")
+
+
+def test_schedule_choice():
+    assert ssd.schedule_of(prob(b=8, H=80, N=128, G=1), False) == "fused"
+    assert ssd.schedule_of(prob(b=2, H=48, N=128, G=1), False) == "split"
+    assert ssd.schedule_of(prob(b=8, H=80, N=128, G=1), True) == "split"
+    assert ssd.schedule_of(prob(b=8, H=80, N=256, G=1), False) == "split"
 
 
 def test_empty_batch_is_a_no_op():

@@ -57,7 +57,7 @@ def test_stage_outputs_match_oracle_dumps(dtype, diag):
     cumulative step, C B^T blocks (lower part), chunk states, entering states."""
     b, T, H, P, N, G, Q = 2, 300, 4, 32, 64, 2, 128
     inp = make_small(b, T, H, P, N, G, seed=77, diag=diag, dtype=dtype)
-    y, hT, ws, prob = run_gpu(inp, dtype, Q, diag, return_ws=True)
+    y, hT, ws, prob = run_gpu(inp, dtype, Q, diag, return_ws=True, flags=ssd.SCHEDULE_SPLIT)
     _, _, st = oracle.chunked(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"],
                               Q=Q, diag=diag, dumps=True)
     lay = ssd.workspace_layout(prob, diag)
@@ -87,6 +87,42 @@ def test_stage_outputs_match_oracle_dumps(dtype, diag):
     check((y, hT), oracle_ref(inp, diag), dtype, "stage case end-to-end")
 
 
+FUSED = [  # b, T, H, P, N, G, Q, h0, D   (bf16, scalar decay; fused schedule forced)
+    (1, 64, 1, 64, 64, 1, 64, False, False),
+    (2, 300, 4, 64, 128, 2, 128, True, True),
+    (1, 700, 3, 64, 128, 1, 256, True, True),
+    (2, 1000, 2, 64, 64, 1, 256, True, False),
+    (1, 257, 8, 64, 128, 4, 64, False, True),
+    (3, 512, 2, 64, 128, 2, 256, True, True),
+    (1, 1, 2, 64, 128, 1, 256, True, True),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "b{}T{}H{}P{}N{}G{}Q{}".format(*c[:7]))
+def test_fused_schedule_matches_oracle(case):
+    """The fused per-(batch, head) kernel (state kept on chip across chunks)."""
+    b, T, H, P, N, G, Q, h0, D = case
+    print(f"[fused case] {case}", flush=True)
+    inp = make_small(b, T, H, P, N, G, seed=2000 + T + N, dtype="bf16", h0=h0, D=D)
+    check(run_gpu(inp, "bf16", Q, False, flags=ssd.SCHEDULE_FUSED), oracle_ref(inp, False), "bf16", str(case))
+
+
+def test_fused_and_split_agree():
+    """Both schedules on the same inputs agree within the bf16 bar (not bitwise: the
+    fused kernel rounds the carried state to bf16 only as an MFMA operand)."""
+    inp = make_small(2, 777, 4, 64, 128, 1, seed=31, dtype="bf16")
+    yf, hf = run_gpu(inp, "bf16", 256, False, flags=ssd.SCHEDULE_FUSED)
+    ys, hs = run_gpu(inp, "bf16", 256, False, flags=ssd.SCHEDULE_SPLIT)
+    assert rel_y(yf, ys) < TOL["bf16"] and rel_h(hf, hs) < TOL["bf16"]
+
+
+def test_fused_unsupported_is_reported():
+    inp = make_small(1, 64, 2, 32, 64, 1, seed=1, dtype="bf16")
+    with pytest.raises(ssd.SSDError) as e:
+        run_gpu(inp, "bf16", 64, False, flags=ssd.SCHEDULE_FUSED)
+    assert e.value.status == 3
+
+
 @pytest.mark.parametrize("w", [TINY_F32, M780, DIAG], ids=lambda w: w.name)
 def test_workload_full_parity(w):
     print(f"[workload] {w.name}", flush=True)
@@ -94,10 +130,10 @@ def test_workload_full_parity(w):
     check(run_gpu(inp, w.dtype, w.chunk, w.diag), oracle_ref(inp, w.diag), w.dtype, w.name)
 
 
-def sampled_parity(w, inp, chunk, pairs):
+def sampled_parity(w, inp, chunk, pairs, flags=0):
     """Full-size run on the GPU; the oracle recomputes the sampled (batch, head) pairs,
     each an independent SSM."""
-    y, hT = run_gpu(inp, w.dtype, chunk, w.diag)
+    y, hT = run_gpu(inp, w.dtype, chunk, w.diag, flags=flags)
     assert not np.isnan(y).any() and not np.isnan(hT).any()
     for bi, h in pairs:
         s = slice_inputs(inp, bi, h, w.nheads, w.ngroups)
@@ -107,12 +143,15 @@ def sampled_parity(w, inp, chunk, pairs):
         assert ey < TOL[w.dtype] and eh < TOL[w.dtype], (w.name, chunk, bi, h, ey, eh)
 
 
-def test_headline_workload_sampled_parity():
-    """Mamba-2 2.7B layer shape (b8 T4096 H80 P64 N128, Q256, nonzero h0), 6 sampled heads."""
+@pytest.mark.parametrize("schedule", ["default", "split"])
+def test_headline_workload_sampled_parity(schedule):
+    """Mamba-2 2.7B layer shape (b8 T4096 H80 P64 N128, Q256, nonzero h0), 6 sampled heads;
+    the default schedule here is the fused one (640 (batch, head) chains)."""
     w = M2P7B
-    print(f"[workload] {w.name}", flush=True)
+    print(f"[workload] {w.name} {schedule}", flush=True)
     inp = make_inputs(w)
-    sampled_parity(w, inp, w.chunk, [(0, 0), (0, 79), (3, 17), (5, 40), (7, 3), (7, 78)])
+    flags = ssd.SCHEDULE_SPLIT if schedule == "split" else 0
+    sampled_parity(w, inp, w.chunk, [(0, 0), (0, 79), (3, 17), (5, 40), (7, 3), (7, 78)], flags)
 
 
 @pytest.mark.parametrize("chunk", LONG_CHUNKS)
