@@ -13,7 +13,6 @@ on a bounded sample of the same workload on this host's cores.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -26,18 +25,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, published
 FP32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix cores, published
-KERNEL_SOURCES = ["ssd_chunked_scan_03_amd/csrc/kernels.hpp", "ssd_chunked_scan_03_amd/csrc/device.hpp",
-                  "ssd_chunked_scan_03_amd/csrc/fused.hpp", "ssd_chunked_scan_03_amd/csrc/launch.hpp"]
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
+COPY_BYTES = 512 << 20      # size of the calibration copy (bytes read = bytes written)
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
     current kernel sources; else None."""
@@ -46,37 +34,29 @@ def measured_traffic(kernel: str, workload: str):
         return None
     with open(path) as f:
         d = json.load(f)
+    from ssd_chunked_scan_03_amd.metrics import kernel_source_hash
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s=15.0):
-    """The fp64 oracle (step-by-step recurrence) on batch row 0 and the first k heads at
-    full length, k sized to about `budget_s` of work; scaled to whole-layer tokens/s."""
-    import numpy as np
+def cpu_baseline(w, inp, budget_s=12.0):
+    """The fp64 oracle (step-by-step recurrence) over the whole workload, repeated until
+    about `budget_s` of wall time has passed; whole-layer tokens/s on this host's cores."""
     import oracle
-    threads = len(os.sched_getaffinity(0))
-    g = lambda a, hs: None if a is None else np.ascontiguousarray(a[hs])
-
-    def run(k):
-        sl = slice(0, k)
-        s = dict(x=inp["x"][0:1, :, sl], dt=inp["dt"][0:1, :, sl], A=inp["A"][sl],
-                 B=inp["B"][0:1, :, 0:1], C=inp["C"][0:1, :, 0:1], D=inp["D"][sl],
-                 h0=None if inp["h0"] is None else inp["h0"][0:1, sl])
-        if w.ngroups != 1:
-            raise ValueError("cpu baseline sample assumes one B/C group")
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = max(1, min(threads, len(os.sched_getaffinity(0))))
+    reps, total = 0, 0.0
+    while total < budget_s:
         t0 = time.perf_counter()
-        oracle.recurrence(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["h0"], diag=w.diag,
+        oracle.recurrence(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"], diag=w.diag,
                           nthreads=threads)
-        return time.perf_counter() - t0
-    t1 = run(1)
-    k = int(max(1, min(w.nheads, budget_s / max(t1, 1e-3))))
-    tk = run(k) if k > 1 else t1
-    tokens_equiv = w.seqlen * k / w.nheads
-    return {"value": tokens_equiv / tk, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"batch row 0, heads 0..{k - 1} of {w.nheads}, all {w.seqlen} tokens "
-                      f"(= {tokens_equiv:.0f} whole-layer tokens) in {tk:.2f} s; fp64 recurrence"}
+        total += time.perf_counter() - t0
+        reps += 1
+    tokens = w.batch * w.seqlen * reps
+    return {"value": round(tokens / total, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole workload ({w.batch} x {w.seqlen} tokens, {w.nheads} heads), {reps} pass(es) "
+                      f"in {total:.2f} s; fp64 step-by-step recurrence, OpenMP over (batch, head, headdim block)"}
 
 
 def main():
@@ -88,6 +68,11 @@ def main():
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--kernel-steps", type=int, default=None, help="launches per kernel timing")
+    ap.add_argument("--schedule", choices=["auto", "split", "fused"], default="auto",
+                    help="kernel schedule (auto: the library's choice for the shape)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed work, stream 512 MiB through a plain elementwise kernel "
+                         "(calibrates the byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -118,7 +103,8 @@ def main():
     h0 = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).to(dev)
     b, T, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     dcode = ssd.SSD_BF16 if w.dtype == "bf16" else ssd.SSD_F32
-    prob = ssd.make_problem(b, T, H, P, N, G, Q, dcode)
+    sched_flag = {"auto": 0, "split": ssd.SCHEDULE_SPLIT, "fused": ssd.SCHEDULE_FUSED}[args.schedule]
+    prob = ssd.make_problem(b, T, H, P, N, G, Q, dcode, flags=sched_flag)
     y = torch.empty_like(x)
     hT = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
     ws = torch.empty(ssd.workspace_bytes(prob, w.diag), dtype=torch.uint8, device=dev)
@@ -154,7 +140,7 @@ def main():
         bit = ssd.STAGES[name]
         if w.diag and name == "k_cb":
             continue
-        pk = ssd.make_problem(b, T, H, P, N, G, Q, dcode, flags=bit)
+        pk = ssd.make_problem(b, T, H, P, N, G, Q, dcode, flags=bit | sched_flag)
         for _ in range(3):
             step(pk)
         torch.cuda.synchronize()
@@ -168,6 +154,13 @@ def main():
                          "GBps": round(kb[name] / (kms * 1e-3) / 1e9, 1)}
     step()  # leave y/hT from a full forward
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)  # one streaming kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     dk = kernels[dom]
     traffic = measured_traffic(dom, w.name)
@@ -202,7 +195,7 @@ def main():
         "path_hbm_frac": round(min_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roof,
         "kernels": kernels,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": metrics.kernel_source_hash(),
     }
     if not args.no_cpu:
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)

@@ -83,13 +83,14 @@ typedef struct {
 /* Schedules.  The library runs one of two kernel sequences:
  *   fused  k_cumsum, k_cb, k_bt, then k_fused: one work-group per (batch, head) walks its
  *          chunks in order with the state held on chip (scalar decay, bf16, headdim 64,
- *          dstate 64 or 128, and at least 512 (batch, head) pairs to fill the GPU);
+ *          dstate 64 or 128);
  *   split  k_cumsum, k_cb (scalar decay), k_state, k_scan, k_out: every stage is a
  *          separate chunk-parallel launch and chunk states go through the workspace.
- * flags = 0 picks fused where it applies, else split.  SSD_SCHEDULE_SPLIT forces split
- * (every intermediate then lands in the workspace); SSD_SCHEDULE_FUSED forces fused
- * regardless of the (batch, head) count, and is SSD_ERR_UNSUPPORTED where the fused
- * kernel does not exist (other dtype, decay, headdim or dstate).
+ * flags = 0 runs fused where it exists and there are at least 512 (batch, head) chains
+ * to fill the GPU (one work-group each), else split.  SSD_SCHEDULE_SPLIT asks for split
+ * explicitly; SSD_SCHEDULE_FUSED asks for fused at any (batch, head) count and is
+ * SSD_ERR_UNSUPPORTED where the fused kernel does not exist (other dtype, decay,
+ * headdim or dstate).
  *
  * Diagnostics only (per-kernel timing and per-stage inspection): a nonzero stage mask
  * in the low byte of `flags` enqueues just those kernels; their inputs are read from the

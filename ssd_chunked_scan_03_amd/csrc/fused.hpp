@@ -31,12 +31,28 @@ namespace ssd {
 template <int Q, int N>
 struct FusedCfg {
     static constexpr int P = 64;
-    static constexpr int RPW = Q / 64;  // row tiles per wave
-    static constexpr int SN = N / 64;   // state n-tiles per wave
-    static constexpr int XR = Q / 32;   // 16-byte x vectors per thread and chunk
-    static constexpr int HSW = (N / 8) < 16 ? (N / 8) : 16;
+    static constexpr int RPW = Q / 64;            // row tiles per wave
+    static constexpr int TPP = RPW >= 2 ? 2 : 1;  // row tiles per output pass
+    static constexpr int NPASS = RPW / TPP;       // output passes per chunk
+    // C B^T fragments (16 rows x 32 columns) one pass needs: the two tiles of a pass
+    // together always cover Q/32 + 1 of them; a single tile at most 2
+    static constexpr int NU = TPP == 2 ? Q / 32 + 1 : 2;
+    static constexpr int SN = N / 64;             // state n-tiles per wave
+    static constexpr int KS = Q / 32;             // k-steps per chunk
+    static constexpr int XR = Q / 32;             // 16-byte x vectors per thread and chunk
+    static constexpr int NF = N / 32;             // C fragments per row tile
     static constexpr size_t lds_bytes = (size_t)Q * P * 2 + (size_t)P * N * 2 + 3 * Q * 4;
 };
+
+// Row tile t of output pass `pass` for wave w.  Tiles r and (Q/16 - 1 - r)-style partners
+// are paired so that every pass of every wave holds the same number of causal fragments:
+// Q = 256: (w, 15 - w) then (7 - w, 8 + w); Q = 128: (w, 7 - w); Q = 64: (w).
+template <int Q>
+__device__ __forceinline__ int fused_tile(int pass, int t, int w) {
+    if (Q == 256) return pass == 0 ? (t == 0 ? w : 15 - w) : (t == 0 ? 7 - w : 8 + w);
+    if (Q == 128) return t == 0 ? w : 7 - w;
+    return w;
+}
 
 // element offset of x(j, p) in the swizzled x tile (64 bf16 = 128 B per row, 16-byte
 // chunks).  A transpose read touches 4 consecutive rows x 32 B per 16-lane group, and two
@@ -73,6 +89,18 @@ __device__ __forceinline__ int hs_off(int p, int n) {
     return p * N + ((((n >> 3) ^ (p % HSW))) << 3) + (n & 7);
 }
 
+// Direct-to-LDS transfer m (1 KB) of a chunk's x tile fills LDS bytes [1024 m, 1024 m + 1024)
+// lane by lane: x-tile rows 8 m .. 8 m + 7, eight 16-byte slots each.  Lane l takes row
+// 8 m + l/8 and slot l % 8; the row swizzle decides which column chunk that slot holds.
+// Within the row the swizzle depends on (l/8) & 3 and on one bit of m (bit 0 ^ bit 1), so
+// a lane needs two source offsets, one per value of that bit; the row offset is uniform.
+__device__ __forceinline__ int xs_dma_lane(int lane, int bit, int XS, int hcol) {
+    const int r = lane >> 3, slot = lane & 7;
+    const int ch = ((((slot >> 1) ^ (r & 3) ^ bit)) << 1) | (slot & 1);
+    return r * XS + hcol + ch * 16;
+}
+__device__ __forceinline__ int xs_dma_bit(int m) { return (m ^ (m >> 1)) & 1; }
+
 template <int Q, int N>
 __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ x, const bf16* __restrict__ Cm,
                                                     const bf16* __restrict__ cb, const bf16* __restrict__ Bt,
@@ -81,7 +109,9 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
                                                     bf16* __restrict__ y, float* __restrict__ hT, int64_t Tn,
                                                     int H, int G, int nc, int BH) {
     typedef FusedCfg<Q, N> CF;
-    constexpr int P = 64, RPW = CF::RPW, SN = CF::SN, XR = CF::XR;
+    constexpr int P = 64, TPP = CF::TPP, NPASS = CF::NPASS, NU = CF::NU, SN = CF::SN, KS = CF::KS,
+                  XR = CF::XR, NF = CF::NF;
+    constexpr int NU0 = NU < 5 ? NU : 5;  // C B^T fragments requested together with the C rows
     constexpr float LOG2E = 1.4426950408889634f;
     __shared__ __attribute__((aligned(16))) bf16 Xs[Q * P];
     __shared__ __attribute__((aligned(16))) bf16 Hs[P * N];
@@ -105,22 +135,18 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
     const brsrc rcb = make_rsrc(cb + bi * (int64_t)nc * G * Q * Q, (uint32_t)((int64_t)nc * G * Q * Q * 2));
     const brsrc rbt = make_rsrc(Bt + bi * (int64_t)nc * G * N * Q, (uint32_t)((int64_t)nc * G * N * Q * 2));
     const int XS = H * P * 2, CS = G * N * 2;                     // row strides in bytes
-    // per-lane byte offsets, the same for every unit
-    const int vx = (tid >> 3) * XS + h * P * 2 + (tid & 7) * 16;  // x prefetch: row tid/8, 8 p
+    // per-lane byte offsets
     const int vc = l16 * CS + g * N * 2 + q * 16;                  // C row l16 of a row tile
-    const int vq = (l16 * Q + 8 * q) * 2;                          // cb / Bt row l16, k-group q
+    const int vq = (l16 * Q + 8 * q) * 2;                          // C B^T / B^T row l16, k-group q
+    const int vq1 = vq + 16 * Q * 2;                               // B^T rows of the next n-tile
     const int vy = l16 * XS + h * P * 2 + q * 8;                   // y row l16, p 4q..4q+3
 
-    auto row_tile = [&](int kk) { return (RPW == 1) ? w : ((kk & 1) ? 8 * (kk >> 1) + 7 - w : 8 * (kk >> 1) + w); };
-    int rts[RPW];  // this wave's row tiles
-#pragma unroll
-    for (int t = 0; t < RPW; ++t) rts[t] = row_tile(t);
     // lane-constant LDS offsets: x fragments per p-tile, H rows per 32-wide n-step
-    int xo[4], ho[N / 32];
+    int xo[4], ho[NF];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) xo[pt] = xs_off(8 * q + ((lane & 15) >> 2), pt * 16 + 4 * (lane & 3));
 #pragma unroll
-    for (int n = 0; n < N / 32; ++n) ho[n] = hs_off<N>(l16, n * 32 + 8 * q);
+    for (int n = 0; n < NF; ++n) ho[n] = hs_off<N>(l16, n * 32 + 8 * q);
 
     // state accumulators: lane holds H^T[n = (w SN + a) 16 + 4q + r][p = pt 16 + l16]
     f32x4 acc_h[SN][4];
@@ -132,13 +158,40 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             acc_h[a][pt] = h0 ? ld4(h0 + (bh * P + p) * N + n) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-    bf16x8 xv[XR];
-    float cdv = 0.f, cdr = 0.f, cdl = 0.f;
-    // next chunk's x rows (zero past T) and cdt -> registers
-    auto prefetch_x = [&](int c) {
-        const int s0 = __builtin_amdgcn_readfirstlane(c * Q * XS);
+    // ---- what one output pass reads from global memory ----
+    struct Front {                 // requested before the pass starts
+        bf16x8 cf[TPP][NF];        //   C rows of the pass's tiles (state term)
+        bf16x8 gf[NU0];            //   the first C B^T fragments
+    };
+    auto pass_tiles = [&](int pass, int& tA, int& tB) {
+        tA = fused_tile<Q>(pass, 0, w);
+        tB = TPP == 2 ? fused_tile<Q>(pass, 1, w) : tA;
+        // opaque per call: the offsets derived from the tile indices are recomputed each
+        // chunk instead of being hoisted out of the chunk loop (and spilled)
+        asm volatile("" : "+s"(tA), "+s"(tB));
+    };
+    // byte offset (in the C B^T resource) of fragment u of a pass with tiles tA, tB
+    auto gf_off = [&](int c, int u, int tA, int tB) {
+        const int KA = tA / 2 + 1;
+        const bool inA = TPP == 1 || u < KA;
+        const int tile = inA ? tA : tB;
+        const int ks = TPP == 1 ? min(u, KA - 1) : (inA ? u : u - KA);
+        return __builtin_amdgcn_readfirstlane(((c * G + g) * Q * Q + tile * 16 * Q + ks * 32) * 2);
+    };
+    auto issue_front = [&](Front& f, int c, int pass) {
+        int tA, tB;
+        pass_tiles(pass, tA, tB);
 #pragma unroll
-        for (int r = 0; r < XR; ++r) xv[r] = bload8(rx, vx, s0 + r * 32 * XS);
+        for (int t = 0; t < TPP; ++t) {
+            const int sb = __builtin_amdgcn_readfirstlane((c * Q + (t == 0 ? tA : tB) * 16) * CS);
+#pragma unroll
+            for (int n = 0; n < NF; ++n) f.cf[t][n] = bload8(rc, vc, sb + n * 64);
+        }
+#pragma unroll
+        for (int u = 0; u < NU0; ++u) f.gf[u] = bload8(rcb, vq, gf_off(c, u, tA, tB));
+    };
+    float cdv = 0.f, cdr = 0.f, cdl = 0.f;
+    auto load_cdt = [&](int c) {
         const float* cd = cdt + (bh * nc + c) * (int64_t)Q;
         if (tid < Q) {
             cdv = cd[tid];
@@ -146,41 +199,39 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
         }
         cdl = cd[Q - 1];
     };
-
-    // ---- the chunk's output in passes of up to two row tiles; pass 0 also carries the state
-    //      update over every k-step.  Per k-step operands (C B^T rows of the pass's tiles, B^T
-    //      rows of the state) are requested one k-step ahead. ----
-    constexpr int KS = Q / 32;
-    constexpr int NPASS = (RPW + 1) / 2;
-    constexpr int TPP = RPW < 2 ? RPW : 2;  // row tiles per pass
-    const int vq1 = vq + 16 * Q * 2;        // Bt rows of the second n-tile
-    struct KOps {
-        bf16x8 gb[TPP];   // C B^T row fragment of each of the pass's row tiles
-        bf16x8 bt[SN];    // B^T fragments of the wave's n-tiles (pass 0)
+    // chunk c's x rows straight into the (swizzled) x tile; rows past T arrive as zeros
+    const int vd0 = xs_dma_lane(lane, 0, XS, h * P * 2), vd1 = xs_dma_lane(lane, 1, XS, h * P * 2);
+    auto dma_x = [&](int c) {
+#pragma unroll
+        for (int r = 0; r < XR; ++r) {
+            const int m = w * XR + r;
+            const int s0 = __builtin_amdgcn_readfirstlane((c * Q + 8 * m) * XS);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(Xs + m * 512), 16,
+                                                     xs_dma_bit(m) ? vd1 : vd0, s0, 0, 0);
+        }
     };
 
-    prefetch_x(0);
+    Front fr;
+    issue_front(fr, 0, 0);
+    load_cdt(0);
+    dma_x(0);
 
     for (int c = 0; c < nc; ++c) {
         const int64_t t0 = (int64_t)c * Q;
-        __syncthreads();  // the previous chunk is done with Xs, Hs and the tables
-#pragma unroll
-        for (int r = 0; r < XR; ++r) {
-            const int v = tid + r * kThreads;
-            const int jj = v >> 3, ch = v & 7;
-            st8(Xs + xs_off(jj, ch * 8), xv[r]);
-        }
+        int wc = w;  // opaque per chunk, as in pass_tiles: lane addresses derived from the
+        asm volatile("" : "+s"(wc));  // wave index are rebuilt here rather than kept live
+        // per-chunk tables and the entering state H_c -> Hs (bf16); the previous chunk's
+        // closing barrier has freed them
         if (tid < Q) {
             cds[tid] = cdv;
-            w2[tid] = exp2f_fast(ah2 * (cdl - cdv));
-            u2[tid] = exp2f_fast(ah2 * (cdr - cdv));
+            w2[tid] = exp2f_fast(ah2 * (cdl - cdv));  // decay from row j to the chunk end
+            u2[tid] = exp2f_fast(ah2 * (cdr - cdv));  // decay from row j to its 32-row block end
         }
-        // entering state H_c -> Hs (bf16), read by the state term
 #pragma unroll
         for (int a = 0; a < SN; ++a)
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
-                const int p = pt * 16 + l16, n = (w * SN + a) * 16 + 4 * q;
+                const int p = pt * 16 + l16, n = (wc * SN + a) * 16 + 4 * q;
                 st4(Hs + hs_off<N>(p, n),
                     bf16x4{(bf16)acc_h[a][pt][0], (bf16)acc_h[a][pt][1], (bf16)acc_h[a][pt][2], (bf16)acc_h[a][pt][3]});
             }
@@ -191,117 +242,135 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) acc_h[a][pt] *= dch;
 
+        // ---- output passes ----
 #pragma unroll
         for (int pass = 0; pass < NPASS; ++pass) {
-            const bool su = pass == 0;  // the state update rides on the first pass
-            if (pass == NPASS - 1 && NPASS > 1 && c + 1 < nc) prefetch_x(c + 1);  // long lead
-            int prt[TPP];               // the pass's row tiles
-#pragma unroll
-            for (int t = 0; t < TPP; ++t) prt[t] = rts[pass * 2 + t];
-            int kend = 0;  // k-steps this pass needs
-#pragma unroll
-            for (int t = 0; t < TPP; ++t) kend = max(kend, prt[t] / 2 + 1);
-            if (su) kend = KS;
+            int tA, tB;
+            pass_tiles(pass, tA, tB);
+            const int KA = tA / 2 + 1, KB = tB / 2 + 1;  // k-steps of each tile (last = diagonal)
+            if (pass > 0) issue_front(fr, c, pass);
+            __builtin_amdgcn_sched_barrier(0);
 
-            auto load_kops = [&](KOps& o, int ks) {
-                const int sbq = __builtin_amdgcn_readfirstlane(((c * G + g) * Q * Q + ks * 32) * 2);
-#pragma unroll
-                for (int t = 0; t < TPP; ++t)
-                    if (ks <= prt[t] / 2) o.gb[t] = bload8(rcb, vq, sbq + prt[t] * 16 * Q * 2);
-                if (su) {
-                    const int sbt = __builtin_amdgcn_readfirstlane(((c * G + g) * N * Q + w * SN * 16 * Q + ks * 32) * 2);
-#pragma unroll
-                    for (int a = 0; a < SN; ++a) o.bt[a] = bload8(rbt, a == 0 ? vq : vq1, sbt);
-                }
-            };
-            KOps ops[2];
-            load_kops(ops[0], 0);
-
-            // state term: y^T[p][i] = exp(A cdt_i) sum_n H_c[p][n] C_i[n]
+            // state term of the pass's tiles: y^T[p][i] = exp(A cdt_i) sum_n H_c[p][n] C_i[n]
             f32x4 acc[TPP][4];
 #pragma unroll
-            for (int t = 0; t < TPP; ++t) {
-                bf16x8 cf[N / 32];
-                const int sb = __builtin_amdgcn_readfirstlane((c * Q + prt[t] * 16) * CS);
-#pragma unroll
-                for (int n = 0; n < N / 32; ++n) cf[n] = bload8(rc, vc, sb + n * 64);
+            for (int t = 0; t < TPP; ++t)
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) acc[t][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int n = 0; n < N / 32; ++n)
+            for (int n = 0; n < NF; ++n)
 #pragma unroll
-                    for (int pt = 0; pt < 4; ++pt)
-                        acc[t][pt] = mma(acc[t][pt], ld8(Hs + ho[n] + pt * 16 * N), cf[n]);
-                const float sc = exp2f_fast(ah2 * cds[prt[t] * 16 + l16]);
+                for (int pt = 0; pt < 4; ++pt) {
+                    const bf16x8 hf = ld8(Hs + ho[n] + pt * 16 * N);
+#pragma unroll
+                    for (int t = 0; t < TPP; ++t) acc[t][pt] = mma(acc[t][pt], hf, fr.cf[t][n]);
+                }
+#pragma unroll
+            for (int t = 0; t < TPP; ++t) {
+                const float sc = exp2f_fast(ah2 * cds[(t == 0 ? tA : tB) * 16 + l16]);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) acc[t][pt] *= sc;
             }
-
-            // k-steps: one read of each x fragment feeds the state update and the pass's tiles
-            auto kstep = [&](KOps& o, KOps& nxt, int ks) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (ks + 1 < kend) load_kops(nxt, ks + 1);
-                __builtin_amdgcn_sched_barrier(0);
-                const int j0 = ks * 32 + 8 * q;
-                bf16x8* mf = o.gb;  // masked in place
-                bf16x8* af = o.bt;  // weighted in place
-#pragma unroll
-                for (int t = 0; t < TPP; ++t) {
-                    const int rt = prt[t], i = rt * 16 + l16, nks = rt / 2 + 1;
-                    if (ks < nks) {
-                        const float ci = cds[i];
-                        if (ks < nks - 1) {
-                            const float vi = exp2f_fast(ah2 * (ci - cds[ks * 32 + 31]));
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) mf[t][e] = (bf16)((float)mf[t][e] * (u2[j0 + e] * vi));
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const int j = j0 + e;
-                                // exponent clamped to <= 0 so the unused (j > i) slots stay finite
-                                float m = (float)mf[t][e] * exp2f_fast(fminf(ah2 * (ci - cds[j]), 0.f));
-                                m = (j <= i) ? m : 0.f;
-                                m += (j == i) ? Dh : 0.f;
-                                mf[t][e] = (bf16)m;
-                            }
-                        }
-                    }
-                }
-                if (su)
-#pragma unroll
-                    for (int a = 0; a < SN; ++a)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) af[a][e] = (bf16)((float)af[a][e] * w2[j0 + e]);
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const bf16x8 xf = frag_xs_o(Xs, xo[pt], ks * 32);
-                    if (su)
-#pragma unroll
-                        for (int a = 0; a < SN; ++a) acc_h[a][pt] = mma(acc_h[a][pt], af[a], xf);
-#pragma unroll
-                    for (int t = 0; t < TPP; ++t)
-                        if (ks <= prt[t] / 2) acc[t][pt] = mma(acc[t][pt], xf, mf[t]);
-                }
-            };
-#pragma unroll 1
-            for (int ks = 0; ks < kend; ks += 2) {
-                kstep(ops[0], ops[1], ks);
-                if (ks + 1 < kend) kstep(ops[1], ops[0], ks + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (pass == 0) {
+                // this wave's x transfers are done; after the barrier every wave's are
+                __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+                __syncthreads();
             }
-
-            // y rows (dropped past T), non-temporal: this lane has 4 consecutive p per p-tile
+            // the remaining C B^T fragments of the pass
+            bf16x8 gf[NU];
 #pragma unroll
-            for (int t = 0; t < TPP; ++t) {
-                const int sy = __builtin_amdgcn_readfirstlane((int)((t0 + prt[t] * 16) * XS));
+            for (int u = 0; u < NU0; ++u) gf[u] = fr.gf[u];
+#pragma unroll
+            for (int u = NU0; u < NU; ++u) gf[u] = bload8(rcb, vq, gf_off(c, u, tA, tB));
+            __builtin_amdgcn_sched_barrier(0);
+
+            auto store_y = [&](const f32x4* a, int tile) {
+                const int sy = __builtin_amdgcn_readfirstlane((int)((t0 + tile * 16) * XS));
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
                     __builtin_amdgcn_raw_buffer_store_b64(
-                        __builtin_bit_cast(u32x2, bf16x4{(bf16)acc[t][pt][0], (bf16)acc[t][pt][1],
-                                                         (bf16)acc[t][pt][2], (bf16)acc[t][pt][3]}),
+                        __builtin_bit_cast(u32x2, bf16x4{(bf16)a[pt][0], (bf16)a[pt][1], (bf16)a[pt][2], (bf16)a[pt][3]}),
                         ry, vy, sy + pt * 32, 2);
+            };
+
+            // C B^T fragments in order: tile A's k-steps, then tile B's.  The running tile's
+            // accumulators are acc[0]; when tile A is done its y rows are stored and tile B's
+            // accumulators move in.
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const bool inA = TPP == 1 || u < KA;
+                if (TPP == 1 && u >= KA) break;
+                if (TPP == 2 && u == KA) {
+                    store_y(acc[0], tA);
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) acc[0][pt] = acc[TPP - 1][pt];
+                }
+                const int tile = inA ? tA : tB;
+                const int ks = inA ? u : u - KA;
+                const int kd = (inA ? KA : KB) - 1;  // the tile's diagonal k-step
+                const int i = tile * 16 + l16, j0 = ks * 32 + 8 * q;
+                const float ci = cds[i];
+                bf16x8 m = gf[u];
+                if (ks < kd) {
+                    // below the diagonal block: exp(A (cdt_i - cdt_j)) = u2_j * v_i, both <= 1
+                    const float vi = exp2f_fast(ah2 * (ci - cds[ks * 32 + 31]));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) m[e] = (bf16)((float)m[e] * (u2[j0 + e] * vi));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = j0 + e;
+                        // exponent clamped to <= 0 so the unused (j > i) slots stay finite
+                        float v = (float)m[e] * exp2f_fast(fminf(ah2 * (ci - cds[j]), 0.f));
+                        v = (j <= i) ? v : 0.f;
+                        v += (j == i) ? Dh : 0.f;
+                        m[e] = (bf16)v;
+                    }
+                }
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) acc[0][pt] = mma(acc[0][pt], frag_xs_o(Xs, xo[pt], ks * 32), m);
+            }
+            store_y(acc[0], TPP == 2 ? tB : tA);
+        }
+
+        // ---- state update H_{c+1} = exp(A cdt_last) H_c + B^T diag(w) X_c, B^T fragments
+        //      requested two k-steps ahead; the next chunk's first reads go out behind them ----
+        __builtin_amdgcn_sched_barrier(0);
+        const int sbt = __builtin_amdgcn_readfirstlane(((c * G + g) * N * Q + w * SN * 16 * Q) * 2);
+        bf16x8 bt[3][SN];
+#pragma unroll
+        for (int ks = 0; ks < 2 && ks < KS; ++ks)
+#pragma unroll
+            for (int a = 0; a < SN; ++a) bt[ks][a] = bload8(rbt, a == 0 ? vq : vq1, sbt + ks * 64);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 2 < KS) {
+#pragma unroll
+                for (int a = 0; a < SN; ++a) bt[(ks + 2) % 3][a] = bload8(rbt, a == 0 ? vq : vq1, sbt + (ks + 2) * 64);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const int j0 = ks * 32 + 8 * q;
+            bf16x8 bw[SN];
+#pragma unroll
+            for (int a = 0; a < SN; ++a)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bw[a][e] = (bf16)((float)bt[ks % 3][a][e] * w2[j0 + e]);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const bf16x8 xf = frag_xs_o(Xs, xo[pt], ks * 32);
+#pragma unroll
+                for (int a = 0; a < SN; ++a) acc_h[a][pt] = mma(acc_h[a][pt], bw[a], xf);
             }
         }
-        if (NPASS == 1 && c + 1 < nc) prefetch_x(c + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 1 < nc) {
+            issue_front(fr, c + 1, 0);
+            load_cdt(c + 1);
+        }
+        __syncthreads();  // every wave is done with Xs, Hs and the tables of this chunk
+        if (c + 1 < nc) dma_x(c + 1);
     }
     if (hT) {
 #pragma unroll

@@ -64,3 +64,19 @@ def kernel_bytes(b, T, H, P, N, G, Q, es, diag=False, h0=True) -> dict:
 def path_min_bytes(b, T, H, P, N, G, es, h0=True) -> int:
     return 2 * b * T * H * P * es + 2 * b * T * G * N * es + b * T * H * 4 + \
         (2 if h0 else 1) * b * H * P * N * 4
+
+
+KERNEL_SOURCES = ("kernels.hpp", "device.hpp", "fused.hpp", "launch.hpp")
+
+
+def kernel_source_hash() -> str:
+    """Short digest of the kernel sources: a counter summary taken on other sources no
+    longer describes the built kernels."""
+    import hashlib
+    import os
+    h = hashlib.sha256()
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(here, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]

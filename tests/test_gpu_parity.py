@@ -145,8 +145,8 @@ def sampled_parity(w, inp, chunk, pairs, flags=0):
 
 @pytest.mark.parametrize("schedule", ["default", "split"])
 def test_headline_workload_sampled_parity(schedule):
-    """Mamba-2 2.7B layer shape (b8 T4096 H80 P64 N128, Q256, nonzero h0), 6 sampled heads;
-    the default schedule here is the fused one (640 (batch, head) chains)."""
+    """Mamba-2 2.7B layer shape (b8 T4096 H80 P64 N128, Q256, nonzero h0), 6 sampled heads,
+    with the default schedule (fused: 640 (batch, head) chains) and with the split one."""
     w = M2P7B
     print(f"[workload] {w.name} {schedule}", flush=True)
     inp = make_inputs(w)
