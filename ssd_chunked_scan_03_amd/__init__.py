@@ -102,7 +102,7 @@ def fused_supported(dtype_code, diag, P, N) -> bool:
 def schedule_of(prob: "Problem", diag: bool) -> str:
     """The schedule the library runs for flags without a stage mask."""
     if prob.flags & SCHEDULE_SPLIT:
-        return "fused" if ok and prob.batch * prob.nheads >= 512 else "split"
+        return "split"
     ok = fused_supported(prob.dtype, diag, prob.headdim, prob.dstate)
     if prob.flags & SCHEDULE_FUSED:
         return "fused" if ok else "unsupported"

@@ -147,6 +147,8 @@ def test_schedule_choice():
     assert ssd.schedule_of(prob(b=2, H=48, N=128, G=1), False) == "split"
     assert ssd.schedule_of(prob(b=8, H=80, N=128, G=1), True) == "split"
     p = prob(b=8, H=80, N=128, G=1)
+    p.flags = ssd.SCHEDULE_SPLIT
+    assert ssd.schedule_of(p, False) == "split"
     p.flags = ssd.SCHEDULE_FUSED
     assert ssd.schedule_of(p, False) == "fused"
     assert ssd.schedule_of(p, True) == "unsupported"
