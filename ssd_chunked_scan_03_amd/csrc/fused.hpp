@@ -191,23 +191,31 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
         for (int u = 0; u < NU0; ++u) f.gf[u] = bload8(rcb, vq, gf_off(c, u, tA, tB));
     };
     float cdv = 0.f, cdr = 0.f, cdl = 0.f;
+    // cdt of this (b, h): one resource, 32-bit offsets (no 64-bit lane addresses to keep)
+    const brsrc rcd = make_rsrc(cdt + bh * nc * (int64_t)Q, (uint32_t)(nc * Q * 4));
     auto load_cdt = [&](int c) {
-        const float* cd = cdt + (bh * nc + c) * (int64_t)Q;
-        if (tid < Q) {
-            cdv = cd[tid];
-            cdr = cd[tid | 31];
-        }
-        cdl = cd[Q - 1];
+        int tl = tid;  // opaque: the lane offsets below are rebuilt per call, not kept live
+        asm volatile("" : "+v"(tl));
+        const int sc = __builtin_amdgcn_readfirstlane(c * Q * 4);
+        // lanes past Q read in bounds (clamped) and ignore the value
+        const int tc = min(tl, Q - 1);
+        cdv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rcd, tc * 4, sc, 0));
+        cdr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rcd, (tc | 31) * 4, sc, 0));
+        cdl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rcd, 0, sc + (Q - 1) * 4, 0));
     };
-    // chunk c's x rows straight into the (swizzled) x tile; rows past T arrive as zeros
-    const int vd0 = xs_dma_lane(lane, 0, XS, h * P * 2), vd1 = xs_dma_lane(lane, 1, XS, h * P * 2);
+    // chunk c's x rows straight into the (swizzled) x tile; rows past T arrive as zeros.
+    // x is read once, so it is fetched non-temporal and leaves the L2 to the per-chunk
+    // tables that every head of the batch row reads.
     auto dma_x = [&](int c) {
+        int ln = lane;  // opaque: the two lane offsets are rebuilt per call, not kept live
+        asm volatile("" : "+v"(ln));
+        const int vd0 = xs_dma_lane(ln, 0, XS, h * P * 2), vd1 = xs_dma_lane(ln, 1, XS, h * P * 2);
 #pragma unroll
         for (int r = 0; r < XR; ++r) {
             const int m = w * XR + r;
             const int s0 = __builtin_amdgcn_readfirstlane((c * Q + 8 * m) * XS);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(Xs + m * 512), 16,
-                                                     xs_dma_bit(m) ? vd1 : vd0, s0, 0, 0);
+                                                     xs_dma_bit(m) ? vd1 : vd0, s0, 0, 2);
         }
     };
 
@@ -222,10 +230,12 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
         asm volatile("" : "+s"(wc));  // wave index are rebuilt here rather than kept live
         // per-chunk tables and the entering state H_c -> Hs (bf16); the previous chunk's
         // closing barrier has freed them
-        if (tid < Q) {
-            cds[tid] = cdv;
-            w2[tid] = exp2f_fast(ah2 * (cdl - cdv));  // decay from row j to the chunk end
-            u2[tid] = exp2f_fast(ah2 * (cdr - cdv));  // decay from row j to its 32-row block end
+        int tl = tid;  // opaque per chunk (see load_cdt)
+        asm volatile("" : "+v"(tl));
+        if (tl < Q) {
+            cds[tl] = cdv;
+            w2[tl] = exp2f_fast(ah2 * (cdl - cdv));  // decay from row j to the chunk end
+            u2[tl] = exp2f_fast(ah2 * (cdr - cdv));  // decay from row j to its 32-row block end
         }
 #pragma unroll
         for (int a = 0; a < SN; ++a)
@@ -285,13 +295,16 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             for (int u = NU0; u < NU; ++u) gf[u] = bload8(rcb, vq, gf_off(c, u, tA, tB));
             __builtin_amdgcn_sched_barrier(0);
 
+            // A y store covers 32 bytes of each of 16 rows; ordinary (write-back) stores let
+            // the L2 merge a row's four stores into whole lines before they reach HBM (as
+            // streaming stores they left as partial lines and doubled the write traffic).
             auto store_y = [&](const f32x4* a, int tile) {
                 const int sy = __builtin_amdgcn_readfirstlane((int)((t0 + tile * 16) * XS));
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
                     __builtin_amdgcn_raw_buffer_store_b64(
                         __builtin_bit_cast(u32x2, bf16x4{(bf16)a[pt][0], (bf16)a[pt][1], (bf16)a[pt][2], (bf16)a[pt][3]}),
-                        ry, vy, sy + pt * 32, 2);
+                        ry, vy, sy + pt * 32, 0);
             };
 
             // C B^T fragments in order: tile A's k-steps, then tile B's.  The running tile's
