@@ -168,6 +168,27 @@ def main():
             "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes": dk["bytes"], "avg_launch_ms": dk["ms"]}
 
+    # one decode step (ssd_step, seqlen 1) at the same batch, heads and state size: the
+    # state is read and written once, so it is timed against HBM bandwidth
+    es = 2 if w.dtype == "bf16" else 4
+    hstate = (h0.clone() if h0 is not None else torch.zeros((b, H, P, N), dtype=torch.float32, device=dev))
+    xs, dts, Bs, Cs = x[:, :1].contiguous(), dt[:, :1].contiguous(), B[:, :1].contiguous(), C[:, :1].contiguous()
+    ys = torch.empty_like(xs)
+    sprob = ssd.make_problem(b, 1, H, P, N, G, Q, dcode)
+    for _ in range(3):
+        ssd.step_into(sprob, w.diag, xs, dts, A, Bs, Cs, D, hstate, ys, stream.cuda_stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(ksteps):
+        ssd.step_into(sprob, w.diag, xs, dts, A, Bs, Cs, D, hstate, ys, stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sms = e0.elapsed_time(e1) / ksteps
+    sbytes = 2 * 4 * b * H * P * N + 2 * es * b * H * P + 2 * es * b * G * N + 4 * b * H
+    decode = {"us": round(sms * 1e3, 2), "bytes": sbytes, "GBps": round(sbytes / (sms * 1e-3) / 1e9, 1),
+              "hbm_frac": round(sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+              "tokens_per_s": round(b / (sms * 1e-3), 1)}
+
     fl = metrics.flops(b, T, H, P, N, G, Q, w.diag)
     tokens = b * T
     tflops = fl["total"] / (ms * 1e-3) / 1e12
@@ -195,6 +216,7 @@ def main():
         "path_hbm_frac": round(min_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roof,
         "kernels": kernels,
+        "decode_step": decode,
         "kernel_source_hash": metrics.kernel_source_hash(),
     }
     if not args.no_cpu:

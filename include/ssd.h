@@ -147,6 +147,32 @@ int ssd_diag_scan_fwd(const ssd_problem* p, const void* x, const float* dt, cons
                       void* y, float* hT, void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
+/* The recurrence itself, token by token, on a state the caller holds (the linear form of
+ * the same map: "Structured State Space Duality" concept page, section "The recurrence as
+ * one matrix"; section "When it breaks" on serving with this form).  For t = 0 .. seqlen-1:
+ *
+ *     h <- a_t h + x_t B_t^T,    y_t = h C_t + D_h x_t,
+ *
+ * with a_t = exp(dt_t A_h) (ssd_step) or exp(dt_t A_{h,n}) per state dimension
+ * (ssd_diag_step).  A decode step is seqlen = 1; longer sequences run the tokens in
+ * order (results agree with ssd_scan_fwd on the same tokens up to rounding, not
+ * bitwise).
+ *
+ *   x, y, dt, A, B, C, D   as for ssd_scan_fwd (same layouts and dtypes; D may be NULL);
+ *   h                      [batch, nheads, headdim, dstate] float32, read and overwritten
+ *                          in place: the state before the first token on entry, the
+ *                          state after the last on return.
+ * `chunk` is ignored; `flags` must be 0.  No workspace.  headdim in {16,32,64,128},
+ * dstate in {16,32,64,128,256}.  batch = 0 or seqlen = 0 leaves h untouched.
+ * Errors as for ssd_scan_fwd: NULL pointers, h not 16-byte aligned, B/C not aligned to
+ * 4 elements, y or h overlapping an input or each other, unsupported sizes -- all
+ * reported before any HIP call. */
+int ssd_step(const ssd_problem* p, const void* x, const float* dt, const float* A,
+             const void* B, const void* C, const float* D, float* h, void* y, void* stream);
+int ssd_diag_step(const ssd_problem* p, const void* x, const float* dt, const float* A,
+                  const void* B, const void* C, const float* D, float* h, void* y,
+                  void* stream);
+
 const char* ssd_status_string(int status);
 
 /* SSD_VERSION of the built library. */

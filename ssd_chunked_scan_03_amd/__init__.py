@@ -28,7 +28,7 @@ SSD_F32, SSD_BF16 = 0, 1
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_ALIGN", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_workspace_bytes", "ssd_get_workspace_layout", "ssd_scan_fwd", "ssd_diag_scan_fwd",
-           "ssd_status_string", "ssd_version")
+           "ssd_step", "ssd_diag_step", "ssd_status_string", "ssd_version")
 
 
 class SSDError(RuntimeError):
@@ -68,6 +68,9 @@ def _load():
     lib.ssd_get_workspace_layout.restype = ci
     for f in (lib.ssd_scan_fwd, lib.ssd_diag_scan_fwd):
         f.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp]
+        f.restype = ci
+    for f in (lib.ssd_step, lib.ssd_diag_step):
+        f.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, vp]
         f.restype = ci
     lib.ssd_status_string.argtypes = [ci]
     lib.ssd_status_string.restype = ctypes.c_char_p
@@ -188,3 +191,32 @@ def scan_fwd(x, dt, A, B, C, D=None, h0=None, chunk=256, return_final_state=True
 def diag_scan_fwd(x, dt, A, B, C, D=None, h0=None, chunk=128, return_final_state=True, workspace=None):
     """Diagonal-decay SSD forward (a_{t,n} = exp(dt_t A_{h,n})). Returns (y, hT)."""
     return _forward(True, x, dt, A, B, C, D, h0, chunk, return_final_state, workspace)
+
+
+def step_into(prob: Problem, diag: bool, x, dt, A, B, C, D, h, y, stream=None) -> None:
+    """Enqueue the token-by-token recurrence over prob.seqlen tokens: h (float32
+    [b, H, P, N]) is updated in place, y receives the outputs.  No allocation."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    lib = _load()
+    fn = lib.ssd_diag_step if diag else lib.ssd_step
+    st = fn(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h), _ptr(y),
+            ctypes.c_void_p(int(stream)))
+    if st:
+        raise SSDError(st, "ssd_diag_step" if diag else "ssd_step")
+
+
+def step(x, dt, A, B, C, h, D=None, diag=None):
+    """Decode: run the recurrence over x's tokens on state h (updated in place).
+    x [b, T, H, P] (bf16 or f32), dt [b, T, H] f32, A [H] or [H, N] f32, B/C [b, T, G, N],
+    h [b, H, P, N] f32.  Returns y [b, T, H, P]."""
+    import torch
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if diag is None:
+        diag = A.dim() == 2
+    prob = make_problem(b, T, H, P, N, G, 64, _dtype_code(x))
+    y = torch.empty_like(x)
+    step_into(prob, diag, x, dt, A, B, C, D, h, y)
+    return y

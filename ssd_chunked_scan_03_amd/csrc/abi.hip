@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include "launch.hpp"
+#include "step.hpp"
 #include "ssd.h"
 
 namespace {
@@ -146,9 +147,54 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     return p->dtype == SSD_BF16 ? ssd::run_bf16(a) : ssd::run_f32(a);
 }
 
+// The token-by-token recurrence on a caller-held state (ssd_step / ssd_diag_step).
+int step(const ssd_problem* p, int diag, const void* x, const float* dt, const float* A, const void* B,
+         const void* C, const float* D, float* h, void* y, void* stream) {
+    if (!p) return SSD_ERR_NULL;
+    if (p->batch < 0 || p->seqlen < 0 || p->nheads <= 0 || p->headdim <= 0 || p->dstate <= 0 ||
+        p->ngroups <= 0 || p->nheads % p->ngroups != 0)
+        return SSD_ERR_SHAPE;
+    if (p->dtype != SSD_F32 && p->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (!pn_supported(p->headdim, p->dstate) || p->flags != 0) return SSD_ERR_UNSUPPORTED;
+    const int64_t b = p->batch, T = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups;
+    if (b * H > 0x7fffffffLL || b * T * H * P > ((int64_t)1 << 40)) return SSD_ERR_UNSUPPORTED;
+    if (b == 0 || T == 0) return SSD_OK;  // nothing to do: h is left as it is
+    if (!x || !dt || !A || !B || !C || !h || !y) return SSD_ERR_NULL;
+    const size_t es = esize(p->dtype);
+    if (!aligned(h, 16) || !aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) || !aligned(x, es) ||
+        !aligned(y, es) || !aligned(B, 4 * es) || !aligned(C, 4 * es))
+        return SSD_ERR_ALIGN;
+    const Range ins[] = {{x, (size_t)(b * T * H * P) * es},
+                         {dt, (size_t)(b * T * H) * 4},
+                         {A, (size_t)(diag ? H * N : H) * 4},
+                         {B, (size_t)(b * T * G * N) * es},
+                         {C, (size_t)(b * T * G * N) * es},
+                         {D, D ? (size_t)H * 4 : 0}};
+    const Range rh = {h, (size_t)(b * H * P * N) * 4}, ry = {y, (size_t)(b * T * H * P) * es};
+    for (const Range& r : ins)
+        if (overlap(ry, r) || overlap(rh, r)) return SSD_ERR_ALIAS;
+    if (overlap(ry, rh)) return SSD_ERR_ALIAS;
+    ssd::StepArgs a;
+    a.b = b; a.T = T; a.H = H; a.P = P; a.N = N; a.G = G;
+    a.diag = diag;
+    a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.h = h; a.y = y;
+    a.stream = (hipStream_t)stream;
+    return p->dtype == SSD_BF16 ? ssd::run_step<ssd::bf16>(a) : ssd::run_step<float>(a);
+}
+
 }  // namespace
 
 extern "C" {
+
+int ssd_step(const ssd_problem* p, const void* x, const float* dt, const float* A, const void* B,
+             const void* C, const float* D, float* h, void* y, void* stream) {
+    return step(p, 0, x, dt, A, B, C, D, h, y, stream);
+}
+
+int ssd_diag_step(const ssd_problem* p, const void* x, const float* dt, const float* A, const void* B,
+                  const void* C, const float* D, float* h, void* y, void* stream) {
+    return step(p, 1, x, dt, A, B, C, D, h, y, stream);
+}
 
 size_t ssd_workspace_bytes(const ssd_problem* p, int diag) {
     if (check_problem(p)) return 0;

@@ -163,3 +163,36 @@ def test_empty_batch_is_a_no_op():
 
 def ssd_status(name):
     return {v: k for k, v in ssd.STATUS.items()}[name]
+
+
+def call_step(p, diag=False, **over):
+    """ssd_step / ssd_diag_step with fake well-formed pointers, some overridden (every use
+    below is invalid on purpose, so the host rejects it before any launch)."""
+    ptrs, _ = fake_ptrs(p, diag)
+    ptrs["h"] = ptrs.pop("h0")
+    ptrs.update(over)
+    fn = ssd._load().ssd_diag_step if diag else ssd._load().ssd_step
+    v = lambda k: ctypes.c_void_p(ptrs[k]) if ptrs[k] else None
+    return fn(ctypes.byref(p), v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"), v("h"), v("y"), None)
+
+
+@pytest.mark.parametrize("diag", [False, True])
+def test_step_error_paths(diag):
+    p = prob(T=1)
+    assert call_step(p, diag, x=0) == ssd_status("SSD_ERR_NULL")
+    assert call_step(p, diag, h=0) == ssd_status("SSD_ERR_NULL")
+    assert call_step(p, diag, h=BASE + 8) == ssd_status("SSD_ERR_ALIGN")
+    assert call_step(p, diag, B=BASE + 2) == ssd_status("SSD_ERR_ALIGN")
+    ptrs, _ = fake_ptrs(p, diag)
+    assert call_step(p, diag, y=ptrs["x"]) == ssd_status("SSD_ERR_ALIAS")
+    assert call_step(p, diag, h=ptrs["B"]) == ssd_status("SSD_ERR_ALIAS")
+    assert call_step(p, diag, y=ptrs["h0"]) == ssd_status("SSD_ERR_ALIAS")
+    assert call_step(prob(T=1, H=6, G=4), diag) == ssd_status("SSD_ERR_SHAPE")
+    assert call_step(prob(T=1, N=24), diag) == ssd_status("SSD_ERR_UNSUPPORTED")
+    q = prob(T=1)
+    q.flags = ssd.STAGE_CUMSUM
+    assert call_step(q, diag) == ssd_status("SSD_ERR_UNSUPPORTED")
+    # the chunk size plays no part in the recurrence: any value is accepted
+    assert call_step(prob(T=0, Q=7), diag) == 0
+    assert call_step(prob(b=0, T=1), diag) == 0
+    assert ssd._load().ssd_step(None, *([None] * 8), None) == ssd_status("SSD_ERR_NULL")
