@@ -106,7 +106,11 @@ def schedule_of(prob: "Problem", diag: bool) -> str:
     """The schedule the library runs for flags without a stage mask."""
     if prob.flags & SCHEDULE_SPLIT:
         return "split"
-    ok = fused_supported(prob.dtype, diag, prob.headdim, prob.dstate)
+    nc = (prob.seqlen + prob.chunk - 1) // prob.chunk
+    lim = 1 << 31  # the fused kernel's per-batch-row tables use 32-bit offsets
+    fits = (prob.seqlen * prob.nheads * prob.headdim * 2 < lim and prob.seqlen * prob.ngroups * prob.dstate * 2 < lim
+            and nc * prob.ngroups * prob.chunk * max(prob.chunk, prob.dstate) * 2 < lim)
+    ok = fused_supported(prob.dtype, diag, prob.headdim, prob.dstate) and fits
     if prob.flags & SCHEDULE_FUSED:
         return "fused" if ok else "unsupported"
     return "fused" if ok and prob.batch * prob.nheads >= 512 else "split"

@@ -114,6 +114,45 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
     const int l16 = lane & 15, q = lane >> 4;
     const int64_t tok0 = (int64_t)c * Q;
     const int jr = J * 64 + 16 * w + l16;
+    // (32-bit buffer offsets: the batch row's B / C must span less than 2 GiB)
+    if constexpr (sizeof(T) == 2 && N % 32 == 0) if (Tn * G * N * 2 < ((int64_t)1 << 31)) {
+        // bfloat16: branch-free buffer loads (rows past T read as zero), requested four
+        // k-steps ahead of the matrix-core step that consumes them
+        constexpr int KS = N / 32, DEPTH = KS < 4 ? KS : 4;
+        const uint32_t rowb = (uint32_t)(G * N * 2);
+        const brsrc rb = make_rsrc(Bm + bi * Tn * G * N, (uint32_t)(Tn * G * N * 2));
+        const brsrc rc = make_rsrc(Cm + bi * Tn * G * N, (uint32_t)(Tn * G * N * 2));
+        const int s0 = __builtin_amdgcn_readfirstlane((int)(tok0 * rowb + g * N * 2));
+        const int vb = jr * rowb + 16 * q;                     // B row jr, k-group q
+        const int vc = (I * 64 + l16) * rowb + 16 * q;          // C row I*64 + l16 (+ 16 ct rows)
+        bf16x8 fb[KS], fc[KS][4];
+        auto load = [&](int ks) {
+            fb[ks] = bload8(rb, vb, s0 + ks * 64);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) fc[ks][ct] = bload8(rc, vc, s0 + ks * 64 + ct * 16 * (int)rowb);
+        };
+        f32x4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DEPTH; ++ks) load(ks);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + DEPTH < KS) load(ks + DEPTH);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) acc[ct] = mma(acc[ct], fb[ks], fc[ks][ct]);
+        }
+        T* out = cb + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
+        const int j0 = J * 64 + 16 * w + 4 * q;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const int i = I * 64 + 16 * ct + l16;
+            st4(out + (int64_t)i * Q + j0, bf16x4{(bf16)acc[ct][0], (bf16)acc[ct][1], (bf16)acc[ct][2], (bf16)acc[ct][3]});
+        }
+        return;
+    }
     const bool jv = tok0 + jr < Tn;
     const T* brow = Bm + ((bi * Tn + tok0 + (jv ? jr : 0)) * G + g) * N;
     f32x4 acc[4];

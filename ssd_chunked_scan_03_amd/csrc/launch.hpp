@@ -33,7 +33,12 @@ struct RunArgs {
 // The fused per-(batch, head) schedule: bf16, scalar decay, P = 64, N in {64, 128},
 // and enough (batch, head) chains to occupy every CU several times over.
 inline bool fused_supported(const RunArgs& a, bool bf16_dtype) {
-    return bf16_dtype && !a.diag && a.P == 64 && (a.N == 64 || a.N == 128);
+    // the fused kernel addresses a batch row's x / y, C, C B^T and B^T tables through
+    // buffer resources with 32-bit offsets: each must span less than 2 GiB
+    const int64_t lim = (int64_t)1 << 31;
+    const bool fits = a.T * a.H * a.P * 2 < lim && a.T * a.G * a.N * 2 < lim &&
+                      a.nc * a.G * a.Q * a.Q * 2 < lim && a.nc * a.G * a.N * a.Q * 2 < lim;
+    return bf16_dtype && !a.diag && a.P == 64 && (a.N == 64 || a.N == 128) && fits;
 }
 inline bool fused_applies(const RunArgs& a, bool bf16_dtype) {
     return fused_supported(a, bf16_dtype) && !a.force_split && (a.force_fused || a.b * a.H >= 512);
