@@ -101,6 +101,15 @@ __device__ __forceinline__ int xs_dma_lane(int lane, int bit, int XS, int hcol) 
 }
 __device__ __forceinline__ int xs_dma_bit(int m) { return (m ^ (m >> 1)) & 1; }
 
+// Lane index recomputed from the execution mask (two VALU ops) instead of kept live:
+// values needed only at chunk boundaries are rebuilt there rather than spilled.
+__device__ __forceinline__ int lane_now() {
+    int l;
+    // volatile: recomputed where it is used, never hoisted and kept live
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 template <int Q, int N>
 __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ x, const bf16* __restrict__ Cm,
                                                     const bf16* __restrict__ cb, const bf16* __restrict__ Bt,
@@ -111,11 +120,12 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
     typedef FusedCfg<Q, N> CF;
     constexpr int P = 64, TPP = CF::TPP, NPASS = CF::NPASS, NU = CF::NU, SN = CF::SN, KS = CF::KS,
                   XR = CF::XR, NF = CF::NF;
-    constexpr int NU0 = NU < 5 ? NU : 5;  // C B^T fragments requested together with the C rows
+    constexpr int GW = NU < 4 ? NU : 4;  // C B^T fragments in flight ahead of the one in use
     constexpr float LOG2E = 1.4426950408889634f;
     __shared__ __attribute__((aligned(16))) bf16 Xs[Q * P];
     __shared__ __attribute__((aligned(16))) bf16 Hs[P * N];
     __shared__ float cds[Q], w2[Q], u2[Q];
+    __shared__ __attribute__((aligned(16))) float cdq[Q];  // the next chunk's cdt row, by transfer
 
     // blocks k, k+8, k+16, ... run on one XCD: give each XCD a contiguous range of (b, h)
     const int k = blockIdx.x;
@@ -160,8 +170,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
 
     // ---- what one output pass reads from global memory ----
     struct Front {                 // requested before the pass starts
-        bf16x8 cf[TPP][NF];        //   C rows of the pass's tiles (state term)
-        bf16x8 gf[NU0];            //   the first C B^T fragments
+        bf16x8 cf[NF];             //   C rows of the pass's first tile (state term)
+        bf16x8 gf[GW];             //   the first C B^T fragments
     };
     auto pass_tiles = [&](int pass, int& tA, int& tB) {
         tA = fused_tile<Q>(pass, 0, w);
@@ -181,27 +191,19 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
     auto issue_front = [&](Front& f, int c, int pass) {
         int tA, tB;
         pass_tiles(pass, tA, tB);
+        const int sb = __builtin_amdgcn_readfirstlane((c * Q + tA * 16) * CS);
 #pragma unroll
-        for (int t = 0; t < TPP; ++t) {
-            const int sb = __builtin_amdgcn_readfirstlane((c * Q + (t == 0 ? tA : tB) * 16) * CS);
+        for (int n = 0; n < NF; ++n) f.cf[n] = bload8(rc, vc, sb + n * 64);
 #pragma unroll
-            for (int n = 0; n < NF; ++n) f.cf[t][n] = bload8(rc, vc, sb + n * 64);
-        }
-#pragma unroll
-        for (int u = 0; u < NU0; ++u) f.gf[u] = bload8(rcb, vq, gf_off(c, u, tA, tB));
+        for (int u = 0; u < GW; ++u) f.gf[u] = bload8(rcb, vq, gf_off(c, u, tA, tB));
     };
-    float cdv = 0.f, cdr = 0.f, cdl = 0.f;
-    // cdt of this (b, h): one resource, 32-bit offsets (no 64-bit lane addresses to keep)
+    // the chunk's cdt row straight into LDS (wave 0, one 16-byte slot per lane), so no
+    // loaded value has to stay in registers across the chunk loop
     const brsrc rcd = make_rsrc(cdt + bh * nc * (int64_t)Q, (uint32_t)(nc * Q * 4));
-    auto load_cdt = [&](int c) {
-        int tl = tid;  // opaque: the lane offsets below are rebuilt per call, not kept live
-        asm volatile("" : "+v"(tl));
-        const int sc = __builtin_amdgcn_readfirstlane(c * Q * 4);
-        // lanes past Q read in bounds (clamped) and ignore the value
-        const int tc = min(tl, Q - 1);
-        cdv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rcd, tc * 4, sc, 0));
-        cdr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rcd, (tc | 31) * 4, sc, 0));
-        cdl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rcd, 0, sc + (Q - 1) * 4, 0));
+    auto dma_cdt = [&](int c) {
+        if (w == 0 && lane_now() * 4 < Q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rcd, (__attribute__((address_space(3))) void*)cdq, 16,
+                                                     lane_now() * 16, __builtin_amdgcn_readfirstlane(c * Q * 4), 0, 0);
     };
     // chunk c's x rows straight into the (swizzled) x tile; rows past T arrive as zeros.
     // x is read once, so it is fetched non-temporal and leaves the L2 to the per-chunk
@@ -221,32 +223,37 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
 
     Front fr;
     issue_front(fr, 0, 0);
-    load_cdt(0);
-    dma_x(0);
+    dma_cdt(0);
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): the cdt row is in place
+    __syncthreads();
 
+    // tables of a chunk from its cdt row (in cdq) and its entering state -> Hs; runs after
+    // the previous chunk's closing barrier and before the chunk's x transfer is issued
+    float dch = 1.f;
+    auto stage_tables = [&]() {
+            const int ln = lane_now(), tl = w * 64 + ln, lr = ln & 15, lq = ln >> 4;
+            const float cl = cdq[Q - 1];
+            dch = exp2f_fast(ah2 * cl);  // decay over the whole chunk
+            if (tl < Q) {
+                const float cv = cdq[tl], cr = cdq[tl | 31];
+                cds[tl] = cv;
+                w2[tl] = exp2f_fast(ah2 * (cl - cv));  // decay from row j to the chunk end
+                u2[tl] = exp2f_fast(ah2 * (cr - cv));  // decay from row j to its 32-row block end
+            }
+#pragma unroll
+            for (int a = 0; a < SN; ++a)
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int p = pt * 16 + lr, n = (w * SN + a) * 16 + 4 * lq;
+                    st4(Hs + hs_off<N>(p, n), bf16x4{(bf16)acc_h[a][pt][0], (bf16)acc_h[a][pt][1],
+                                                     (bf16)acc_h[a][pt][2], (bf16)acc_h[a][pt][3]});
+                }
+    };
+    stage_tables();
+    dma_x(0);
     for (int c = 0; c < nc; ++c) {
         const int64_t t0 = (int64_t)c * Q;
-        int wc = w;  // opaque per chunk, as in pass_tiles: lane addresses derived from the
-        asm volatile("" : "+s"(wc));  // wave index are rebuilt here rather than kept live
-        // per-chunk tables and the entering state H_c -> Hs (bf16); the previous chunk's
-        // closing barrier has freed them
-        int tl = tid;  // opaque per chunk (see load_cdt)
-        asm volatile("" : "+v"(tl));
-        if (tl < Q) {
-            cds[tl] = cdv;
-            w2[tl] = exp2f_fast(ah2 * (cdl - cdv));  // decay from row j to the chunk end
-            u2[tl] = exp2f_fast(ah2 * (cdr - cdv));  // decay from row j to its 32-row block end
-        }
-#pragma unroll
-        for (int a = 0; a < SN; ++a)
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int p = pt * 16 + l16, n = (wc * SN + a) * 16 + 4 * q;
-                st4(Hs + hs_off<N>(p, n),
-                    bf16x4{(bf16)acc_h[a][pt][0], (bf16)acc_h[a][pt][1], (bf16)acc_h[a][pt][2], (bf16)acc_h[a][pt][3]});
-            }
-        const float dch = exp2f_fast(ah2 * cdl);  // decay over the whole chunk
-        __syncthreads();
+        __syncthreads();  // the chunk's tables and Hs are in place
 #pragma unroll
         for (int a = 0; a < SN; ++a)
 #pragma unroll
@@ -261,38 +268,38 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             if (pass > 0) issue_front(fr, c, pass);
             __builtin_amdgcn_sched_barrier(0);
 
-            // state term of the pass's tiles: y^T[p][i] = exp(A cdt_i) sum_n H_c[p][n] C_i[n]
+            // the second tile's C rows, requested now and consumed after the first tile's
+            bf16x8 cfB[TPP == 2 ? NF : 1];
+            if (TPP == 2) {
+                const int sb = __builtin_amdgcn_readfirstlane((c * Q + tB * 16) * CS);
+#pragma unroll
+                for (int n = 0; n < NF; ++n) cfB[n] = bload8(rc, vc, sb + n * 64);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // state term, one tile at a time: y^T[p][i] = exp(A cdt_i) sum_n H_c[p][n] C_i[n]
             f32x4 acc[TPP][4];
 #pragma unroll
-            for (int t = 0; t < TPP; ++t)
+            for (int t = 0; t < TPP; ++t) {
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) acc[t][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int n = 0; n < NF; ++n)
+                for (int n = 0; n < NF; ++n)
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const bf16x8 hf = ld8(Hs + ho[n] + pt * 16 * N);
-#pragma unroll
-                    for (int t = 0; t < TPP; ++t) acc[t][pt] = mma(acc[t][pt], hf, fr.cf[t][n]);
-                }
-#pragma unroll
-            for (int t = 0; t < TPP; ++t) {
+                    for (int pt = 0; pt < 4; ++pt)
+                        acc[t][pt] = mma(acc[t][pt], ld8(Hs + ho[n] + pt * 16 * N), t == 0 ? fr.cf[n] : cfB[n]);
                 const float sc = exp2f_fast(ah2 * cds[(t == 0 ? tA : tB) * 16 + l16]);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) acc[t][pt] *= sc;
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
             if (pass == 0) {
                 // this wave's x transfers are done; after the barrier every wave's are
                 __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
                 __syncthreads();
             }
-            // the remaining C B^T fragments of the pass
             bf16x8 gf[NU];
 #pragma unroll
-            for (int u = 0; u < NU0; ++u) gf[u] = fr.gf[u];
-#pragma unroll
-            for (int u = NU0; u < NU; ++u) gf[u] = bload8(rcb, vq, gf_off(c, u, tA, tB));
+            for (int u = 0; u < GW; ++u) gf[u] = fr.gf[u];
             __builtin_amdgcn_sched_barrier(0);
 
             // A y store covers 32 bytes of each of 16 rows; ordinary (write-back) stores let
@@ -312,6 +319,9 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             // accumulators move in.
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (u + GW < NU) gf[u + GW] = bload8(rcb, vq, gf_off(c, u + GW, tA, tB));
+                __builtin_amdgcn_sched_barrier(0);
                 const bool inA = TPP == 1 || u < KA;
                 if (TPP == 1 && u >= KA) break;
                 if (TPP == 2 && u == KA) {
@@ -347,8 +357,11 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             store_y(acc[0], TPP == 2 ? tB : tA);
         }
 
+        // the next chunk's cdt row: every wave read this chunk's at the chunk top
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 1 < nc) dma_cdt(c + 1);
         // ---- state update H_{c+1} = exp(A cdt_last) H_c + B^T diag(w) X_c, B^T fragments
-        //      requested two k-steps ahead; the next chunk's first reads go out behind them ----
+        //      requested two k-steps ahead ----
         __builtin_amdgcn_sched_barrier(0);
         const int sbt = __builtin_amdgcn_readfirstlane(((c * G + g) * N * Q + w * SN * 16 * Q) * 2);
         bf16x8 bt[3][SN];
@@ -378,12 +391,13 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (c + 1 < nc) {
-            issue_front(fr, c + 1, 0);
-            load_cdt(c + 1);
-        }
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): the next cdt row has landed
+        if (c + 1 < nc) issue_front(fr, c + 1, 0);
         __syncthreads();  // every wave is done with Xs, Hs and the tables of this chunk
-        if (c + 1 < nc) dma_x(c + 1);
+        if (c + 1 < nc) {
+            stage_tables();
+            dma_x(c + 1);
+        }
     }
     if (hT) {
 #pragma unroll
