@@ -130,26 +130,30 @@ def main():
     print(f"[bench] {args.steps} steps: {ms:.4f} ms/step (host wall {wall * 1e3 / args.steps:.4f})",
           file=sys.stderr, flush=True)
 
-    # per-kernel average launch duration, HIP events on the same stream
+    # per-kernel average launch duration, HIP events on the same stream: a staged forward
+    # launches the forward's kernels in the forward's order, one stage per library call,
+    # with an event between stages, so each kernel runs on the cache state it meets in the
+    # forward itself
     kb = metrics.kernel_bytes(b, T, H, P, N, G, Q, 2 if w.dtype == "bf16" else 4, w.diag, h0 is not None)
     ksteps = args.kernel_steps or max(10, args.steps)
-    kernels = {}
     schedule = ssd.schedule_of(prob, w.diag)
-    names = ssd.FUSED_KERNELS if schedule == "fused" else ssd.SPLIT_KERNELS
-    for name in names:
-        bit = ssd.STAGES[name]
-        if w.diag and name == "k_cb":
-            continue
-        pk = ssd.make_problem(b, T, H, P, N, G, Q, dcode, flags=bit | sched_flag)
-        for _ in range(3):
+    names = [k for k in (ssd.FUSED_KERNELS if schedule == "fused" else ssd.SPLIT_KERNELS)
+             if not (w.diag and k == "k_cb")]
+    staged = [ssd.make_problem(b, T, H, P, N, G, Q, dcode, flags=ssd.STAGES[k] | sched_flag) for k in names]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(ksteps)]
+    for _ in range(2):
+        for pk in staged:
             step(pk)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(ksteps):
+    torch.cuda.synchronize()
+    for ev in evs:
+        for i, pk in enumerate(staged):
+            ev[i].record(stream)
             step(pk)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        kms = e0.elapsed_time(e1) / ksteps
+        ev[-1].record(stream)
+    torch.cuda.synchronize()
+    kernels = {}
+    for i, name in enumerate(names):
+        kms = sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / ksteps
         kernels[name] = {"ms": round(kms, 5), "bytes": kb[name],
                          "GBps": round(kb[name] / (kms * 1e-3) / 1e9, 1)}
     step()  # leave y/hT from a full forward
