@@ -146,7 +146,38 @@ int ssd_diag_scan_fwd(const ssd_problem* p, const void* x, const float* dt, cons
                       const void* B, const void* C, const float* D, const float* h0,
                       void* y, float* hT, void* ws, size_t ws_bytes, void* stream);
 
-/* Static text for a status code. */
+/* Packed variable-length sequences.  The batch holds `batch` sequences of different
+ * lengths back to back on one token axis of `seqlen` tokens: sequence s is tokens
+ * [cu_seqlens[s], cu_seqlens[s+1]).  Each sequence is a separate map with its own state
+ * ("Structured State Space Duality" concept page, section "The chunked algorithm takes
+ * both": the state passes from chunk to chunk within a sequence), so the result for
+ * sequence s equals ssd_scan_fwd on that sequence alone, up to rounding.  Chunks restart
+ * at each sequence's first token.
+ *
+ *   x, y            [seqlen, nheads, headdim]   (the batch dimension is the packing)
+ *   dt              [seqlen, nheads] float32
+ *   B, C            [seqlen, ngroups, dstate]
+ *   A, D            [nheads] float32 (scalar decay; D may be NULL)
+ *   h0, hT          [batch, nheads, headdim, dstate] float32, one state per sequence
+ *                   (h0 NULL = zero; hT NULL = not written)
+ *   cu_seqlens      device int32 [batch + 1], nondecreasing from 0 to seqlen.  The
+ *                   library reads only clamped copies (each offset is clamped into
+ *                   [previous offset, seqlen]), so any values are memory-safe; offsets
+ *                   outside that contract give unspecified y and hT.  Empty sequences
+ *                   are allowed (their hT is their h0).
+ *
+ * Runs on the fused schedule: dtype SSD_BF16, headdim 64, dstate 64 or 128, scalar
+ * decay; any other problem, SSD_SCHEDULE_SPLIT, or a packed axis whose per-tensor spans
+ * reach 2 GiB returns SSD_ERR_UNSUPPORTED before any HIP call.  `ws` must hold
+ * ssd_varlen_workspace_bytes(p) bytes (0 for an empty problem); alignment and aliasing
+ * rules as for ssd_scan_fwd, and cu_seqlens must not overlap the workspace or outputs.
+ * Stage flags work as for ssd_scan_fwd (the row map is built with the cumsum stage). */
+size_t ssd_varlen_workspace_bytes(const ssd_problem* p);
+int ssd_scan_fwd_varlen(const ssd_problem* p, const int32_t* cu_seqlens, const void* x,
+                        const float* dt, const float* A, const void* B, const void* C,
+                        const float* D, const float* h0, void* y, float* hT, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* The recurrence itself, token by token, on a state the caller holds (the linear form of
  * the same map: "Structured State Space Duality" concept page, section "The recurrence as
  * one matrix"; section "When it breaks" on serving with this form).  For t = 0 .. seqlen-1:
@@ -173,6 +204,7 @@ int ssd_diag_step(const ssd_problem* p, const void* x, const float* dt, const fl
                   const void* B, const void* C, const float* D, float* h, void* y,
                   void* stream);
 
+/* Static text for a status code. */
 const char* ssd_status_string(int status);
 
 /* SSD_VERSION of the built library. */

@@ -10,7 +10,7 @@ Space Models" abstract; "Semiseparable Matrix Transformations" definition).
 Three independent forms of the same map, all in fp64:
 
 * :func:`recurrence` -- O1, the selective recurrence stepped token by token
-  (C, OpenMP);
+  (C, OpenMP); :func:`recurrence_packed` runs it per sequence of a packed batch;
 * :func:`quadratic`  -- O2, the materialised lower-triangular matrix M with
   explicit decay products (C), and :func:`quadratic_np`, a numpy twin of O2
   for tiny inputs;
@@ -104,6 +104,37 @@ def recurrence(x, dt, A, B, C, D=None, h0=None, diag=False, nthreads=None):
                                    nthreads or default_threads())
     if rc:
         raise ValueError("oracle_recurrence: bad dimensions")
+    return y, hT
+
+
+def recurrence_packed(x, dt, A, B, C, cu_seqlens, D=None, h0=None, diag=False, nthreads=None):
+    """O1 over packed variable-length sequences.  x [T,H,P], dt [T,H], B/C [T,G,N] hold
+    the sequences back to back, sequence s on tokens [cu[s], cu[s+1]); h0 [nseq,H,P,N]
+    (None: zero).  Each sequence is its own map with its own state, which the chunked
+    algorithm passes only between the chunks of one sequence ("Structured State Space
+    Duality" concept page, section "The chunked algorithm takes both"), so each slice
+    runs through :func:`recurrence` alone; an empty sequence keeps its initial state.
+    Returns (y [T,H,P], hT [nseq,H,P,N])."""
+    x = np.asarray(x)
+    cu = [int(v) for v in np.asarray(cu_seqlens)]
+    T, H, P = x.shape
+    N = np.asarray(B).shape[2]
+    nseq = len(cu) - 1
+    if cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must be nondecreasing from 0 to T")
+    y = np.zeros((T, H, P))
+    hT = np.zeros((nseq, H, P, N))
+    for s in range(nseq):
+        a, b = cu[s], cu[s + 1]
+        h0s = None if h0 is None else np.asarray(h0)[s:s + 1]
+        if a == b:
+            if h0s is not None:
+                hT[s] = h0s[0]
+            continue
+        ys, hs = recurrence(x[None, a:b], np.asarray(dt)[None, a:b], A, np.asarray(B)[None, a:b],
+                            np.asarray(C)[None, a:b], D, h0s, diag=diag, nthreads=nthreads)
+        y[a:b] = ys[0]
+        hT[s] = hs[0]
     return y, hT
 
 

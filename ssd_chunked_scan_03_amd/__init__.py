@@ -28,6 +28,7 @@ SSD_F32, SSD_BF16 = 0, 1
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_ALIGN", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_workspace_bytes", "ssd_get_workspace_layout", "ssd_scan_fwd", "ssd_diag_scan_fwd",
+           "ssd_varlen_workspace_bytes", "ssd_scan_fwd_varlen",
            "ssd_step", "ssd_diag_step", "ssd_status_string", "ssd_version")
 
 
@@ -69,6 +70,10 @@ def _load():
     for f in (lib.ssd_scan_fwd, lib.ssd_diag_scan_fwd):
         f.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp]
         f.restype = ci
+    lib.ssd_varlen_workspace_bytes.argtypes = [P]
+    lib.ssd_varlen_workspace_bytes.restype = sz
+    lib.ssd_scan_fwd_varlen.argtypes = [P, vp, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp]
+    lib.ssd_scan_fwd_varlen.restype = ci
     for f in (lib.ssd_step, lib.ssd_diag_step):
         f.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, vp]
         f.restype = ci
@@ -195,6 +200,56 @@ def scan_fwd(x, dt, A, B, C, D=None, h0=None, chunk=256, return_final_state=True
 def diag_scan_fwd(x, dt, A, B, C, D=None, h0=None, chunk=128, return_final_state=True, workspace=None):
     """Diagonal-decay SSD forward (a_{t,n} = exp(dt_t A_{h,n})). Returns (y, hT)."""
     return _forward(True, x, dt, A, B, C, D, h0, chunk, return_final_state, workspace)
+
+
+def varlen_workspace_bytes(prob: Problem) -> int:
+    return int(_load().ssd_varlen_workspace_bytes(ctypes.byref(prob)))
+
+
+def scan_fwd_varlen_into(prob: Problem, cu_seqlens, x, dt, A, B, C, D, h0, y, hT, ws, stream=None) -> None:
+    """Enqueue one packed variable-length forward (prob.batch sequences on one token axis
+    of prob.seqlen tokens) into caller-provided outputs and workspace (no allocation)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _load().ssd_scan_fwd_varlen(ctypes.byref(prob), _ptr(cu_seqlens), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(hT), _ptr(ws), nbytes,
+                                     ctypes.c_void_p(int(stream)))
+    if st:
+        raise SSDError(st, "ssd_scan_fwd_varlen")
+
+
+def scan_fwd_varlen(x, dt, A, B, C, cu_seqlens, D=None, h0=None, chunk=256, return_final_state=True,
+                    workspace=None):
+    """Scalar-decay SSD forward over packed sequences: x [T, H, P], dt [T, H], B/C [T, G, N]
+    hold the sequences back to back, sequence s on tokens [cu_seqlens[s], cu_seqlens[s+1])
+    (cu_seqlens: int32 GPU tensor of nseq + 1 offsets).  h0 / hT are [nseq, H, P, N].
+    Returns (y, hT)."""
+    import torch
+    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D), ("h0", h0),
+                    ("cu_seqlens", cu_seqlens)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise TypeError("cu_seqlens must be a 1-D int32 tensor of nseq + 1 offsets")
+    if not (x.dtype == B.dtype == C.dtype):
+        raise TypeError("x, B and C must share one dtype")
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if B.shape != (T, G, N) or C.shape != B.shape or dt.shape != (T, H) or A.shape != (H,):
+        raise ValueError("shape mismatch among x [T,H,P], dt [T,H], A [H], B/C [T,G,N]")
+    nseq = cu_seqlens.numel() - 1
+    prob = make_problem(nseq, T, H, P, N, G, chunk, _dtype_code(x))
+    y = torch.empty_like(x)
+    hT = torch.empty((nseq, H, P, N), dtype=torch.float32, device=x.device) if return_final_state else None
+    need = varlen_workspace_bytes(prob)
+    if need == 0 and nseq > 0 and T > 0:
+        raise SSDError(3, "ssd_scan_fwd_varlen (problem not supported for packed sequences)")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    scan_fwd_varlen_into(prob, cu_seqlens, x, dt, A, B, C, D, h0, y, hT, workspace)
+    return y, hT
 
 
 def step_into(prob: Problem, diag: bool, x, dt, A, B, C, D, h, y, stream=None) -> None:

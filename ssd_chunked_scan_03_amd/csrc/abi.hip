@@ -140,11 +140,129 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     a.states = reinterpret_cast<float*>(w + L.states_off);
     a.hin = static_cast<void*>(w + L.hin_off);
     a.bt = diag ? nullptr : static_cast<void*>(w + L.bt_off);
+    a.ts = nullptr; a.kb = nullptr; a.kcap = 0;
     a.stream = (hipStream_t)stream;
     a.stages = p->flags & SSD_STAGE_ALL;
     a.force_split = (p->flags & SSD_SCHEDULE_SPLIT) != 0;
     a.force_fused = (p->flags & SSD_SCHEDULE_FUSED) != 0;
     return p->dtype == SSD_BF16 ? ssd::run_bf16(a) : ssd::run_f32(a);
+}
+
+// ---- packed variable-length sequences (ssd_scan_fwd_varlen) ----
+// batch = number of sequences, seqlen = tokens of the packed axis.  Workspace: cdt
+// [H][kcap][Q] f32, C B^T [kcap][G][Q][Q] and B^T [kcap][G][N][Q] in the problem dtype,
+// then the row maps ts and kb (batch + 1 int32 each).  kcap = ceil(T/Q) + batch bounds
+// the chunks of all sequences together (each adds at most one partial chunk).
+struct VarlenLayout {
+    size_t cdt_off, cb_off, bt_off, ts_off, kb_off, total;
+    int64_t kcap;
+};
+
+VarlenLayout varlen_layout_of(const ssd_problem* p) {
+    VarlenLayout L;
+    memset(&L, 0, sizeof(L));
+    const int64_t Q = p->chunk, nseq = p->batch;
+    L.kcap = (p->seqlen + Q - 1) / Q + nseq;
+    const size_t es = esize(p->dtype), kc = (size_t)L.kcap;
+    size_t off = 0;
+    L.cdt_off = off;
+    off += align_up((size_t)p->nheads * kc * (size_t)Q * 4);
+    L.cb_off = off;
+    off += align_up(kc * (size_t)p->ngroups * (size_t)(Q * Q) * es);
+    L.bt_off = off;
+    off += align_up(kc * (size_t)p->ngroups * (size_t)(p->dstate * Q) * es);
+    L.ts_off = off;
+    off += align_up((size_t)(nseq + 1) * 4);
+    L.kb_off = off;
+    off += align_up((size_t)(nseq + 1) * 4);
+    L.total = (nseq == 0 || p->seqlen == 0) ? 0 : off;
+    return L;
+}
+
+// Packed sequences run on the fused schedule only: bf16, scalar decay, P = 64, N in
+// {64, 128}, and every buffer-resource span under 2 GiB.
+int check_varlen(const ssd_problem* p) {
+    const int st = check_problem(p);
+    if (st) return st;
+    if (p->flags & SSD_SCHEDULE_SPLIT) return SSD_ERR_UNSUPPORTED;
+    if (p->dtype != SSD_BF16 || p->headdim != 64 || (p->dstate != 64 && p->dstate != 128))
+        return SSD_ERR_UNSUPPORTED;
+    const int64_t T = p->seqlen, H = p->nheads, G = p->ngroups, N = p->dstate, Q = p->chunk;
+    const int64_t lim = (int64_t)1 << 31, kcap = (T + Q - 1) / Q + p->batch;
+    if (T * H * 64 * 2 >= lim || T * G * N * 2 >= lim || kcap * H * Q >= lim) return SSD_ERR_UNSUPPORTED;
+    if (kcap * G * Q * Q * 2 >= lim || kcap * G * N * Q * 2 >= lim) return SSD_ERR_UNSUPPORTED;
+    if (p->batch * H >= lim) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+int scan_varlen(const ssd_problem* p, const int* cu, const void* x, const float* dt, const float* A,
+                const void* B, const void* C, const float* D, const float* h0, void* y, float* hT,
+                void* ws, size_t ws_bytes, void* stream) {
+    int st = check_varlen(p);
+    if (st) return st;
+    const int64_t nseq = p->batch, T = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate,
+                  G = p->ngroups, Q = p->chunk;
+    const size_t es = esize(p->dtype);
+    const size_t state_bytes = (size_t)(nseq * H * P * N) * 4;
+    if (nseq == 0) return SSD_OK;
+    if (!A) return SSD_ERR_NULL;
+    if (!aligned(A, 4) || (D && !aligned(D, 4)) || (h0 && !aligned(h0, 16)) || (hT && !aligned(hT, 16)))
+        return SSD_ERR_ALIGN;
+    if (T == 0) {
+        // every sequence is empty: hT = h0 (or 0)
+        if (!hT) return SSD_OK;
+        if (overlap({hT, state_bytes}, {h0, state_bytes})) return SSD_ERR_ALIAS;
+        const int64_t n = nseq * H * P * N;
+        k_copy_state<<<(unsigned)((n + 255) / 256), 256, 0, (hipStream_t)stream>>>(h0, hT, n);
+        return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    }
+    if (!cu || !x || !dt || !B || !C || !y) return SSD_ERR_NULL;
+    if (!aligned(cu, 4) || !aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
+        !aligned(dt, 4))
+        return SSD_ERR_ALIGN;
+    const VarlenLayout L = varlen_layout_of(p);
+    if (!ws || ws_bytes < L.total) return SSD_ERR_WORKSPACE;
+    if (!aligned(ws, kAlign)) return SSD_ERR_ALIGN;
+    const size_t xb = (size_t)(T * H * P) * es;
+    const Range ins[] = {{x, xb},
+                         {dt, (size_t)(T * H) * 4},
+                         {A, (size_t)H * 4},
+                         {B, (size_t)(T * G * N) * es},
+                         {C, (size_t)(T * G * N) * es},
+                         {D, D ? (size_t)H * 4 : 0},
+                         {h0, h0 ? state_bytes : 0},
+                         {cu, (size_t)(nseq + 1) * 4},
+                         {ws, L.total}};
+    const Range ry = {y, xb}, rh = {hT, hT ? state_bytes : 0};
+    for (const Range& r : ins)
+        if (overlap(ry, r) || overlap(rh, r)) return SSD_ERR_ALIAS;
+    if (overlap(ry, rh)) return SSD_ERR_ALIAS;
+    if (overlap({cu, (size_t)(nseq + 1) * 4}, {ws, L.total})) return SSD_ERR_ALIAS;
+
+    char* w = static_cast<char*>(ws);
+    int* ts = reinterpret_cast<int*>(w + L.ts_off);
+    int* kb = reinterpret_cast<int*>(w + L.kb_off);
+    if (!(p->flags & SSD_STAGE_ALL) || (p->flags & 1)) {  // the row map goes with the cumsum stage
+        ssd::k_rows<1024><<<1, 1024, 0, (hipStream_t)stream>>>(cu, (int)nseq, T, (int)Q, ts, kb);
+        if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+    }
+    ssd::RunArgs a;
+    a.b = nseq; a.T = T; a.H = H; a.P = P; a.N = N; a.G = G; a.Q = Q;
+    a.nc = (T + Q - 1) / Q;
+    a.diag = 0;
+    a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.h0 = h0;
+    a.y = y; a.hT = hT;
+    a.cdt = reinterpret_cast<float*>(w + L.cdt_off);
+    a.cb = static_cast<void*>(w + L.cb_off);
+    a.states = nullptr;
+    a.hin = nullptr;
+    a.bt = static_cast<void*>(w + L.bt_off);
+    a.ts = ts; a.kb = kb; a.kcap = L.kcap;
+    a.stream = (hipStream_t)stream;
+    a.stages = p->flags & SSD_STAGE_ALL;
+    a.force_split = false;
+    a.force_fused = true;
+    return ssd::run_bf16(a);
 }
 
 // The token-by-token recurrence on a caller-held state (ssd_step / ssd_diag_step).
@@ -219,6 +337,17 @@ int ssd_diag_scan_fwd(const ssd_problem* p, const void* x, const float* dt, cons
                       const void* B, const void* C, const float* D, const float* h0, void* y,
                       float* hT, void* ws, size_t ws_bytes, void* stream) {
     return scan(p, 1, x, dt, A, B, C, D, h0, y, hT, ws, ws_bytes, stream);
+}
+
+size_t ssd_varlen_workspace_bytes(const ssd_problem* p) {
+    if (check_varlen(p)) return 0;
+    return varlen_layout_of(p).total;
+}
+
+int ssd_scan_fwd_varlen(const ssd_problem* p, const int32_t* cu_seqlens, const void* x, const float* dt,
+                        const float* A, const void* B, const void* C, const float* D, const float* h0,
+                        void* y, float* hT, void* ws, size_t ws_bytes, void* stream) {
+    return scan_varlen(p, cu_seqlens, x, dt, A, B, C, D, h0, y, hT, ws, ws_bytes, stream);
 }
 
 const char* ssd_status_string(int status) {

@@ -115,8 +115,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
                                                     const bf16* __restrict__ cb, const bf16* __restrict__ Bt,
                                                     const float* __restrict__ A, const float* __restrict__ D,
                                                     const float* __restrict__ cdt, const float* __restrict__ h0,
-                                                    bf16* __restrict__ y, float* __restrict__ hT, int64_t Tn,
-                                                    int H, int G, int nc, int BH) {
+                                                    bf16* __restrict__ y, float* __restrict__ hT, Rows rows,
+                                                    int G) {
     typedef FusedCfg<Q, N> CF;
     constexpr int P = 64, TPP = CF::TPP, NPASS = CF::NPASS, NU = CF::NU, SN = CF::SN, KS = CF::KS,
                   XR = CF::XR, NF = CF::NF;
@@ -127,23 +127,28 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
     __shared__ float cds[Q], w2[Q], u2[Q];
     __shared__ __attribute__((aligned(16))) float cdq[Q];  // the next chunk's cdt row, by transfer
 
-    // blocks k, k+8, k+16, ... run on one XCD: give each XCD a contiguous range of (b, h)
+    // blocks k, k+8, k+16, ... run on one XCD: give each XCD a contiguous range of (row, h)
+    const int H = rows.H, BH = rows.nrows * H;
     const int k = blockIdx.x;
     const int64_t bh = (BH % 8 == 0) ? (int64_t)(k % 8) * (BH / 8) + k / 8 : k;
     const int h = (int)(bh % H);
-    const int64_t bi = bh / H;
+    const int ri = (int)(bh / H);
     const int g = h / (H / G);
+    // this row's tokens [0, Tn) and chunks [0, nc) from its bases in each tensor
+    const int64_t Tn = rows.len(ri), rt0 = rows.tok0(ri);
+    const int nc = rows.nchunks(ri);
+    const int64_t kb0 = rows.kbase(ri);
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), l16 = lane & 15, q = lane >> 4;
     const float ah2 = A[h] * LOG2E;
     const float Dh = D ? D[h] : 0.f;
     // one buffer resource per tensor, based at this batch row; rows t >= T fall outside
     // it, so they read as zero and their stores are dropped
     const uint32_t xbytes = (uint32_t)(Tn * H * P * 2);
-    const brsrc rx = make_rsrc(x + bi * Tn * H * P, xbytes);
-    const brsrc ry = make_rsrc(y + bi * Tn * H * P, xbytes);
-    const brsrc rc = make_rsrc(Cm + bi * Tn * G * N, (uint32_t)(Tn * G * N * 2));
-    const brsrc rcb = make_rsrc(cb + bi * (int64_t)nc * G * Q * Q, (uint32_t)((int64_t)nc * G * Q * Q * 2));
-    const brsrc rbt = make_rsrc(Bt + bi * (int64_t)nc * G * N * Q, (uint32_t)((int64_t)nc * G * N * Q * 2));
+    const brsrc rx = make_rsrc(x + rt0 * H * P, xbytes);
+    const brsrc ry = make_rsrc(y + rt0 * H * P, xbytes);
+    const brsrc rc = make_rsrc(Cm + rt0 * G * N, (uint32_t)(Tn * G * N * 2));
+    const brsrc rcb = make_rsrc(cb + kb0 * G * Q * Q, (uint32_t)((int64_t)nc * G * Q * Q * 2));
+    const brsrc rbt = make_rsrc(Bt + kb0 * G * N * Q, (uint32_t)((int64_t)nc * G * N * Q * 2));
     const int XS = H * P * 2, CS = G * N * 2;                     // row strides in bytes
     // per-lane byte offsets
     const int vc = l16 * CS + g * N * 2 + q * 16;                  // C row l16 of a row tile
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
     };
     // the chunk's cdt row straight into LDS (wave 0, one 16-byte slot per lane), so no
     // loaded value has to stay in registers across the chunk loop
-    const brsrc rcd = make_rsrc(cdt + bh * nc * (int64_t)Q, (uint32_t)(nc * Q * 4));
+    const brsrc rcd = make_rsrc(cdt + rows.cdt_row(ri, h, 0) * Q, (uint32_t)(nc * Q * 4));
     auto dma_cdt = [&](int c) {
         if (w == 0 && lane_now() * 4 < Q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rcd, (__attribute__((address_space(3))) void*)cdq, 16,
@@ -249,7 +254,10 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
                 }
     };
     stage_tables();
-    dma_x(0);
+    // An empty row (packed sequences) reads zeros through its zero-size resources, skips
+    // the loop and stores hT = h0; its first x transfer is not issued, so no transfer into
+    // this work-group's LDS is still in flight when it ends.
+    if (nc > 0) dma_x(0);
     for (int c = 0; c < nc; ++c) {
         const int64_t t0 = (int64_t)c * Q;
         __syncthreads();  // the chunk's tables and Hs are in place

@@ -25,27 +25,137 @@ namespace ssd {
 constexpr int kThreads = 256;  // 4 waves of 64
 
 // ---------------------------------------------------------------------------
-// k_cumsum: cdt[b,h,c,i] = sum_{k=0..i} dt[b, cQ+k, h] (restarting every chunk;
-// positions past T repeat the last valid value exactly).  The log-decay of the
-// chunk-local product of a_k is A * cdt.  Grid (nc, b, ceil(H/16)); a [Q x 16]
-// tile of dt is transposed through LDS, then each wave scans one head at a time:
-// Q/64 consecutive tokens per lane, a lane-serial sum and a wave prefix sum.
+// The rows of a launch.  A row is one sequence with its own state; the state restarts at
+// every row ("Structured State Space Duality" concept page, section "The chunked
+// algorithm takes both": the chunks of one sequence pass the state along; separate
+// sequences are separate maps).
+//  * Dense: `nrows` rows of T tokens each; row r holds tokens [r T, (r + 1) T) and
+//    chunks [r nc, (r + 1) nc).
+//  * Packed (variable length): all rows share one token axis of T tokens; ts[r] is row
+//    r's first token and kb[r] its first chunk (nrows + 1 entries each, built on the
+//    device by k_rows from the caller's cu_seqlens).
+// Per-chunk tables (C B^T, B^T) are indexed by the global chunk k = first chunk + c.
+// cdt is [b][H][nc][Q] for dense rows and [H][kcap][Q] for packed rows.
+// ---------------------------------------------------------------------------
+struct Rows {
+    const int* ts;  // nullptr: dense rows
+    const int* kb;
+    int64_t T;      // dense: tokens per row; packed: tokens of the shared axis
+    int nc;         // dense: chunks per row
+    int nrows, H;
+    int kcap;       // packed: capacity of the global chunk axis (cdt row stride)
+    __device__ bool packed() const { return ts != nullptr; }
+    __device__ int64_t tok0(int r) const { return packed() ? (int64_t)ts[r] : (int64_t)r * T; }
+    __device__ int64_t len(int r) const { return packed() ? (int64_t)(ts[r + 1] - ts[r]) : T; }
+    __device__ int kbase(int r) const { return packed() ? kb[r] : r * nc; }
+    __device__ int nchunks(int r) const { return packed() ? kb[r + 1] - kb[r] : nc; }
+    __device__ int total_chunks() const { return packed() ? kb[nrows] : nrows * nc; }
+    // the row holding global chunk k (0 <= k < total_chunks()): the last r with kb[r] <= k,
+    // which skips empty rows
+    __device__ int row_of(int k) const {
+        if (!packed()) return k / nc;
+        int lo = 0, hi = nrows;  // kb[lo] <= k < kb[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (kb[mid] <= k) lo = mid;
+            else hi = mid;
+        }
+        return lo;
+    }
+    // first element of chunk c's cdt row of (row r, head h), in units of Q floats
+    __device__ int64_t cdt_row(int r, int h, int c) const {
+        return packed() ? (int64_t)h * kcap + kb[r] + c : ((int64_t)r * H + h) * nc + c;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// k_rows: the packed-row map from the caller's cu_seqlens (nrows + 1 token offsets).
+// ts[r] = cu[r] clamped to [ts[r-1], T] (so every row lies inside the token axis, in
+// order, whatever the offsets hold), ts[0] = clamp(cu[0]); kb = prefix sums of
+// ceil((ts[r+1] - ts[r]) / Q).  One work-group of 1024 threads, two block scans.
+// ---------------------------------------------------------------------------
+template <typename V, typename Op>
+__device__ V block_inclusive_scan(V v, Op op, V* part) {  // part: >= 16 entries of LDS
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const V o = __shfl_up(v, off, 64);
+        if (lane >= off) v = op(v, o);
+    }
+    if (lane == 63) part[w] = v;
+    __syncthreads();
+    if (w == 0) {
+        V pv = lane < nw ? part[lane] : part[0];
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const V o = __shfl_up(pv, off, 64);
+            if (lane >= off) pv = op(pv, o);
+        }
+        if (lane < nw) part[lane] = pv;
+    }
+    __syncthreads();
+    if (w > 0) v = op(v, part[w - 1]);
+    __syncthreads();
+    return v;
+}
+
+template <int BLOCK = 1024>  // a template so only the unit that launches it instantiates it
+__global__ __launch_bounds__(BLOCK) void k_rows(const int* __restrict__ cu, int nrows, int64_t T, int Q,
+                                               int* __restrict__ ts, int* __restrict__ kb) {
+    __shared__ long long part[16];
+    const int n = nrows + 1, per = (n + BLOCK - 1) / BLOCK, i0 = threadIdx.x * per;
+    // 1. ts = running maximum of the clamped offsets (a nondecreasing sequence in [0, T])
+    long long mx = 0;
+    for (int i = i0; i < i0 + per && i < n; ++i) mx = max(mx, min((long long)max(cu[i], 0), (long long)T));
+    const auto vmax = [](long long a, long long b) { return a > b ? a : b; };
+    long long pre = block_inclusive_scan(mx, vmax, part);
+    long long run = __shfl_up(pre, 1, 64);
+    if ((threadIdx.x & 63) == 0) run = (threadIdx.x >> 6) > 0 ? part[(threadIdx.x >> 6) - 1] : 0;
+    __syncthreads();
+    for (int i = i0; i < i0 + per && i < n; ++i) {
+        run = max(run, min((long long)max(cu[i], 0), (long long)T));
+        ts[i] = (int)run;
+    }
+    __syncthreads();
+    // 2. kb = exclusive prefix sums of the rows' chunk counts
+    long long cnt = 0;
+    for (int i = i0; i < i0 + per && i < nrows; ++i) cnt += (ts[i + 1] - ts[i] + Q - 1) / Q;
+    const auto vadd = [](long long a, long long b) { return a + b; };
+    const long long inc = block_inclusive_scan(cnt, vadd, part);
+    long long acc = inc - cnt;
+    for (int i = i0; i < i0 + per && i < nrows; ++i) {
+        kb[i] = (int)acc;
+        acc += (ts[i + 1] - ts[i] + Q - 1) / Q;
+    }
+    if (threadIdx.x == BLOCK - 1) kb[nrows] = (int)inc;
+}
+
+// ---------------------------------------------------------------------------
+// k_cumsum: cdt[r,h,c,i] = sum_{k=0..i} dt[row r, cQ+k, h] (restarting every chunk;
+// positions past the row's end repeat the last valid value exactly).  The log-decay of
+// the chunk-local product of a_k is A * cdt.  Grid (chunks, 1, ceil(H/16)) over the
+// global chunk axis; a [Q x 16] tile of dt is transposed through LDS, then each wave
+// scans one head at a time: Q/64 consecutive tokens per lane, a lane-serial sum and a
+// wave prefix sum.
 // ---------------------------------------------------------------------------
 template <int Q>
 __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ dt,
-                                                     float* __restrict__ cdt, int64_t T, int H,
-                                                     int nc) {
+                                                     float* __restrict__ cdt, Rows rows) {
     constexpr int HS = 16, QPL = Q / 64;
     __shared__ float s[HS][Q + 1];
-    const int c = blockIdx.x;
-    const int64_t bi = blockIdx.y;
+    const int k = blockIdx.x;
+    if (k >= rows.total_chunks()) return;
+    const int r = rows.row_of(k);
+    const int c = k - rows.kbase(r);
+    const int64_t T = rows.len(r), rt0 = rows.tok0(r);
+    const int H = rows.H;
     const int hbase = blockIdx.z * HS;
     const int tid = threadIdx.x;
     for (int idx = tid; idx < Q * HS; idx += kThreads) {
         const int t = idx / HS, hh = idx - t * HS;
         const int64_t tok = (int64_t)c * Q + t;
         const int h = hbase + hh;
-        s[hh][t] = (tok < T && h < H) ? dt[(bi * T + tok) * H + h] : 0.f;
+        s[hh][t] = (tok < T && h < H) ? dt[(rt0 + tok) * H + h] : 0.f;
     }
     __syncthreads();
     const int lane = tid & 63, w = tid >> 6;
@@ -82,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ d
             for (int e = 0; e < QPL; ++e)
                 if (lane * QPL + e > pl) v[e] = lastv;
         }
-        float* out = cdt + ((bi * H + hbase + hh) * nc + c) * (int64_t)Q + lane * QPL;
+        float* out = cdt + rows.cdt_row(r, hbase + hh, c) * Q + lane * QPL;
 #pragma unroll
         for (int e = 0; e < QPL; ++e) out[e] = v[e];
     }
@@ -92,24 +202,29 @@ __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ d
 // k_cb: cb[b,c,g][i][j] = sum_n C[b,cQ+i,g,n] B[b,cQ+j,g,n] for the 64x64 blocks on
 // and below the diagonal (block row >= block column); tokens past T read as 0.
 // This is the query-key product of the diagonal block, shared by every head of the
-// group.  Grid (nb(nb+1)/2, nc, b*G), nb = Q/64.  Each wave computes the transposed
+// group.  Grid (chunks, nb(nb+1)/2, G) over the global chunk axis, nb = Q/64.  Each wave computes the transposed
 // tile cb^T[j][i] for 16 j x 64 i, so a lane ends up owning 4 consecutive j of one
 // row i and stores them as one vector.
 // ---------------------------------------------------------------------------
 template <typename T, int N>
 __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const T* __restrict__ Cm,
-                                                 T* __restrict__ cb, int64_t Tn, int G, int Q,
-                                                 int nc) {
+                                                 T* __restrict__ cb, Rows rows, int G, int Q) {
     typedef typename V8<T>::type v8;
     typedef typename V4<T>::type v4;
+    const int kg = blockIdx.x;  // global chunk
+    if (kg >= rows.total_chunks()) return;
+    const int rr = rows.row_of(kg);
+    const int c = kg - rows.kbase(rr);
+    const int64_t Tn = rows.len(rr);
+    // this row's B / C start here; its tokens are [0, Tn) from this base
+    Bm += rows.tok0(rr) * G * N;
+    Cm += rows.tok0(rr) * G * N;
+    const int64_t bi = 0;
     int I = 0;
-    const int pidx = blockIdx.x;
+    const int pidx = blockIdx.y;
     while ((I + 1) * (I + 2) / 2 <= pidx) ++I;
     const int J = pidx - I * (I + 1) / 2;
-    const int c = blockIdx.y;
-    const int64_t bg = blockIdx.z;
-    const int64_t bi = bg / G;
-    const int g = (int)(bg - bi * G);
+    const int g = blockIdx.z;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l16 = lane & 15, q = lane >> 4;
     const int64_t tok0 = (int64_t)c * Q;
@@ -144,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) acc[ct] = mma(acc[ct], fb[ks], fc[ks][ct]);
         }
-        T* out = cb + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
+        T* out = cb + ((int64_t)kg * G + g) * (int64_t)Q * Q;
         const int j0 = J * 64 + 16 * w + 4 * q;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
@@ -170,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
             acc[ct] = mma(acc[ct], a, b);
         }
     }
-    T* out = cb + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
+    T* out = cb + ((int64_t)kg * G + g) * (int64_t)Q * Q;
     const int j0 = J * 64 + 16 * w + 4 * q;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -185,19 +300,24 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
 // ---------------------------------------------------------------------------
 // k_bt: Bt[b,c,g][n][j] = B[b, cQ+j, g, n] (0 past T): each chunk's B with tokens
 // contiguous, the layout the fused kernel reads its chunk-state A operand from.
-// Grid (nc * Q/64, b*G): one 64-token slab per work-group, transposed through LDS.
+// Grid (chunks * Q/64, G) over the global chunk axis: one 64-token slab per
+// work-group, transposed through LDS.
 // ---------------------------------------------------------------------------
 template <typename T, int N>
-__global__ __launch_bounds__(kThreads) void k_bt(const T* __restrict__ Bm, T* __restrict__ Bt, int64_t Tn,
-                                                 int G, int Q, int nc) {
+__global__ __launch_bounds__(kThreads) void k_bt(const T* __restrict__ Bm, T* __restrict__ Bt, Rows rows,
+                                                 int G, int Q) {
     typedef typename V8<T>::type v8;
     constexpr int JB = 64, LD = JB + 8;
     __shared__ __attribute__((aligned(16))) T s[N * LD];
     const int slabs = Q / JB;
-    const int c = blockIdx.x / slabs, j0 = (blockIdx.x - c * slabs) * JB;
-    const int64_t bg = blockIdx.y;
-    const int64_t bi = bg / G;
-    const int g = (int)(bg - bi * G);
+    const int kg = blockIdx.x / slabs, j0 = (blockIdx.x - kg * slabs) * JB;
+    if (kg >= rows.total_chunks()) return;
+    const int rr = rows.row_of(kg);
+    const int c = kg - rows.kbase(rr);
+    const int64_t Tn = rows.len(rr);
+    Bm += rows.tok0(rr) * G * N;
+    const int64_t bi = 0;
+    const int g = blockIdx.y;
     const int64_t tok0 = (int64_t)c * Q + j0;
     for (int v = threadIdx.x; v < JB * N / 8; v += kThreads) {
         const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
@@ -206,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void k_bt(const T* __restrict__ Bm, T* __
         for (int e = 0; e < 8; ++e) s[(n0 + e) * LD + jj] = val[e];
     }
     __syncthreads();
-    T* out = Bt + ((bi * nc + c) * G + g) * (int64_t)N * Q + j0;
+    T* out = Bt + ((int64_t)kg * G + g) * (int64_t)N * Q + j0;
     for (int v = threadIdx.x; v < N * JB / 8; v += kThreads) {
         const int n = v / (JB / 8), jv = (v - n * (JB / 8)) * 8;
         st8(out + (int64_t)n * Q + jv, ld8(&s[n * LD + jv]));

@@ -23,6 +23,14 @@ struct RunArgs {
     float* states;  // [b,H,nc,P,N]
     void* hin;      // [b,H,nc,P,N]
     void* bt;       // [b,nc,G,N,Q]  (scalar decay only)
+    // packed variable-length rows (nullptr: dense).  b rows share the token axis of T
+    // tokens; ts / kb (b + 1 entries, in the workspace) are each row's first token and
+    // first chunk, kcap bounds the chunk axis, nc is the most chunks any row can have.
+    // Packed rows run only on the fused schedule; cdt is then [H][kcap][Q] and cb / bt
+    // are [kcap, G, ...].
+    const int* ts;
+    const int* kb;
+    int64_t kcap;
     hipStream_t stream;
     int stages;       // 0: the whole schedule; else a mask of kernels to enqueue
                       // (1 cumsum, 2 cb, 4 state, 8 scan, 16 out, 32 bt, 64 fused)
@@ -41,7 +49,19 @@ inline bool fused_supported(const RunArgs& a, bool bf16_dtype) {
     return bf16_dtype && !a.diag && a.P == 64 && (a.N == 64 || a.N == 128) && fits;
 }
 inline bool fused_applies(const RunArgs& a, bool bf16_dtype) {
-    return fused_supported(a, bf16_dtype) && !a.force_split && (a.force_fused || a.b * a.H >= 512);
+    return fused_supported(a, bf16_dtype) && !a.force_split && (a.ts || a.force_fused || a.b * a.H >= 512);
+}
+
+inline Rows rows_of(const RunArgs& a) {
+    Rows r;
+    r.ts = a.ts;
+    r.kb = a.kb;
+    r.T = a.T;
+    r.nc = (int)a.nc;
+    r.nrows = (int)a.b;
+    r.H = (int)a.H;
+    r.kcap = a.ts ? (int)a.kcap : (int)(a.b * a.nc);
+    return r;
 }
 
 template <int Q, int N>
@@ -49,8 +69,7 @@ void launch_fused(const RunArgs& a) {
     const int BH = (int)(a.b * a.H);
     k_fused<Q, N><<<BH, kThreads, 0, a.stream>>>(
         static_cast<const bf16*>(a.x), static_cast<const bf16*>(a.C), static_cast<const bf16*>(a.cb),
-        static_cast<const bf16*>(a.bt), a.A, a.D, a.cdt, a.h0, static_cast<bf16*>(a.y), a.hT, a.T, (int)a.H,
-        (int)a.G, (int)a.nc, BH);
+        static_cast<const bf16*>(a.bt), a.A, a.D, a.cdt, a.h0, static_cast<bf16*>(a.y), a.hT, rows_of(a), (int)a.G);
 }
 
 template <typename T, int P, int N>
@@ -58,6 +77,7 @@ int run(const RunArgs& a) {
     constexpr bool kBF16 = sizeof(T) == 2;
     if (a.force_fused && !fused_supported(a, kBF16)) return 3;
     const bool fused = fused_applies(a, kBF16);
+    if (a.ts && (!fused || a.force_split)) return 3;  // packed rows: fused schedule only
     const int st = a.stages ? a.stages : (fused ? (1 | 2 | 32 | 64) : (1 | 2 | 4 | 8 | 16));
     const int Q = (int)a.Q, nc = (int)a.nc, H = (int)a.H, G = (int)a.G;
     hipStream_t s = a.stream;
@@ -72,17 +92,20 @@ int run(const RunArgs& a) {
     const size_t smem = a.diag ? OutSmem<T, P, N, true>::bytes(Q) : OutSmem<T, P, N, false>::bytes(Q);
     if (smem > 160 * 1024) return 3;
 
-    const dim3 g1(nc, (unsigned)a.b, (H + 15) / 16);
+    // the prep kernels run over the global chunk axis (blocks past the last chunk exit)
+    const Rows rows = rows_of(a);
+    const unsigned kc = (unsigned)rows.kcap;
+    const dim3 g1(kc, 1, (H + 15) / 16);
     if (st & 1) switch (Q) {
-        case 64: k_cumsum<64><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, a.T, H, nc); break;
-        case 128: k_cumsum<128><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, a.T, H, nc); break;
-        case 256: k_cumsum<256><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, a.T, H, nc); break;
+        case 64: k_cumsum<64><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
+        case 128: k_cumsum<128><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
+        case 256: k_cumsum<256><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
         default: return 3;
     }
     if (!a.diag && (st & 2)) {
         const int nb = Q / 64;
-        const dim3 g2(nb * (nb + 1) / 2, nc, (unsigned)(a.b * G));
-        k_cb<T, N><<<g2, kThreads, 0, s>>>(Bm, Cm, cb, a.T, G, Q, nc);
+        const dim3 g2(kc, nb * (nb + 1) / 2, (unsigned)G);
+        k_cb<T, N><<<g2, kThreads, 0, s>>>(Bm, Cm, cb, rows, G, Q);
     }
     const dim3 g3((unsigned)(a.b * H * nc));
     if (!(st & 4)) {
@@ -108,8 +131,8 @@ int run(const RunArgs& a) {
         k_out<T, P, N, false><<<g3, kThreads, smem, s>>>(x, Bm, Cm, cb, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);
     }
     if (!a.diag && (st & 32)) {
-        const dim3 g6((unsigned)(nc * (Q / 64)), (unsigned)(a.b * G));
-        k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, static_cast<T*>(a.bt), a.T, G, Q, nc);
+        const dim3 g6(kc * (unsigned)(Q / 64), (unsigned)G);
+        k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, static_cast<T*>(a.bt), rows, G, Q);
     }
     if (st & 64) {
         if constexpr (kBF16 && P == 64 && (N == 64 || N == 128)) {

@@ -90,3 +90,19 @@ def make_small(b, T, H, P, N, G, seed, *, diag=False, dtype="f32", dt_lo=1e-3, d
     if not D:
         d["D"] = None
     return d
+
+
+def make_packed(lengths, H, P, N, G, seed, *, dtype="bf16", dt_lo=1e-3, dt_hi=0.1, h0=True) -> dict:
+    """Inputs for packed variable-length sequences (tests, bench): the sequences of
+    `lengths` back to back on one token axis, with the workloads' distributions.
+    Returns x [T,H,P], dt [T,H], B/C [T,G,N] (float32 arrays, bf16-rounded for bf16),
+    A [H], D [H], h0 [nseq,H,P,N] (N(0, 0.1), or None) and cu_seqlens (int32, nseq + 1)."""
+    lengths = [int(v) for v in lengths]
+    T = sum(lengths)
+    d = make_small(1, max(T, 1), H, P, N, G, seed, dtype=dtype, dt_lo=dt_lo, dt_hi=dt_hi, h0=False)
+    out = {k: (v[0, :T] if k in ("x", "dt", "B", "C") else v) for k, v in d.items()
+           if k in ("x", "dt", "B", "C", "A", "D")}
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    out["h0"] = (rng.standard_normal((len(lengths), H, P, N)) * 0.1).astype(np.float32) if h0 else None
+    out["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return out

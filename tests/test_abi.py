@@ -196,3 +196,66 @@ def test_step_error_paths(diag):
     assert call_step(prob(T=0, Q=7), diag) == 0
     assert call_step(prob(b=0, T=1), diag) == 0
     assert ssd._load().ssd_step(None, *([None] * 8), None) == ssd_status("SSD_ERR_NULL")
+
+
+def _align(v, a=256):
+    return (v + a - 1) // a * a
+
+
+def test_varlen_workspace_bytes_and_support():
+    """Packed sequences run on the fused schedule: bf16, headdim 64, dstate 64/128.
+    Workspace = cdt [H][kcap][Q] f32 + C B^T [kcap][G][Q][Q] + B^T [kcap][G][N][Q] (bf16)
+    + two int32 row maps of nseq + 1 entries, kcap = ceil(T/Q) + nseq."""
+    for nseq, T, H, N, G, Q in [(3, 1000, 8, 128, 1, 256), (7, 33, 4, 64, 2, 64), (1, 4096, 80, 128, 1, 128)]:
+        p = ssd.make_problem(nseq, T, H, 64, N, G, Q, ssd.SSD_BF16)
+        kcap = -(-T // Q) + nseq
+        want = (_align(H * kcap * Q * 4) + _align(kcap * G * Q * Q * 2) + _align(kcap * G * N * Q * 2)
+                + 2 * _align((nseq + 1) * 4))
+        assert ssd.varlen_workspace_bytes(p) == want
+    for kw in ({"dtype": ssd.SSD_F32}, {"P": 32}, {"N": 256}, {"N": 32}, {"Q": 32}):
+        a = dict(b=3, T=1000, H=8, P=64, N=128, G=1, Q=256, dtype=ssd.SSD_BF16)
+        a.update(kw)
+        p = ssd.make_problem(a["b"], a["T"], a["H"], a["P"], a["N"], a["G"], a["Q"], a["dtype"])
+        assert ssd.varlen_workspace_bytes(p) == 0, kw
+    assert ssd.varlen_workspace_bytes(ssd.make_problem(3, 0, 8, 64, 128, 1, 256, ssd.SSD_BF16)) == 0
+
+
+def test_varlen_error_paths_return_before_any_launch():
+    nseq, T, H, P, N, G, Q = 3, 300, 4, 64, 128, 2, 128
+    p = ssd.make_problem(nseq, T, H, P, N, G, Q, ssd.SSD_BF16)
+    need = ssd.varlen_workspace_bytes(p)
+    sizes = {"cu": (nseq + 1) * 4, "x": T * H * P * 2, "dt": T * H * 4, "A": H * 4, "B": T * G * N * 2,
+             "C": T * G * N * 2, "D": H * 4, "h0": nseq * H * P * N * 4, "y": T * H * P * 2,
+             "hT": nseq * H * P * N * 4, "ws": need}
+    ptrs, off = {}, BASE
+    for k, n in sizes.items():
+        ptrs[k] = off
+        off += _align(n) + 4096
+    fn = ssd._load().ssd_scan_fwd_varlen
+
+    def run(prob=p, ws_bytes=need, **over):
+        q = dict(ptrs, **over)
+        v = lambda k: ctypes.c_void_p(q[k]) if q[k] else None
+        return fn(ctypes.byref(prob), v("cu"), v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"), v("h0"),
+                  v("y"), v("hT"), v("ws"), ws_bytes, None)
+
+    assert run(cu=0) == ssd_status("SSD_ERR_NULL")
+    assert run(x=0) == ssd_status("SSD_ERR_NULL")
+    assert run(A=0) == ssd_status("SSD_ERR_NULL")
+    assert run(ws=0) == ssd_status("SSD_ERR_WORKSPACE")
+    assert run(ws_bytes=need - 1) == ssd_status("SSD_ERR_WORKSPACE")
+    assert run(cu=BASE + 2) == ssd_status("SSD_ERR_ALIGN")
+    assert run(x=ptrs["x"] + 8) == ssd_status("SSD_ERR_ALIGN")
+    assert run(ws=ptrs["ws"] + 16) == ssd_status("SSD_ERR_ALIGN")
+    assert run(y=ptrs["x"]) == ssd_status("SSD_ERR_ALIAS")
+    assert run(hT=ptrs["h0"]) == ssd_status("SSD_ERR_ALIAS")
+    assert run(cu=ptrs["ws"] + 256) == ssd_status("SSD_ERR_ALIAS")
+    assert run(y=ptrs["cu"]) == ssd_status("SSD_ERR_ALIAS")
+    split = ssd.make_problem(nseq, T, H, P, N, G, Q, ssd.SSD_BF16, flags=ssd.SCHEDULE_SPLIT)
+    assert run(prob=split) == ssd_status("SSD_ERR_UNSUPPORTED")
+    f32 = ssd.make_problem(nseq, T, H, P, N, G, Q, ssd.SSD_F32)
+    assert run(prob=f32) == ssd_status("SSD_ERR_UNSUPPORTED")
+    assert run(prob=ssd.make_problem(nseq, T, 6, P, N, 4, Q, ssd.SSD_BF16)) == ssd_status("SSD_ERR_SHAPE")
+    assert fn(None, *([None] * 11), 0, None) == ssd_status("SSD_ERR_NULL")
+    # no sequences: nothing to do
+    assert run(prob=ssd.make_problem(0, T, H, P, N, G, Q, ssd.SSD_BF16)) == 0

@@ -276,3 +276,43 @@ def test_chunk_stage_dumps_are_consistent():
     x = np.asarray(d["x"], np.float64)
     np.testing.assert_allclose(y, st["ydiag"] + st["yoff"] + np.asarray(d["D"])[None, None, :, None] * x,
                                rtol=1e-13, atol=1e-14)
+
+
+def test_packed_equal_lengths_equal_the_dense_batch():
+    """Sequences of one length packed back to back are a dense batch: the per-sequence
+    oracle on the packed axis equals the C oracle's own batched run."""
+    b, T, H, P, N, G = 3, 29, 2, 8, 8, 1
+    ins = make_small(b, T, H, P, N, G, seed=31)
+    y, hT = oracle.recurrence(ins["x"], ins["dt"], ins["A"], ins["B"], ins["C"], ins["D"], ins["h0"])
+    cu = np.arange(b + 1) * T
+    yp, hp = oracle.recurrence_packed(ins["x"].reshape(b * T, H, P), ins["dt"].reshape(b * T, H), ins["A"],
+                                      ins["B"].reshape(b * T, G, N), ins["C"].reshape(b * T, G, N), cu,
+                                      ins["D"], ins["h0"])
+    np.testing.assert_allclose(yp, y.reshape(b * T, H, P), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(hp, hT, rtol=0, atol=1e-13)
+
+
+def test_packed_sequences_are_separate_maps():
+    """Each packed sequence equals the quadratic form (O2, independent C code) on its own
+    tokens with its own h0; an empty sequence keeps its h0; and changing one sequence's
+    inputs leaves every other sequence's outputs unchanged."""
+    from ssd_chunked_scan_03_amd.synth import make_packed
+    lengths = [5, 0, 17, 1, 9]
+    d = make_packed(lengths, 3, 8, 16, 1, seed=5, dtype="f32")
+    cu = d["cu_seqlens"]
+    y, hT = oracle.recurrence_packed(d["x"], d["dt"], d["A"], d["B"], d["C"], cu, d["D"], d["h0"])
+    for s, n in enumerate(lengths):
+        a, b = cu[s], cu[s + 1]
+        if n == 0:
+            np.testing.assert_array_equal(hT[s], d["h0"][s])
+            continue
+        yq, hq = oracle.quadratic(d["x"][None, a:b], d["dt"][None, a:b], d["A"], d["B"][None, a:b],
+                                  d["C"][None, a:b], d["D"], d["h0"][s:s + 1])
+        assert rel_y(y[a:b][None], yq) < TOL and rel_h(hT[s:s + 1], hq) < TOL
+    x2 = d["x"].copy()
+    x2[cu[2]:cu[3]] *= -3.0
+    y2, h2 = oracle.recurrence_packed(x2, d["dt"], d["A"], d["B"], d["C"], cu, d["D"], d["h0"])
+    for s in (0, 3, 4):
+        np.testing.assert_array_equal(y2[cu[s]:cu[s + 1]], y[cu[s]:cu[s + 1]])
+        np.testing.assert_array_equal(h2[s], hT[s])
+    assert not np.array_equal(y2[cu[2]:cu[3]], y[cu[2]:cu[3]])
