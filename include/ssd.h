@@ -86,6 +86,12 @@ typedef struct {
  *          dstate 64 or 128);
  *   split  k_cumsum, k_cb (scalar decay), k_state, k_scan, k_out: every stage is a
  *          separate chunk-parallel launch and chunk states go through the workspace.
+ *          k_scan is one sequential pass over chunks per state element; when
+ *          batch * nheads * headdim * dstate / 4 is under 131072 and there are at least 8
+ *          chunks, it runs instead as a parallel scan over 2 to 64 segments of at least 4
+ *          chunks ("Semiseparable Matrix Transformations": state-space evaluation as a
+ *          parallel scan): each segment from a zero state, a short pass over segments for
+ *          the state entering each, and each segment again from that state.
  * flags = 0 runs fused where it exists and there are at least 512 (batch, head) chains
  * to fill the GPU (one work-group each), else split.  SSD_SCHEDULE_SPLIT asks for split
  * explicitly; SSD_SCHEDULE_FUSED asks for fused at any (batch, head) count and is
@@ -122,7 +128,13 @@ size_t ssd_workspace_bytes(const ssd_problem* p, int diag);
  *   hin  dtype   [batch, nheads, nchunks, headdim, dstate]  state entering chunk c
  *   bt   dtype   [batch, nchunks, ngroups, dstate, chunk]  B of each chunk, tokens contiguous
  *        (scalar decay)
- * The split schedule fills cdt, cb, states and hin; the fused one fills cdt, cb and bt.
+ *   carry float32 [nseg, batch, nheads, headdim, dstate] then [batch, nheads, nseg]: the
+ *        state entering each segment of chunks and each segment's summed cdt totals,
+ *        when the split schedule's state scan runs as a parallel scan over segments
+ *        (batch * nheads * headdim * dstate too small to fill the GPU; see the schedule
+ *        notes); absent otherwise
+ * The split schedule fills cdt, cb, states and hin (and carry); the fused one fills
+ * cdt, cb and bt.
  * Returns an ssd_status.  Pure host function. */
 typedef struct {
     size_t cdt_off, cdt_bytes;
@@ -130,6 +142,7 @@ typedef struct {
     size_t states_off, states_bytes;
     size_t hin_off, hin_bytes;
     size_t bt_off, bt_bytes;
+    size_t carry_off, carry_bytes;
     size_t total_bytes;
 } ssd_workspace_layout;
 int ssd_get_workspace_layout(const ssd_problem* p, int diag, ssd_workspace_layout* out);

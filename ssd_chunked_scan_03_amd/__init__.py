@@ -47,7 +47,7 @@ class Problem(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("cdt_off", "cdt_bytes", "cb_off", "cb_bytes", "states_off", "states_bytes",
-                 "hin_off", "hin_bytes", "bt_off", "bt_bytes", "total_bytes")]
+                 "hin_off", "hin_bytes", "bt_off", "bt_bytes", "carry_off", "carry_bytes", "total_bytes")]
 
 
 def library_path() -> str:

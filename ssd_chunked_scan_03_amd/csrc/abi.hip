@@ -70,6 +70,13 @@ ssd_workspace_layout layout_of(const ssd_problem* p, int diag) {
     L.bt_off = off;
     L.bt_bytes = diag ? 0 : (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->dstate * p->chunk) * es;
     off += align_up(L.bt_bytes);
+    // the split schedule's state scan in segments (few state elements, many chunks)
+    const int64_t sl = ssd::scan_segment_len(p->batch, p->nheads, p->headdim, p->dstate, nc);
+    const int64_t nseg = nc > 0 ? (nc + sl - 1) / sl : 0;
+    L.carry_off = off;
+    L.carry_bytes = nseg > 1 ? (size_t)nseg * (size_t)(p->batch * p->nheads) * (size_t)(p->headdim * p->dstate + 1) * 4
+                             : 0;
+    off += align_up(L.carry_bytes);
     L.total_bytes = (p->batch == 0 || p->seqlen == 0) ? 0 : off;
     return L;
 }
@@ -140,6 +147,7 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     a.states = reinterpret_cast<float*>(w + L.states_off);
     a.hin = static_cast<void*>(w + L.hin_off);
     a.bt = diag ? nullptr : static_cast<void*>(w + L.bt_off);
+    a.carry = L.carry_bytes ? reinterpret_cast<float*>(w + L.carry_off) : nullptr;
     a.ts = nullptr; a.kb = nullptr; a.kcap = 0;
     a.stream = (hipStream_t)stream;
     a.stages = p->flags & SSD_STAGE_ALL;
@@ -258,6 +266,7 @@ int scan_varlen(const ssd_problem* p, const int* cu, const void* x, const float*
     a.hin = nullptr;
     a.bt = static_cast<void*>(w + L.bt_off);
     a.ts = ts; a.kb = kb; a.kcap = L.kcap;
+    a.carry = nullptr;
     a.stream = (hipStream_t)stream;
     a.stages = p->flags & SSD_STAGE_ALL;
     a.force_split = false;

@@ -485,15 +485,83 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
 // (per n for the diagonal decay).  Sequential over chunks, parallel over
 // b x H x P x N: each thread owns 4 consecutive (p, n) elements of one head and
 // streams its chunk states with loads issued 8 chunks ahead.
-// Grid b*H*ceil(P*N/1024), flattened.
+// Grid (b*H*ceil(P*N/1024), segments).
+//
+// When b H P N is too small to fill the GPU, the chunks are cut into segments of L and
+// the step, being linear (H -> a H + S composes associatively: (a2, S2) o (a1, S1) =
+// (a2 a1, a2 S1 + S2)), runs as a parallel scan ("Semiseparable Matrix Transformations"
+// keyword page, definition: parallel scans evaluate the same map) in three launches:
+//   MODE 1  each segment from a zero state -> its end state E_s      (into `carry`),
+//           and the sum of its chunks' cdt totals                     (into `segsum`)
+//   k_scan_carry   in segment order: carry[s] <- H entering segment s
+//   MODE 2  each segment again from carry[s]: hin, and hT from the last segment
+// MODE 0 is the whole sequence in one segment (L = nc).
 // ---------------------------------------------------------------------------
-template <typename T, bool DIAG>
+template <typename T, bool DIAG, int MODE>
 __global__ __launch_bounds__(kThreads) void k_scan(const float* __restrict__ S, T* __restrict__ hin,
                                                    float* __restrict__ hT, const float* __restrict__ h0,
                                                    const float* __restrict__ A,
-                                                   const float* __restrict__ cdt, int H, int PN,
-                                                   int N, int Q, int nc, int per_head) {
+                                                   const float* __restrict__ cdt, float* __restrict__ carry,
+                                                   float* __restrict__ segsum, int H, int PN, int N, int Q,
+                                                   int nc, int per_head, int L, int64_t BHPN) {
     typedef typename V4<T>::type v4;
+    const int64_t bh = blockIdx.x / per_head;
+    const int part = (int)(blockIdx.x - bh * per_head);
+    const int h = (int)(bh % H);
+    const int e0 = (part * kThreads + threadIdx.x) * 4;
+    if (e0 >= PN) return;
+    const int seg = blockIdx.y;
+    const int cb = seg * L, ce = min(nc, cb + L);
+    const int n0 = e0 % N;
+    float a4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a4[k] = DIAG ? A[h * N + n0 + k] : A[h];
+    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (MODE == 2) st = ld4(carry + seg * BHPN + bh * PN + e0);
+    else if (MODE == 0 && h0) st = ld4(h0 + bh * PN + e0);
+    const float* cl = cdt + bh * (int64_t)nc * Q + (Q - 1);
+    const float* sp = S + bh * (int64_t)nc * PN + e0;
+    T* hp = hin + bh * (int64_t)nc * PN + e0;
+    constexpr int DEPTH = 8;
+    float lsum = 0.f;  // the segment's log-decay per unit A (MODE 1)
+    for (int c0 = cb; c0 < ce; c0 += DEPTH) {
+        f32x4 s[DEPTH];
+        float Lc[DEPTH];
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) {
+            if (c0 + k < ce) {
+                s[k] = ld4(sp + (int64_t)(c0 + k) * PN);
+                Lc[k] = cl[(int64_t)(c0 + k) * Q];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) {
+            if (c0 + k < ce) {
+                if (MODE != 1) {
+                    v4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = from_f<T>(st[r]);
+                    st4(hp + (int64_t)(c0 + k) * PN, o);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[r] = exp_f(a4[r] * Lc[k]) * st[r] + s[k][r];
+                if (MODE == 1) lsum += Lc[k];
+            }
+        }
+    }
+    if (MODE == 1) {
+        st4(carry + seg * BHPN + bh * PN + e0, st);
+        if (e0 == 0) segsum[bh * gridDim.y + seg] = lsum;
+    }
+    else if (hT && ce == nc) st4(hT + bh * PN + e0, st);
+}
+
+// The segments in order: carry[s] holds segment s's end state from a zero start and is
+// replaced by the state entering it; the segment's decay is exp(A * segsum[s]).
+template <bool DIAG>
+__global__ __launch_bounds__(kThreads) void k_scan_carry(const float* __restrict__ h0, const float* __restrict__ A,
+                                                         const float* __restrict__ segsum, float* __restrict__ carry,
+                                                         int H, int PN, int N, int per_head, int nseg, int64_t BHPN) {
     const int64_t bh = blockIdx.x / per_head;
     const int part = (int)(blockIdx.x - bh * per_head);
     const int h = (int)(bh % H);
@@ -504,33 +572,14 @@ __global__ __launch_bounds__(kThreads) void k_scan(const float* __restrict__ S, 
 #pragma unroll
     for (int k = 0; k < 4; ++k) a4[k] = DIAG ? A[h * N + n0 + k] : A[h];
     f32x4 st = h0 ? ld4(h0 + bh * PN + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* cl = cdt + bh * (int64_t)nc * Q + (Q - 1);
-    const float* sp = S + bh * (int64_t)nc * PN + e0;
-    T* hp = hin + bh * (int64_t)nc * PN + e0;
-    constexpr int DEPTH = 8;
-    for (int c0 = 0; c0 < nc; c0 += DEPTH) {
-        f32x4 s[DEPTH];
-        float L[DEPTH];
+    for (int sg = 0; sg < nseg; ++sg) {
+        float* cp = carry + sg * BHPN + bh * PN + e0;
+        const f32x4 e = ld4(cp);
+        const float ls = segsum[bh * nseg + sg];
+        st4(cp, st);
 #pragma unroll
-        for (int k = 0; k < DEPTH; ++k) {
-            if (c0 + k < nc) {
-                s[k] = ld4(sp + (int64_t)(c0 + k) * PN);
-                L[k] = cl[(int64_t)(c0 + k) * Q];
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < DEPTH; ++k) {
-            if (c0 + k < nc) {
-                v4 o;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = from_f<T>(st[r]);
-                st4(hp + (int64_t)(c0 + k) * PN, o);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st[r] = exp_f(a4[r] * L[k]) * st[r] + s[k][r];
-            }
-        }
+        for (int r = 0; r < 4; ++r) st[r] = exp_f(a4[r] * ls) * st[r] + e[r];
     }
-    if (hT) st4(hT + bh * PN + e0, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -31,12 +31,28 @@ struct RunArgs {
     const int* ts;
     const int* kb;
     int64_t kcap;
+    float* carry;   // [nseg, b, H, P, N] then [b, H, nseg] when the state scan runs in
+                    // segments (entering states, then each segment's summed cdt totals)
     hipStream_t stream;
     int stages;       // 0: the whole schedule; else a mask of kernels to enqueue
                       // (1 cumsum, 2 cb, 4 state, 8 scan, 16 out, 32 bt, 64 fused)
     bool force_split;
     bool force_fused;
 };
+
+// Segments of the split schedule's state scan: 1 (one sequential pass) unless b H P N / 4
+// threads cannot fill the GPU; then enough segments of at least 4 chunks, at most 64,
+// that the parallel scan has about 128 K threads.  Returns the segment length in chunks
+// (nc for one segment); the segment count is ceil(nc / length).
+inline int64_t scan_segment_len(int64_t b, int64_t H, int64_t P, int64_t N, int64_t nc) {
+    const int64_t want = 131072, threads = b * H * P * N / 4;
+    if (threads >= want || nc < 8) return nc > 0 ? nc : 1;
+    int64_t S = (want + threads - 1) / threads;
+    if (S > nc / 4) S = nc / 4;
+    if (S > 64) S = 64;
+    if (S < 2) return nc;
+    return (nc + S - 1) / S;
+}
 
 // The fused per-(batch, head) schedule: bf16, scalar decay, P = 64, N in {64, 128},
 // and enough (batch, head) chains to occupy every CU several times over.
@@ -115,12 +131,32 @@ int run(const RunArgs& a) {
         k_state<T, P, N, false><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
 
     const int per_head = (P * N / 4 + kThreads - 1) / kThreads;
-    const dim3 g4((unsigned)(a.b * H * per_head));
+    const int L = (int)scan_segment_len(a.b, H, P, N, nc);
+    const int nseg = (nc + L - 1) / L;
+    const int64_t BHPN = a.b * H * P * N;
+    const dim3 g4((unsigned)(a.b * H * per_head)), g4s((unsigned)(a.b * H * per_head), (unsigned)nseg);
+    float* segsum = a.carry ? a.carry + nseg * BHPN : nullptr;  // [b, H, nseg]
     if (!(st & 8)) {
-    } else if (a.diag)
-        k_scan<T, true><<<g4, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, H, P * N, N, Q, nc, per_head);
-    else
-        k_scan<T, false><<<g4, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, H, P * N, N, Q, nc, per_head);
+    } else if (nseg <= 1) {
+        if (a.diag)
+            k_scan<T, true, 0><<<g4, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, nullptr, nullptr, H,
+                                                      P * N, N, Q, nc, per_head, nc, BHPN);
+        else
+            k_scan<T, false, 0><<<g4, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, nullptr, nullptr, H,
+                                                       P * N, N, Q, nc, per_head, nc, BHPN);
+    } else if (a.diag) {
+        k_scan<T, true, 1><<<g4s, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
+                                                    P * N, N, Q, nc, per_head, L, BHPN);
+        k_scan_carry<true><<<g4, kThreads, 0, s>>>(a.h0, a.A, segsum, a.carry, H, P * N, N, per_head, nseg, BHPN);
+        k_scan<T, true, 2><<<g4s, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
+                                                    P * N, N, Q, nc, per_head, L, BHPN);
+    } else {
+        k_scan<T, false, 1><<<g4s, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
+                                                     P * N, N, Q, nc, per_head, L, BHPN);
+        k_scan_carry<false><<<g4, kThreads, 0, s>>>(a.h0, a.A, segsum, a.carry, H, P * N, N, per_head, nseg, BHPN);
+        k_scan<T, false, 2><<<g4s, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
+                                                     P * N, N, Q, nc, per_head, L, BHPN);
+    }
 
     if (!(st & 16)) {
     } else if (a.diag) {

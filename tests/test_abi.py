@@ -49,12 +49,30 @@ def test_workspace_layout_arithmetic():
         assert lay["states_bytes"] == 2 * 4 * nc * 64 * 128 * 4
         assert lay["hin_bytes"] == 2 * 4 * nc * 64 * 128 * 2
         assert lay["bt_bytes"] == (0 if diag else 2 * nc * 2 * 128 * 128 * 2)
-        offs = [lay[k] for k in ("cdt_off", "cb_off", "states_off", "hin_off", "bt_off")]
+        assert lay["carry_bytes"] == 0  # 2 x 4 x 64 x 128 / 4 threads is not "few", and nc < 8
+        offs = [lay[k] for k in ("cdt_off", "cb_off", "states_off", "hin_off", "bt_off", "carry_off")]
         assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
         assert lay["total_bytes"] >= lay["bt_off"] + lay["bt_bytes"]
         assert ssd.workspace_bytes(p, diag) == lay["total_bytes"]
     assert ssd.workspace_bytes(prob(T=0)) == 0
     assert ssd.workspace_bytes(prob(b=0)) == 0
+
+
+def test_segmented_state_scan_workspace():
+    """Few state elements (b H P N / 4 = 4096 threads) and 256 chunks: the state scan runs
+    in 32 segments of 8 chunks (enough segments for about 128 K threads, at least 4 chunks
+    each, at most 64), with one entering state per segment and one summed cdt total per
+    (head, segment) in the carry region."""
+    p = ssd.make_problem(1, 16384, 4, 64, 64, 1, 64, ssd.SSD_BF16)
+    lay = ssd.workspace_layout(p)
+    assert lay["carry_bytes"] == 32 * 4 * (64 * 64 + 1) * 4
+    assert lay["carry_off"] >= lay["bt_off"] + lay["bt_bytes"]
+    assert lay["total_bytes"] >= lay["carry_off"] + lay["carry_bytes"]
+    # segments need at least 4 chunks each: 40 chunks allow 10
+    p = ssd.make_problem(1, 40 * 64, 4, 64, 64, 1, 64, ssd.SSD_BF16)
+    assert ssd.workspace_layout(p)["carry_bytes"] == 10 * 4 * (64 * 64 + 1) * 4
+    # 7 chunks: one sequential pass
+    assert ssd.workspace_layout(ssd.make_problem(1, 7 * 64, 4, 64, 64, 1, 64, ssd.SSD_BF16))["carry_bytes"] == 0
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -225,3 +225,31 @@ def test_python_api_and_stream():
     assert none is None
     assert torch.equal(y, y2)
     check((y.float().cpu().numpy(), hT.cpu().numpy()), oracle_ref(inp, False), "bf16", "api")
+
+
+SEGMENTED = [  # b, T, H, P, N, G, Q, dtype, diag -- few state elements, many chunks
+    (1, 16384, 4, 64, 64, 1, 64, "bf16", False),      # 256 chunks: 32 segments of 8
+    (1, 41 * 64 + 5, 4, 64, 64, 2, 64, "bf16", False),  # 42 chunks, ragged: 9 segments of 5 (last 2)
+    (1, 8192, 2, 64, 64, 1, 64, "f32", True),         # diagonal decay: 32 segments of 4
+    (2, 4096, 2, 32, 32, 1, 64, "f32", False),        # 64 chunks: 16 segments of 4
+]
+
+
+@pytest.mark.parametrize("case", SEGMENTED, ids=lambda c: "b{}T{}H{}P{}N{}G{}Q{}{}{}".format(*c[:8], "D" if c[8] else "S"))
+def test_segmented_state_scan_matches_oracle(case):
+    """The split schedule's state scan as a parallel scan over segments of chunks (few
+    state elements, many chunks): end to end against the oracle, and every chunk's
+    entering state against the chunked oracle's dumps."""
+    b, T, H, P, N, G, Q, dtype, diag = case
+    print(f"[segmented case] {case}", flush=True)
+    inp = make_small(b, T, H, P, N, G, seed=91, diag=diag, dtype=dtype)
+    y, hT, ws, prob = run_gpu(inp, dtype, Q, diag, return_ws=True, flags=ssd.SCHEDULE_SPLIT)
+    lay = ssd.workspace_layout(prob, diag)
+    assert lay["carry_bytes"] > 0, "this shape should run the state scan in segments"
+    check((y, hT), oracle_ref(inp, diag), dtype, f"segmented {case}")
+    nc = (T + Q - 1) // Q
+    _, _, st = oracle.chunked(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"],
+                              Q=Q, diag=diag, dumps=True)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Hc = ws[lay["hin_off"]:lay["hin_off"] + lay["hin_bytes"]].view(td).reshape(b, H, nc, P, N).float().cpu().numpy()
+    assert max_rel_err(Hc, st["Hc"], (0, 1, 2)) < TOL[dtype]
