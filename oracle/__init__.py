@@ -7,7 +7,7 @@ with them: it is a plain fp64 implementation written from the pages
 ("Structured State Space Duality" concept page; "Diagonal Equivalence in State
 Space Models" abstract; "Semiseparable Matrix Transformations" definition).
 
-Three independent forms of the same map, all in fp64:
+Three independent forms of the same map, and its gradients, all in fp64:
 
 * :func:`recurrence` -- O1, the selective recurrence stepped token by token
   (C, OpenMP); :func:`recurrence_packed` runs it per sequence of a packed batch;
@@ -16,7 +16,9 @@ Three independent forms of the same map, all in fp64:
   for tiny inputs;
 * :func:`chunked`    -- O3, the chunked algorithm with every intermediate
   dumped (chunk-local cumulative step, C B^T blocks, chunk states, entering
-  states, diagonal-block and off-diagonal outputs).
+  states, diagonal-block and off-diagonal outputs);
+* :func:`recurrence_bwd` -- O4, the gradients of O1 (the backward pass) by
+  reverse-mode differentiation of the recurrence written out by hand (C, OpenMP).
 
 Inputs are numpy arrays in the layouts x [b,T,H,P], dt [b,T,H],
 A [H] or [H,N], B/C [b,T,G,N], D [H], h0 [b,H,P,N]; they are converted to
@@ -57,7 +59,8 @@ def _load():
         lib.oracle_recurrence.argtypes = [i64] * 6 + [ci] + [dp] * 9 + [ci]
         lib.oracle_quadratic.argtypes = [i64] * 6 + [ci] + [dp] * 10 + [ci]
         lib.oracle_chunked.argtypes = [i64] * 6 + [ci, i64] + [dp] * 15 + [ci]
-        for f in (lib.oracle_recurrence, lib.oracle_quadratic, lib.oracle_chunked):
+        lib.oracle_recurrence_bwd.argtypes = [i64] * 6 + [ci] + [dp] * 16 + [ci]
+        for f in (lib.oracle_recurrence, lib.oracle_quadratic, lib.oracle_chunked, lib.oracle_recurrence_bwd):
             f.restype = ci
         _lib = lib
     return _lib
@@ -136,6 +139,28 @@ def recurrence_packed(x, dt, A, B, C, cu_seqlens, D=None, h0=None, diag=False, n
         y[a:b] = ys[0]
         hT[s] = hs[0]
     return y, hT
+
+
+def recurrence_bwd(x, dt, A, B, C, D=None, h0=None, dy=None, dhT=None, diag=False, nthreads=None):
+    """O4: gradients of O1 for the output gradients dy [b,T,H,P] and dhT [b,H,P,N]
+    (None: zero).  Returns a dict with dx [b,T,H,P], ddt [b,T,H], dA [H] or [H,N],
+    dB and dC [b,T,G,N], dD [H] and dh0 [b,H,P,N], all float64.  dD and dh0 are the
+    gradients for D and h0 whether or not those were given (a missing D or h0 is zero)."""
+    (x, dt, A, B, C, D, h0), (b, T, H, P, N, G) = _prep(x, dt, A, B, C, D, h0, diag)
+    dy = _f64(dy) if dy is not None else np.zeros((b, T, H, P))
+    dhT = _f64(dhT)
+    assert dy.shape == (b, T, H, P)
+    assert dhT is None or dhT.shape == (b, H, P, N)
+    out = dict(dx=np.empty((b, T, H, P)), ddt=np.empty((b, T, H)), dA=np.empty((H, N) if diag else (H,)),
+               dB=np.empty((b, T, G, N)), dC=np.empty((b, T, G, N)), dD=np.empty((H,)),
+               dh0=np.empty((b, H, P, N)))
+    rc = _load().oracle_recurrence_bwd(b, T, H, P, N, G, int(diag), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                       _ptr(C), _ptr(D), _ptr(h0), _ptr(dy), _ptr(dhT), _ptr(out["dx"]),
+                                       _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                                       _ptr(out["dD"]), _ptr(out["dh0"]), nthreads or default_threads())
+    if rc:
+        raise ValueError("oracle_recurrence_bwd: bad dimensions or out of memory")
+    return out
 
 
 def quadratic(x, dt, A, B, C, D=None, h0=None, diag=False, return_M=False, nthreads=None):

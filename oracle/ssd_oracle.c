@@ -363,4 +363,203 @@ int oracle_chunked(int64_t b, int64_t T, int64_t H, int64_t P, int64_t N, int64_
     return 0;
 }
 
+/* ------------------------------------------------------------------------- *
+ * O4: gradients of the recurrence (the backward pass), by reverse-mode
+ * differentiation of O1 written out by hand.  The loss is any L whose gradients
+ * with respect to the outputs are given: dy = dL/dy [b,T,H,P] and dhT = dL/dhT
+ * [b,H,P,N] (NULL = 0).  The pages give no backward algorithm; their speed claims
+ * are about training ([SSD] "The chunked algorithm takes both").  This follows the
+ * recurrence of [SSD] "The recurrence as one matrix" step by step, in reverse:
+ *
+ *   g_t   = dL/dh_t (through y_t and every later state)
+ *         = r_t + dy_t C_t^T,        r_{T-1} = dhT,  r_{t-1} = a_t o g_t
+ *   dx_t  = D_h dy_t + g_t B_t                      (sum over n)
+ *   dB_t += g_t^T x_t,  dC_t += h_t^T dy_t          (sum over p and over the heads of the group)
+ *   dl_t  = sum_p g_t o (a_t h_{t-1})               (per n: dL / d(dt_t A_{h,n}))
+ *   ddt_t = sum_n A_{h(,n)} dl_{t,n},  dA_{h(,n)} += dt_t dl_{t,n},  dD_h += dy_t . x_t
+ *   dh0   = r_{-1} = a_0 o g_0
+ *
+ * Two passes, so that every sum has one fixed order and no two threads write one
+ * element:
+ *   pass A, one item per (b, h): the state sequence is rebuilt segment by segment
+ *     from checkpoints every ~sqrt(T) tokens, the adjoint runs backward over the
+ *     full P x N state; dx, ddt, dh0 and per-(b, h) partials of dA and dD;
+ *   pass B, one item per (b, g, n): every state column n evolves on its own (the
+ *     decay is a_t or a_{t,n}), so h_t[:, n] forward and g_t[:, n] backward give
+ *     dC_t[n] and dB_t[n] summed over the group's heads in head order.
+ * dA and dD are then summed over b in order.
+ * ------------------------------------------------------------------------- */
+int oracle_recurrence_bwd(int64_t b, int64_t T, int64_t H, int64_t P, int64_t N, int64_t G, int diag,
+                          const double* x, const double* dt, const double* A, const double* B,
+                          const double* C, const double* D, const double* h0, const double* dy,
+                          const double* dhT, double* dx, double* ddt, double* dA, double* dB, double* dC,
+                          double* dD, double* dh0, int nthreads) {
+    dims_t d = {b, T, H, P, N, G, diag};
+    if (check_dims(&d)) return 1;
+    set_threads(nthreads);
+    const int64_t PN = P * N;
+    const int64_t nA = diag ? N : 1;  /* dA entries per head */
+    int64_t SEG = 1;
+    while (SEG * SEG < T) ++SEG;
+    const int64_t nseg = T > 0 ? (T + SEG - 1) / SEG : 0;
+    double* dApart = (double*)calloc((size_t)(b * H * nA + 1), sizeof(double));
+    double* dDpart = (double*)calloc((size_t)(b * H + 1), sizeof(double));
+    if (!dApart || !dDpart) {
+        free(dApart);
+        free(dDpart);
+        return 2;
+    }
+
+    /* pass A: one (b, h) per item */
+#pragma omp parallel
+    {
+        double* ck = (double*)malloc(sizeof(double) * (size_t)((nseg > 0 ? nseg : 1) * PN));
+        double* buf = (double*)malloc(sizeof(double) * (size_t)(SEG * PN));
+        double* S = (double*)malloc(sizeof(double) * (size_t)PN);
+        double* r = (double*)malloc(sizeof(double) * (size_t)PN);
+        double* a = (double*)malloc(sizeof(double) * (size_t)N);
+        double* dl = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(static)
+        for (int64_t it = 0; it < b * H; ++it) {
+            const int64_t bi = it / H, h = it % H, g = group_of(&d, h);
+            const double Dh = D ? D[h] : 0.0;
+            double* dAp = dApart + it * nA;
+            double dDp = 0.0;
+            /* forward, keeping the state before every SEG-th token */
+            for (int64_t e = 0; e < PN; ++e) S[e] = h0 ? h0[(bi * H + h) * PN + e] : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                if (t % SEG == 0) memcpy(ck + (t / SEG) * PN, S, sizeof(double) * (size_t)PN);
+                const double dtv = dt[(bi * T + t) * H + h];
+                for (int64_t n = 0; n < N; ++n) a[n] = exp(decay_log(&d, A, h, n, dtv));
+                const double* Bt = B + ((bi * T + t) * G + g) * N;
+                for (int64_t p = 0; p < P; ++p) {
+                    const double xv = x[((bi * T + t) * H + h) * P + p];
+                    for (int64_t n = 0; n < N; ++n) S[p * N + n] = a[n] * S[p * N + n] + xv * Bt[n];
+                }
+            }
+            /* backward: r holds dL/dh_t through the later tokens (dhT after the last) */
+            for (int64_t e = 0; e < PN; ++e) r[e] = dhT ? dhT[(bi * H + h) * PN + e] : 0.0;
+            for (int64_t k = nseg - 1; k >= 0; --k) {
+                const int64_t t0 = k * SEG, t1 = (t0 + SEG < T) ? t0 + SEG : T;
+                memcpy(S, ck + k * PN, sizeof(double) * (size_t)PN);
+                for (int64_t t = t0; t < t1; ++t) {
+                    const double dtv = dt[(bi * T + t) * H + h];
+                    for (int64_t n = 0; n < N; ++n) a[n] = exp(decay_log(&d, A, h, n, dtv));
+                    const double* Bt = B + ((bi * T + t) * G + g) * N;
+                    for (int64_t p = 0; p < P; ++p) {
+                        const double xv = x[((bi * T + t) * H + h) * P + p];
+                        for (int64_t n = 0; n < N; ++n) S[p * N + n] = a[n] * S[p * N + n] + xv * Bt[n];
+                    }
+                    memcpy(buf + (t - t0) * PN, S, sizeof(double) * (size_t)PN);
+                }
+                for (int64_t t = t1 - 1; t >= t0; --t) {
+                    const double* hprev = (t == t0) ? ck + k * PN : buf + (t - 1 - t0) * PN;
+                    const double dtv = dt[(bi * T + t) * H + h];
+                    for (int64_t n = 0; n < N; ++n) a[n] = exp(decay_log(&d, A, h, n, dtv));
+                    const double* Bt = B + ((bi * T + t) * G + g) * N;
+                    const double* Ct = C + ((bi * T + t) * G + g) * N;
+                    const double* dyt = dy + ((bi * T + t) * H + h) * P;
+                    const double* xt = x + ((bi * T + t) * H + h) * P;
+                    for (int64_t n = 0; n < N; ++n) dl[n] = 0.0;
+                    for (int64_t p = 0; p < P; ++p) {
+                        double* gp = r + p * N;  /* becomes g_t, then r_{t-1} */
+                        double acc = 0.0;
+                        for (int64_t n = 0; n < N; ++n) {
+                            gp[n] += dyt[p] * Ct[n];
+                            acc += gp[n] * Bt[n];
+                            dl[n] += gp[n] * a[n] * hprev[p * N + n];
+                        }
+                        dx[((bi * T + t) * H + h) * P + p] = Dh * dyt[p] + acc;
+                        dDp += dyt[p] * xt[p];
+                    }
+                    double dd = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        const double An = diag ? A[h * N + n] : A[h];
+                        dd += An * dl[n];
+                        dAp[diag ? n : 0] += dtv * dl[n];
+                    }
+                    ddt[(bi * T + t) * H + h] = dd;
+                    for (int64_t p = 0; p < P; ++p)
+                        for (int64_t n = 0; n < N; ++n) r[p * N + n] *= a[n];
+                }
+            }
+            if (dh0)
+                for (int64_t e = 0; e < PN; ++e) dh0[(bi * H + h) * PN + e] = r[e];
+            dDpart[it] = dDp;
+        }
+        free(ck);
+        free(buf);
+        free(S);
+        free(r);
+        free(a);
+        free(dl);
+    }
+
+    /* pass B: one (b, g, n) per item; the group's heads in order */
+    const int64_t hpg = H / G;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)P);
+        double* accB = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+        double* accC = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+#pragma omp for schedule(static)
+        for (int64_t it = 0; it < b * G * N; ++it) {
+            const int64_t bi = it / (G * N), g = (it / N) % G, n = it % N;
+            for (int64_t t = 0; t < T; ++t) accB[t] = accC[t] = 0.0;
+            for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {
+                for (int64_t p = 0; p < P; ++p) s[p] = h0 ? h0[((bi * H + h) * P + p) * N + n] : 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    const double at = exp(decay_log(&d, A, h, n, dt[(bi * T + t) * H + h]));
+                    const double Bn = B[((bi * T + t) * G + g) * N + n];
+                    const double* xt = x + ((bi * T + t) * H + h) * P;
+                    const double* dyt = dy + ((bi * T + t) * H + h) * P;
+                    double acc = 0.0;
+                    for (int64_t p = 0; p < P; ++p) {
+                        s[p] = at * s[p] + xt[p] * Bn;
+                        acc += dyt[p] * s[p];
+                    }
+                    accC[t] += acc;
+                }
+                for (int64_t p = 0; p < P; ++p) s[p] = dhT ? dhT[((bi * H + h) * P + p) * N + n] : 0.0;
+                for (int64_t t = T - 1; t >= 0; --t) {
+                    const double at = exp(decay_log(&d, A, h, n, dt[(bi * T + t) * H + h]));
+                    const double Cn = C[((bi * T + t) * G + g) * N + n];
+                    const double* xt = x + ((bi * T + t) * H + h) * P;
+                    const double* dyt = dy + ((bi * T + t) * H + h) * P;
+                    double acc = 0.0;
+                    for (int64_t p = 0; p < P; ++p) {
+                        s[p] += dyt[p] * Cn;   /* g_t[p][n] */
+                        acc += s[p] * xt[p];
+                        s[p] *= at;            /* r_{t-1}[p][n] */
+                    }
+                    accB[t] += acc;
+                }
+            }
+            for (int64_t t = 0; t < T; ++t) {
+                dB[((bi * T + t) * G + g) * N + n] = accB[t];
+                dC[((bi * T + t) * G + g) * N + n] = accC[t];
+            }
+        }
+        free(s);
+        free(accB);
+        free(accC);
+    }
+
+    for (int64_t h = 0; h < H; ++h) {
+        for (int64_t k = 0; k < nA; ++k) {
+            double v = 0.0;
+            for (int64_t bi = 0; bi < b; ++bi) v += dApart[(bi * H + h) * nA + k];
+            dA[h * nA + k] = v;
+        }
+        if (dD) {
+            double v = 0.0;
+            for (int64_t bi = 0; bi < b; ++bi) v += dDpart[bi * H + h];
+            dD[h] = v;
+        }
+    }
+    free(dApart);
+    free(dDpart);
+    return 0;
+}
+
 int oracle_abi_version(void) { return 1; }

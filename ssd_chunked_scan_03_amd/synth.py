@@ -106,3 +106,22 @@ def make_packed(lengths, H, P, N, G, seed, *, dtype="bf16", dt_lo=1e-3, dt_hi=0.
     out["h0"] = (rng.standard_normal((len(lengths), H, P, N)) * 0.1).astype(np.float32) if h0 else None
     out["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     return out
+
+
+def make_grads(b, T, H, P, N, seed, *, dtype="f32", dhT=True) -> dict:
+    """Output gradients for a backward pass over inputs of shape (b, T, H, P, N): the
+    gradient of a loss with respect to y, dy ~ N(0, 1) [b,T,H,P] (rounded to bfloat16
+    for a bf16 problem, like x), and with respect to the final state, dhT ~ N(0, 0.1^2)
+    [b,H,P,N] float32 (None when not drawn).  Its own generator stream (seed + 104729),
+    drawn in the order dy, dhT."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    dy = rng.standard_normal((b, T, H, P), dtype=np.float32)
+    g = rng.standard_normal((b, H, P, N), dtype=np.float32) * np.float32(0.1)
+    out = dict(dy=dy, dhT=g if dhT else None)
+    if dtype == "bf16":
+        bits = bf16_round_bits(dy)
+        out["dy_bits"] = bits
+        out["dy"] = bf16_bits_to_f32(bits)
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype}")
+    return out
