@@ -7,8 +7,9 @@ shape (b8 T4096 H80 P64 N128 G1 Q256, bf16 x/B/C, fp32 dt/A/D/h0, nonzero h0), w
 seeded synthetic inputs already resident in HBM.  Prints one JSON line with
 tokens/s, TFLOP/s (causal flop count) against the bf16 matrix-core peak, the
 roofline of the dominant kernel (timed live with HIP events on the launch stream
-through the library's per-stage mask), per-kernel times, and the fp64 oracle timed
-on a bounded sample of the same workload on this host's cores.
+through the library's per-stage mask), per-kernel times, the decode step and the
+backward pass at the same shape, and the fp64 oracle timed on a bounded sample of the
+same workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -70,6 +71,7 @@ def main():
     ap.add_argument("--kernel-steps", type=int, default=None, help="launches per kernel timing")
     ap.add_argument("--schedule", choices=["auto", "split", "fused"], default="auto",
                     help="kernel schedule (auto: the library's choice for the shape)")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed work, stream 512 MiB through a plain elementwise kernel "
                          "(calibrates the byte counters)")
@@ -83,7 +85,7 @@ def main():
     import torch
     import ssd_chunked_scan_03_amd as ssd
     from ssd_chunked_scan_03_amd import configs, metrics
-    from ssd_chunked_scan_03_amd.synth import make_inputs
+    from ssd_chunked_scan_03_amd.synth import make_grads, make_inputs
 
     w = configs.HEADLINE
     if args.workload:
@@ -193,6 +195,42 @@ def main():
               "hbm_frac": round(sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
               "tokens_per_s": round(b / (sms * 1e-3), 1)}
 
+    # the backward pass (scalar decay) at the same workload: gradients of every input for
+    # seeded output gradients dy, dhT, timed as a whole with HIP events on the launch stream
+    backward = None
+    if not w.diag and not args.no_bwd:
+        print("[bench] timing the backward pass", file=sys.stderr, flush=True)
+        gr = make_grads(b, T, H, P, N, w.seed, dtype=w.dtype)
+        dy = torch.from_numpy(gr["dy"]).to(dev).to(td).contiguous()
+        dhT = torch.from_numpy(gr["dhT"]).to(dev)
+        bprob = ssd.make_problem(b, T, H, P, N, G, Q, dcode)
+        bws = torch.empty(max(ssd.bwd_workspace_bytes(bprob), 1), dtype=torch.uint8, device=dev)
+        g = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dA=torch.empty_like(A), dB=torch.empty_like(B),
+                 dC=torch.empty_like(C), dD=torch.empty_like(D),
+                 dh0=torch.empty((b, H, P, N), dtype=torch.float32, device=dev))
+
+        def bstep():
+            ssd.scan_bwd_into(bprob, x, dt, A, B, C, D, h0, dy, dhT, g["dx"], g["ddt"], g["dA"], g["dB"], g["dC"],
+                              g["dD"], g["dh0"], bws, stream.cuda_stream)
+
+        for _ in range(3):
+            bstep()
+        torch.cuda.synchronize()
+        bsteps = max(5, ksteps // 2)
+        e0.record(stream)
+        for _ in range(bsteps):
+            bstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / bsteps
+        bmin = metrics.bwd_path_min_bytes(b, T, H, P, N, G, 2 if w.dtype == "bf16" else 4, h0 is not None, True)
+        backward = {"ms": round(bms, 5), "tokens_per_s": round(b * T / (bms * 1e-3), 1), "steps": bsteps,
+                    "path_min_bytes": bmin,
+                    "path_hbm_frac": round(bmin / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "workspace_bytes": int(bws.numel())}
+        del bws, g, dy, dhT
+        print(f"[bench] backward: {bms:.4f} ms", file=sys.stderr, flush=True)
+
     fl = metrics.flops(b, T, H, P, N, G, Q, w.diag)
     tokens = b * T
     tflops = fl["total"] / (ms * 1e-3) / 1e12
@@ -221,6 +259,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "decode_step": decode,
+        "backward": backward,
         "kernel_source_hash": metrics.kernel_source_hash(),
     }
     if not args.no_cpu:

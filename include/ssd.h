@@ -217,6 +217,45 @@ int ssd_diag_step(const ssd_problem* p, const void* x, const float* dt, const fl
                   const void* B, const void* C, const float* D, float* h, void* y,
                   void* stream);
 
+/* Backward pass of ssd_scan_fwd (scalar decay): the gradients of a loss L with respect to
+ * every input, given dy = dL/dy and dhT = dL/dhT.  The pages define the forward map only
+ * ("Structured State Space Duality" concept page, sections "The recurrence as one matrix"
+ * and "The chunked algorithm takes both"); these are its derivatives.  With
+ * g_t = dL/dh_t = dy_t C_t^T + a_{t+1} g_{t+1} (and dhT after the last token):
+ *
+ *     dx_t  = g_t B_t + D_h dy_t            dB_t = sum over the group's heads of g_t^T x_t
+ *     dC_t  = sum over heads of h_t^T dy_t  dh0  = a_0 g_0
+ *     ddt_t = A_h sum_{u >= t} [dy_u . (y_u - D_h x_u) - x_u . (dx_u - D_h dy_u)] + A_h <dhT, hT>
+ *     dA_h  = sum_{b,t} dt_t ddt_t / A_h (formed without the division)
+ *     dD_h  = sum_{b,t} dy_t . x_t
+ *
+ * computed chunk-wise like the forward: the adjoint g is the same recurrence run backward in
+ * time, carried across chunks by a reverse scan; the forward states entering each chunk are
+ * rebuilt from the inputs (nothing from a previous forward call is reused).
+ *
+ *   inputs   x, dt, A [nheads], B, C, D, h0: as for ssd_scan_fwd (D, h0 may be NULL = 0);
+ *            dy [batch, seqlen, nheads, headdim] in the problem dtype;
+ *            dhT [batch, nheads, headdim, dstate] float32 (NULL = 0)
+ *   outputs  dx [batch, seqlen, nheads, headdim] problem dtype; ddt [batch, seqlen, nheads]
+ *            float32; dA [nheads] float32; dB, dC [batch, seqlen, ngroups, dstate] problem
+ *            dtype; dD [nheads] float32 (NULL = not written); dh0 [batch, nheads, headdim,
+ *            dstate] float32 (NULL = not written).  Every output is overwritten, not
+ *            accumulated into; dD and dh0 are the gradients for D and h0 whether or not D
+ *            and h0 were given.
+ * Precision as for the forward: decay sums, exponentials, states and every accumulation in
+ * float32; matrix-core operands in the problem dtype; each output rounded once.
+ * `ws` must hold ssd_bwd_workspace_bytes(p) bytes (0 for an empty problem, where dA = dD = 0
+ * and dh0 = dhT).  flags must be 0.  Same support set as ssd_scan_fwd (chunk, headdim,
+ * dstate, dtype; SSD_ERR_UNSUPPORTED otherwise).  Alignment as for ssd_scan_fwd
+ * (dy, dx, dB, dC 16 bytes; ddt, dA, dD 4; dhT, dh0 16); no output may overlap an input,
+ * the workspace or another output (SSD_ERR_ALIAS).  Errors are reported before any HIP
+ * call. */
+size_t ssd_bwd_workspace_bytes(const ssd_problem* p);
+int ssd_scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* A,
+                 const void* B, const void* C, const float* D, const float* h0, const void* dy,
+                 const float* dhT, void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
+                 float* dh0, void* ws, size_t ws_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* ssd_status_string(int status);
 

@@ -1,4 +1,4 @@
-"""MI355X-native SSD chunked scan (the Mamba-2 core layer), forward pass.
+"""MI355X-native SSD chunked scan (the Mamba-2 core layer): forward and backward passes.
 
 Thin Python binding over ``libssd.so`` (C ABI in ``include/ssd.h``): argument
 marshalling only -- every step of the scan runs in the library's HIP kernels.
@@ -7,6 +7,7 @@ to load, every call raises: there is no fallback path.
 
     y, hT = scan_fwd(x, dt, A, B, C, D=None, h0=None, chunk=256)
     y, hT = diag_scan_fwd(x, dt, A, B, C, D=None, h0=None, chunk=128)
+    grads = scan_bwd(x, dt, A, B, C, dy, D=None, h0=None, dhT=None, chunk=256)
 
 Layouts: x [b,T,H,P]; dt [b,T,H] f32; A [H] (scalar decay) or [H,N] (diagonal
 decay) f32; B, C [b,T,G,N]; D [H] f32; h0 [b,H,P,N] f32.  x/B/C share one dtype,
@@ -17,7 +18,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["scan_fwd", "diag_scan_fwd", "scan_fwd_into", "Problem", "workspace_bytes",
+__all__ = ["scan_fwd", "diag_scan_fwd", "scan_fwd_into", "scan_bwd", "scan_bwd_into", "bwd_workspace_bytes",
+           "Problem", "workspace_bytes",
            "workspace_layout", "status_string", "version", "library_path", "SSDError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +31,8 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPP
           4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_ALIGN", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_workspace_bytes", "ssd_get_workspace_layout", "ssd_scan_fwd", "ssd_diag_scan_fwd",
            "ssd_varlen_workspace_bytes", "ssd_scan_fwd_varlen",
-           "ssd_step", "ssd_diag_step", "ssd_status_string", "ssd_version")
+           "ssd_step", "ssd_diag_step", "ssd_bwd_workspace_bytes", "ssd_scan_bwd",
+           "ssd_status_string", "ssd_version")
 
 
 class SSDError(RuntimeError):
@@ -77,6 +80,10 @@ def _load():
     for f in (lib.ssd_step, lib.ssd_diag_step):
         f.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, vp]
         f.restype = ci
+    lib.ssd_bwd_workspace_bytes.argtypes = [P]
+    lib.ssd_bwd_workspace_bytes.restype = sz
+    lib.ssd_scan_bwd.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, fp, fp, vp, vp, fp, fp, vp, sz, vp]
+    lib.ssd_scan_bwd.restype = ci
     lib.ssd_status_string.argtypes = [ci]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_version.argtypes = []
@@ -279,3 +286,54 @@ def step(x, dt, A, B, C, h, D=None, diag=None):
     y = torch.empty_like(x)
     step_into(prob, diag, x, dt, A, B, C, D, h, y)
     return y
+
+
+def bwd_workspace_bytes(prob: Problem) -> int:
+    return int(_load().ssd_bwd_workspace_bytes(ctypes.byref(prob)))
+
+
+def scan_bwd_into(prob: Problem, x, dt, A, B, C, D, h0, dy, dhT, dx, ddt, dA, dB, dC, dD, dh0, ws,
+                  stream=None) -> None:
+    """Enqueue one backward pass into caller-provided gradients and workspace (no allocation)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(dA.device).cuda_stream
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _load().ssd_scan_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                              _ptr(dy), _ptr(dhT), _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD),
+                              _ptr(dh0), _ptr(ws), nbytes, ctypes.c_void_p(int(stream)))
+    if st:
+        raise SSDError(st, "ssd_scan_bwd")
+
+
+def scan_bwd(x, dt, A, B, C, dy, D=None, h0=None, dhT=None, chunk=256, workspace=None):
+    """Backward pass of the scalar-decay forward: gradients of a loss with respect to every
+    input, given dy (like x) and dhT ([b, H, P, N] float32, None = 0).  Returns a dict with
+    dx (x's dtype), ddt (float32), dA (float32 [H]), dB and dC (B's dtype), dD (float32 [H])
+    and dh0 (float32 [b, H, P, N])."""
+    import torch
+    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D), ("h0", h0), ("dy", dy),
+                    ("dhT", dhT)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if not (x.dtype == B.dtype == C.dtype == dy.dtype):
+        raise TypeError("x, B, C and dy must share one dtype")
+    for name, t in (("dt", dt), ("A", A), ("D", D), ("h0", h0), ("dhT", dhT)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if (B.shape != (b, T, G, N) or C.shape != B.shape or dt.shape != (b, T, H) or A.shape != (H,)
+            or dy.shape != x.shape):
+        raise ValueError("shape mismatch among x, dt, A [H], B, C, dy")
+    prob = make_problem(b, T, H, P, N, G, chunk, _dtype_code(x))
+    dev = x.device
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dA=torch.empty_like(A), dB=torch.empty_like(B),
+               dC=torch.empty_like(C), dD=torch.empty((H,), dtype=torch.float32, device=dev),
+               dh0=torch.empty((b, H, P, N), dtype=torch.float32, device=dev))
+    need = bwd_workspace_bytes(prob)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    scan_bwd_into(prob, x, dt, A, B, C, D, h0, dy, dhT, out["dx"], out["ddt"], out["dA"], out["dB"], out["dC"],
+                  out["dD"], out["dh0"], workspace)
+    return out

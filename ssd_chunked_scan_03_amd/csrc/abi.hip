@@ -3,6 +3,7 @@
 // mutable state; every check happens before the first HIP call.
 #include <string.h>
 
+#include "bwd_launch.hpp"
 #include "launch.hpp"
 #include "step.hpp"
 #include "ssd.h"
@@ -14,6 +15,12 @@ namespace {
 __global__ void k_copy_state(const float* __restrict__ h0, float* __restrict__ hT, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) hT[i] = h0 ? h0[i] : 0.f;
+}
+
+// dst[0 .. n) = 0: the empty-problem values of the backward's parameter gradients
+__global__ void k_zero(float* __restrict__ dst, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = 0.f;
 }
 
 constexpr size_t kAlign = 256;
@@ -309,6 +316,131 @@ int step(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     return p->dtype == SSD_BF16 ? ssd::run_step<ssd::bf16>(a) : ssd::run_step<float>(a);
 }
 
+
+// ---- backward pass (ssd_scan_bwd) ----
+struct BwdLayout {
+    size_t cdt, cb, cbt, bt, ct, states, hin, rin, hTf, ds, dDp, dAp, total;
+};
+
+BwdLayout bwd_layout_of(const ssd_problem* p) {
+    BwdLayout L;
+    memset(&L, 0, sizeof(L));
+    const int64_t b = p->batch, H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups, Q = p->chunk;
+    const int64_t nc = (p->seqlen + Q - 1) / Q;
+    const size_t es = esize(p->dtype), bhc = (size_t)(b * H * nc), bgc = (size_t)(b * nc * G);
+    size_t off = 0;
+    auto take = [&](size_t& at, size_t bytes) {
+        at = off;
+        off += align_up(bytes);
+    };
+    take(L.cdt, bhc * (size_t)Q * 4);
+    take(L.cb, bgc * (size_t)(Q * Q) * es);
+    take(L.cbt, bgc * (size_t)(Q * Q) * es);
+    take(L.bt, bgc * (size_t)(N * Q) * es);
+    take(L.ct, bgc * (size_t)(N * Q) * es);
+    take(L.states, bhc * (size_t)(P * N) * 4);
+    take(L.hin, bhc * (size_t)(P * N) * es);
+    take(L.rin, bhc * (size_t)(P * N) * es);
+    take(L.hTf, (size_t)(b * H * P * N) * 4);
+    take(L.ds, bhc * (size_t)Q * 4);
+    take(L.dDp, bhc * 4);
+    take(L.dAp, (size_t)(b * H) * 4);
+    L.total = (b == 0 || p->seqlen == 0) ? 0 : off;
+    return L;
+}
+
+int check_bwd(const ssd_problem* p) {
+    const int st = check_problem(p);
+    if (st) return st;
+    if (p->flags != 0) return SSD_ERR_UNSUPPORTED;
+    const int64_t nc = (p->seqlen + p->chunk - 1) / p->chunk;
+    // k_bwd_bc's grid: (batch, chunk, group, 64-token slab, n range)
+    if (p->batch * (nc > 0 ? nc : 1) * p->ngroups * (p->chunk / 64) * 2 > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+int scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* A, const void* B, const void* C,
+             const float* D, const float* h0, const void* dy, const float* dhT, void* dx, float* ddt, float* dA,
+             void* dB, void* dC, float* dD, float* dh0, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_bwd(p);
+    if (st) return st;
+    const int64_t b = p->batch, T = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups,
+                  Q = p->chunk;
+    const size_t es = esize(p->dtype);
+    const size_t state_bytes = (size_t)(b * H * P * N) * 4;
+    if (!A || !dA) return SSD_ERR_NULL;
+    if (!aligned(A, 4) || !aligned(dA, 4) || (D && !aligned(D, 4)) || (dD && !aligned(dD, 4)) ||
+        (h0 && !aligned(h0, 16)) || (dhT && !aligned(dhT, 16)) || (dh0 && !aligned(dh0, 16)))
+        return SSD_ERR_ALIGN;
+    const Range rdA = {dA, (size_t)H * 4}, rdD = {dD, dD ? (size_t)H * 4 : 0}, rdh0 = {dh0, dh0 ? state_bytes : 0};
+    hipStream_t s = (hipStream_t)stream;
+    if (b == 0 || T == 0) {
+        // no tokens: dA = dD = 0 and dh0 = dhT (hT is h0 itself); nothing else to write
+        const Range small_in[] = {{A, (size_t)H * 4}, {D, D ? (size_t)H * 4 : 0}, {h0, h0 ? state_bytes : 0},
+                                  {dhT, dhT ? state_bytes : 0}};
+        const Range small_out[] = {rdA, rdD, rdh0};
+        for (const Range& o : small_out) {
+            for (const Range& r : small_in)
+                if (overlap(o, r)) return SSD_ERR_ALIAS;
+            for (const Range& o2 : small_out)
+                if (&o != &o2 && overlap(o, o2)) return SSD_ERR_ALIAS;
+        }
+        k_zero<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(dA, H);
+        if (dD) k_zero<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(dD, H);
+        if (dh0 && b > 0) {
+            const int64_t n = b * H * P * N;
+            k_copy_state<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(dhT, dh0, n);
+        }
+        return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    }
+    if (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC) return SSD_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(dy, 16) || !aligned(dx, 16) ||
+        !aligned(dB, 16) || !aligned(dC, 16) || !aligned(dt, 4) || !aligned(ddt, 4))
+        return SSD_ERR_ALIGN;
+    const BwdLayout L = bwd_layout_of(p);
+    if (!ws || ws_bytes < L.total) return SSD_ERR_WORKSPACE;
+    if (!aligned(ws, kAlign)) return SSD_ERR_ALIGN;
+    const size_t xb = (size_t)(b * T * H * P) * es, bcb = (size_t)(b * T * G * N) * es;
+    const Range ins[] = {{x, xb},
+                         {dt, (size_t)(b * T * H) * 4},
+                         {A, (size_t)H * 4},
+                         {B, bcb},
+                         {C, bcb},
+                         {D, D ? (size_t)H * 4 : 0},
+                         {h0, h0 ? state_bytes : 0},
+                         {dy, xb},
+                         {dhT, dhT ? state_bytes : 0},
+                         {ws, L.total}};
+    const Range outs[] = {{dx, xb}, {ddt, (size_t)(b * T * H) * 4}, rdA, {dB, bcb}, {dC, bcb}, rdD, rdh0};
+    for (const Range& o : outs) {
+        for (const Range& r : ins)
+            if (overlap(o, r)) return SSD_ERR_ALIAS;
+        for (const Range& o2 : outs)
+            if (&o != &o2 && overlap(o, o2)) return SSD_ERR_ALIAS;
+    }
+
+    ssd::BwdArgs a;
+    a.b = b; a.T = T; a.H = H; a.P = P; a.N = N; a.G = G; a.Q = Q;
+    a.nc = (T + Q - 1) / Q;
+    a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.h0 = h0; a.dy = dy; a.dhT = dhT;
+    a.dx = dx; a.ddt = ddt; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dh0 = dh0;
+    char* w = static_cast<char*>(ws);
+    a.cdt = reinterpret_cast<float*>(w + L.cdt);
+    a.cb = w + L.cb;
+    a.cbt = w + L.cbt;
+    a.bt = w + L.bt;
+    a.ct = w + L.ct;
+    a.states = reinterpret_cast<float*>(w + L.states);
+    a.hin = w + L.hin;
+    a.rin = w + L.rin;
+    a.hTf = reinterpret_cast<float*>(w + L.hTf);
+    a.ds = reinterpret_cast<float*>(w + L.ds);
+    a.dDp = reinterpret_cast<float*>(w + L.dDp);
+    a.dAp = reinterpret_cast<float*>(w + L.dAp);
+    a.stream = s;
+    return p->dtype == SSD_BF16 ? ssd::run_bwd_bf16(a) : ssd::run_bwd_f32(a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -357,6 +489,18 @@ int ssd_scan_fwd_varlen(const ssd_problem* p, const int32_t* cu_seqlens, const v
                         const float* A, const void* B, const void* C, const float* D, const float* h0,
                         void* y, float* hT, void* ws, size_t ws_bytes, void* stream) {
     return scan_varlen(p, cu_seqlens, x, dt, A, B, C, D, h0, y, hT, ws, ws_bytes, stream);
+}
+
+size_t ssd_bwd_workspace_bytes(const ssd_problem* p) {
+    if (check_bwd(p)) return 0;
+    return bwd_layout_of(p).total;
+}
+
+int ssd_scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* A, const void* B,
+                 const void* C, const float* D, const float* h0, const void* dy, const float* dhT, void* dx,
+                 float* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0, void* ws, size_t ws_bytes,
+                 void* stream) {
+    return scan_bwd(p, x, dt, A, B, C, D, h0, dy, dhT, dx, ddt, dA, dB, dC, dD, dh0, ws, ws_bytes, stream);
 }
 
 const char* ssd_status_string(int status) {

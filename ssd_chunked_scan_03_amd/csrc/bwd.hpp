@@ -1,0 +1,775 @@
+// bwd.hpp -- the backward pass of the SSD chunked scan (scalar decay): the gradients
+// of a loss with respect to x, dt, A, B, C, D and h0, given its gradients dy and dhT
+// with respect to y and the final state.
+//
+// The pages give the forward map only ("Structured State Space Duality" concept
+// page, sections "The recurrence as one matrix" and "The chunked algorithm takes
+// both"); the gradients below follow from differentiating that recurrence.  Per
+// (batch, head), with a_t = exp(dt_t A), states h_t (P x N) and g_t = dL/dh_t:
+//
+//   g_t   = dy_t C_t^T + a_{t+1} g_{t+1},   g_{T-1} = dy_{T-1} C_{T-1}^T + dhT
+//   dx_t  = g_t B_t + D dy_t                dB_t = sum_heads g_t^T x_t
+//   dC_t  = sum_heads h_t^T dy_t            dh0  = a_0 g_0
+//
+// The adjoint g runs the same linear recurrence backward in time with C in place of
+// B, so it is chunked the same way: per chunk an adjoint input
+// S'_c = sum_i exp(A cdt_i) dy_i C_i^T (k_state with ADJ), a reverse scan over chunks
+// R_{c-1} = exp(A cdt_last) R_c + S'_c from R_{nc-1} = dhT (k_scan_rev; R_c is the
+// adjoint arriving at chunk c's last token from the chunks after it), and within a
+// chunk
+//   dx_j = sum_{i >= j} exp(A (cdt_i - cdt_j)) (C_i . B_j) dy_i + exp(A (cdt_last - cdt_j)) R_c B_j + D dy_j
+//   dC_i = sum_h [ sum_{j <= i} W_ij B_j + exp(A cdt_i) H_c^T dy_i ]
+//   dB_j = sum_h [ sum_{i >= j} W_ij C_i + exp(A (cdt_last - cdt_j)) R_c^T x_j ]
+// with W_ij = exp(A (cdt_i - cdt_j)) (dy_i . x_j) for i >= j, H_c the forward state
+// entering the chunk.  B and C are shared by the heads of a group, so the head sum of
+// W is formed first and multiplied by B and C once per group.
+//
+// The decay gradient.  With s_t the running sum of log-decays, the loss depends on
+// s through y and hT only, and
+//   dL/ds_t = dy_t . (y_t - D x_t) - x_t . (dx_t - D dy_t)    (+ <dhT, hT> at t = T-1)
+// (each pair i >= j of the quadratic form contributes +W_ij at its row and -W_ij at its
+// column); the log-decay of token t enters every s_u with u >= t, so
+//   dL/d(dt_t A) = sum_{u >= t} dL/ds_u,   ddt_t = A dL/d(dt_t A),   dA = sum dt_t dL/d(dt_t A).
+// k_bwd_x forms the per-token term from the fp32 accumulators of y - D x (recomputed)
+// and dx - D dy; k_bwd_dt takes the reverse running sum.
+//
+// Kernels, in launch order after the forward's k_cumsum, k_cb (both orientations), k_bt
+// (B and C), k_state and k_scan (entering states H_c, final state hT):
+//   k_state<ADJ>  adjoint chunk inputs S'_c                        -> states (reused)
+//   k_scan_rev    R_c per chunk, dh0                               -> rin, dh0
+//   k_bwd_x       dx, per-token decay term, D partial sums, per (b, h, c)
+//   k_bwd_bc      dB and dC per (b, c, group, 64-row slab, n range)
+//   k_bwd_dt      chunk-boundary values <R_c, H_{c+1}>, reverse running sums within
+//                 each chunk -> ddt, per-(b, h) A partial sums
+//   k_bwd_reduce  dA, dD
+#pragma once
+
+#include "kernels.hpp"
+
+namespace ssd {
+
+// sum over the four lanes l16, l16 + 16, l16 + 32, l16 + 48 (one matrix-core column)
+__device__ __forceinline__ float sum_q(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+__device__ __forceinline__ float sum_wave(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// k_scan_rev: the adjoint carried across chunks, last chunk first:
+//   R = dhT;  for c = nc-1 .. 0: rin[c] = R;  R = exp(A cdt_last(c)) R + S'_c;  dh0 = R
+// Parallel over b x H x P x N like k_scan (4 consecutive elements per thread), loads
+// issued 8 chunks ahead.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_scan_rev(const float* __restrict__ S, T* __restrict__ rin,
+                                                       float* __restrict__ dh0, const float* __restrict__ dhT,
+                                                       const float* __restrict__ A, const float* __restrict__ cdt,
+                                                       int H, int PN, int Q, int nc, int per_head) {
+    typedef typename V4<T>::type v4;
+    const int64_t bh = blockIdx.x / per_head;
+    const int part = (int)(blockIdx.x - bh * per_head);
+    const int h = (int)(bh % H);
+    const int e0 = (part * kThreads + threadIdx.x) * 4;
+    if (e0 >= PN) return;
+    const float a = A[h];
+    f32x4 st = dhT ? ld4(dhT + bh * PN + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* cl = cdt + bh * (int64_t)nc * Q + (Q - 1);
+    const float* sp = S + bh * (int64_t)nc * PN + e0;
+    T* rp = rin + bh * (int64_t)nc * PN + e0;
+    constexpr int DEPTH = 8;
+    for (int c0 = nc - 1; c0 >= 0; c0 -= DEPTH) {
+        f32x4 s[DEPTH];
+        float Lc[DEPTH];
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) {
+            if (c0 - k >= 0) {
+                s[k] = ld4(sp + (int64_t)(c0 - k) * PN);
+                Lc[k] = cl[(int64_t)(c0 - k) * Q];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) {
+            if (c0 - k >= 0) {
+                v4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = from_f<T>(st[r]);
+                st4(rp + (int64_t)(c0 - k) * PN, o);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[r] = exp_f(a * Lc[k]) * st[r] + s[k][r];
+            }
+        }
+    }
+    if (dh0) st4(dh0 + bh * PN + e0, st);
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_x: one (b, h, c) chunk of the input gradient and of the decay term.
+//   phase 1  yhat^T[p][i] = sum_{j <= i} (L o C B^T)_ij x_j[p] + exp(A cdt_i) (H_c C_i)[p]
+//            (y without the D term, fp32), then dy_i . yhat_i and dy_i . x_i
+//   phase 2  dxhat^T[p][j] = sum_{i >= j} (L o C B^T)_ij dy_i[p] + exp(A (cdt_last - cdt_j)) (R_c B_j)[p]
+//            then x_j . dxhat_j; ds_j = dy_j . yhat_j - x_j . dxhat_j; dx = dxhat + D dy
+// One 64-token-major LDS tile holds x in phase 1 and dy in phase 2 (both read back as
+// token-contiguous fragments by the LDS transpose read).  Phase 1 is k_out's output
+// without D.  Phase 2 reads the transposed table cbt[j][i] = B_j . C_i so a lane's
+// fragment holds 8 consecutive i of one column j; off the diagonal k-step the mask
+// factors as exp(A (cdt_i - cdt_r)) exp(A (cdt_r - cdt_j)) with r the first token of
+// the k-step (both <= 1).  Each wave owns the same row tiles in both phases (paired
+// k, 7-k: the forward's causal work on a tile grows with its index and the backward's
+// shrinks, so every tile costs the same), so the per-token sum needs no exchange.
+// ---------------------------------------------------------------------------
+template <typename T, int P>
+struct BxSmem {
+    static constexpr int LDX = P + 8;
+    __host__ __device__ static size_t bytes(int Q) {
+        return (size_t)Q * LDX * sizeof(T) + (size_t)3 * Q * sizeof(float) + 4 * sizeof(float);
+    }
+};
+
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kThreads) void k_bwd_x(const T* __restrict__ x, const T* __restrict__ dy,
+                                                    const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                                    const T* __restrict__ cb, const T* __restrict__ cbt,
+                                                    const T* __restrict__ hin, const T* __restrict__ rin,
+                                                    const float* __restrict__ A, const float* __restrict__ D,
+                                                    const float* __restrict__ cdt, T* __restrict__ dx,
+                                                    float* __restrict__ ds, float* __restrict__ dDp, int64_t Tn,
+                                                    int H, int G, int Q, int nc) {
+    typedef typename V8<T>::type v8;
+    typedef typename V4<T>::type v4;
+    constexpr int LDX = P + 8, PT = P / 16;
+    constexpr float LOG2E = 1.4426950408889634f;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    T* Ts = reinterpret_cast<T*>(smem_raw);
+    float* cds = reinterpret_cast<float*>(Ts + Q * LDX);
+    float* u2 = cds + Q;   // exp(A (cdt_{j|31} - cdt_j)): from j to the end of its 32-token block
+    float* v2 = u2 + Q;    // exp(A (cdt_i - cdt_{i&~31})): from the start of i's 32-token block to i
+    float* red = v2 + Q;   // one partial sum per wave
+
+    const int64_t blk = blockIdx.x;
+    const int c = (int)(blk % nc);
+    const int64_t bh = blk / nc;
+    const int h = (int)(bh % H);
+    const int64_t bi = bh / H;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, q = lane >> 4;
+    const int64_t tok0 = (int64_t)c * Q;
+    const int len = (int)((Tn - tok0) < Q ? (Tn - tok0) : Q);
+    const int rpw = Q / 64;
+    const int KS = Q / 32;
+    const T* xb = x + ((bi * Tn + tok0) * H + h) * P;     // row j at + j * H * P
+    const T* dyb = dy + ((bi * Tn + tok0) * H + h) * P;
+    const T* crow = Cm + ((bi * Tn + tok0) * G + g) * N;  // row i at + i * G * N
+    const T* brow = Bm + ((bi * Tn + tok0) * G + g) * N;
+    const T* hbase = hin + (bh * nc + c) * (int64_t)(P * N);
+    const T* rbase = rin + (bh * nc + c) * (int64_t)(P * N);
+    const float* cd = cdt + (bh * nc + c) * (int64_t)Q;
+    const float ah2 = A[h] * LOG2E;
+    const float Dh = D ? D[h] : 0.f;
+
+    auto row_tile = [&](int k) { return (rpw == 1) ? w : ((k & 1) ? 8 * (k >> 1) + 7 - w : 8 * (k >> 1) + w); };
+
+    constexpr int XR = (256 * P / 8 + kThreads - 1) / kThreads;  // enough for Q = 256
+    const int XV = Q * P / 8;
+    v8 rv[XR];
+    auto load_rows = [&](const T* base) {
+#pragma unroll
+        for (int r = 0; r < XR; ++r) {
+            const int v = tid + r * kThreads;
+            const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
+            const int jr = jj < len ? jj : len - 1;
+            rv[r] = sel8(v < XV && jj < len, ld8(base + (int64_t)jr * H * P + p0));
+        }
+    };
+    auto store_rows = [&]() {
+#pragma unroll
+        for (int r = 0; r < XR; ++r) {
+            const int v = tid + r * kThreads;
+            if (v < XV) {
+                const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
+                st8(&Ts[jj * LDX + p0], rv[r]);
+            }
+        }
+    };
+    // state term, raw: acc^T[p][t] += sum_n S[p][n] V_t[n] for the wave's row tiles t
+    // (S = H_c with V = C in phase 1, S = R_c with V = B in phase 2)
+    f32x4 acc[4][PT];
+    auto state_term = [&](const T* sbase, const T* vrow) {
+#pragma unroll
+        for (int n0 = 0; n0 < N; n0 += 32) {
+            const int nn = n0 + 8 * q;
+            const bool nv = (N % 32 == 0) || (nn < N);  // N = 16: half the k-step is padding
+            v8 hf[PT], cf[4];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) hf[pt] = sel8(nv, ld8(sbase + (pt * 16 + l16) * N + (nv ? nn : 0)));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = row_tile(k) * 16 + l16;
+                const int ir = i < len ? i : len - 1;
+                cf[k] = sel8(k < rpw && nv && i < len, ld8(vrow + (int64_t)ir * G * N + (nv ? nn : 0)));
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (k < rpw)
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) acc[k][pt] = mma(acc[k][pt], hf[pt], cf[k]);
+        }
+    };
+
+    // ---- phase 1: yhat ----
+    load_rows(xb);
+    const float cdv = tid < Q ? cd[tid] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    state_term(hbase, crow);
+    store_rows();
+    if (tid < Q) cds[tid] = cdv;
+    __syncthreads();
+    if (tid < Q) {
+        u2[tid] = exp2f_fast(ah2 * (cds[tid | 31] - cds[tid]));
+        v2[tid] = exp2f_fast(ah2 * (cds[tid] - cds[tid & ~31]));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (k < rpw) {
+            const float sc = exp2f_fast(ah2 * cds[row_tile(k) * 16 + l16]);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[k][pt] *= sc;
+        }
+    const T* cbb = cb + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (k < rpw) {
+            const int rt = row_tile(k);
+            const int i = rt * 16 + l16;
+            const T* cbrow = cbb + (int64_t)i * Q;
+            const int nks = rt / 2 + 1;  // k-steps of 32 tokens up to this row tile
+            v8 gf[8];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbrow + (ks < nks ? ks : nks - 1) * 32 + 8 * q);
+            const float ci = cds[i];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                if (ks < nks) {
+                    const int j0 = ks * 32 + 8 * q;
+                    v8 mf;
+                    if (ks < nks - 1) {
+                        const float vi = exp2f_fast(ah2 * (ci - cds[ks * 32 + 31]));
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) mf[e] = from_f<T>(to_f(gf[ks][e]) * (u2[j0 + e] * vi));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int j = j0 + e;
+                            const float m = to_f(gf[ks][e]) * exp2f_fast(fminf(ah2 * (ci - cds[j]), 0.f));
+                            mf[e] = from_f<T>(j <= i ? m : 0.f);
+                        }
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt)
+                        acc[k][pt] = mma(acc[k][pt], frag_rows(Ts, LDX, ks * 32, pt * 16, lane), mf);
+                }
+            }
+        }
+    }
+    // dy_i . yhat_i per row (lane (i, q) holds p = 16 pt + 4 q + r), and dy . x for dD
+    float p1[4];
+    float dd = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        p1[k] = 0.f;
+        if (k < rpw) {
+            const int i = row_tile(k) * 16 + l16;
+            float s = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                v4 dv;
+                if (i < len) dv = ld4(dyb + (int64_t)i * H * P + pt * 16 + 4 * q);
+                else
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dv[r] = from_f<T>(0.f);
+                const v4 xv = ld4(&Ts[i * LDX + pt * 16 + 4 * q]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    s += to_f(dv[r]) * acc[k][pt][r];
+                    dd += to_f(dv[r]) * to_f(xv[r]);
+                }
+            }
+            p1[k] = sum_q(s);
+        }
+    }
+    __syncthreads();  // every wave is done with the x tile
+
+    // ---- phase 2: dxhat ----
+    load_rows(dyb);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    state_term(rbase, brow);
+    store_rows();
+    __syncthreads();
+    const float clast = cds[Q - 1];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (k < rpw) {
+            const float sc = exp2f_fast(ah2 * (clast - cds[row_tile(k) * 16 + l16]));
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[k][pt] *= sc;
+        }
+    const T* cbtb = cbt + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (k < rpw) {
+            const int rt = row_tile(k);
+            const int j = rt * 16 + l16;
+            const T* trow = cbtb + (int64_t)j * Q;
+            const int kd = rt / 2;  // the k-step holding row tile rt
+            v8 gf[8];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(trow + ((ks >= kd && ks < KS) ? ks : kd) * 32 + 8 * q);
+            const float cj = cds[j];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                if (ks >= kd && ks < KS) {
+                    const int i0 = ks * 32 + 8 * q;
+                    v8 mf;
+                    if (ks > kd) {
+                        const float wj = exp2f_fast(ah2 * (cds[ks * 32] - cj));
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) mf[e] = from_f<T>(to_f(gf[ks][e]) * (v2[i0 + e] * wj));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int i = i0 + e;
+                            const float m = to_f(gf[ks][e]) * exp2f_fast(fminf(ah2 * (cds[i] - cj), 0.f));
+                            mf[e] = from_f<T>(i >= j ? m : 0.f);
+                        }
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt)
+                        acc[k][pt] = mma(acc[k][pt], frag_rows(Ts, LDX, ks * 32, pt * 16, lane), mf);
+                }
+            }
+        }
+    }
+    // ds_j = dy_j . yhat_j - x_j . dxhat_j; then dx = dxhat + D dy
+    float* dsb = ds + (bh * nc + c) * (int64_t)Q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (k < rpw) {
+            const int j = row_tile(k) * 16 + l16;
+            float s = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                v4 xv;
+                if (j < len) xv = ld4(xb + (int64_t)j * H * P + pt * 16 + 4 * q);
+                else
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) xv[r] = from_f<T>(0.f);
+                const v4 dv = ld4(&Ts[j * LDX + pt * 16 + 4 * q]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    s += to_f(xv[r]) * acc[k][pt][r];
+                    acc[k][pt][r] += Dh * to_f(dv[r]);
+                }
+            }
+            s = sum_q(s);
+            if (q == 0) dsb[j] = p1[k] - s;
+        }
+    }
+    dd = sum_wave(dd);
+    if (lane == 0) red[w] = dd;
+    __syncthreads();  // every wave is done with the dy tile
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (k < rpw) {
+            const int j = row_tile(k) * 16 + l16;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                v4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = from_f<T>(acc[k][pt][r]);
+                st4(&Ts[j * LDX + pt * 16 + 4 * q], o);
+            }
+        }
+    }
+    __syncthreads();
+    if (tid == 0) dDp[bh * nc + c] = (red[0] + red[1]) + (red[2] + red[3]);
+    T* dxb = dx + ((bi * Tn + tok0) * H + h) * P;
+    for (int v = tid; v < len * (P / 8); v += kThreads) {
+        const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
+        st8(dxb + (int64_t)jj * H * P + p0, ld8(&Ts[jj * LDX + p0]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_bc: dB and dC of one (b, c, group) chunk, for the 64-row slab s of tokens and
+// the n range [n0, n0 + NB).  Loop over the group's heads:
+//   W   += L^h o (dy^h x^h^T)  on the tiles a slab needs: rows i in the slab with
+//          j <= i (for dC) and columns j in the slab with i >= j (for dB); fp32, each
+//          16x16 tile owned by one wave (u = w, w + 4, ...).  Off the diagonal tile
+//          the decay factors as exp(A(cdt_i - cdt_I0)) exp(A(cdt_I0 - cdt_J15))
+//          exp(A(cdt_J15 - cdt_j)) (I0 first row of i's tile, J15 last of j's), all <= 1.
+//   dC^T[n][i] += sum_p H_c^h[p][n] exp(A cdt_i) dy_i^h[p]          (wave w: rows of tile 4s + w)
+//   dB^T[n][j] += sum_p R_c^h[p][n] exp(A (cdt_last - cdt_j)) x_j^h[p]
+// then, once per group: dC^T += B^T W^T (W rows of the slab, k over j), dB^T += C^T W
+// (W columns of the slab, k over i), with W staged in LDS in the operand dtype and
+// B^T, C^T from the per-chunk transposed tables.  H_c^h and R_c^h are staged in LDS per
+// head (the next head's prefetched into registers meanwhile) and read with the
+// transpose read, p running down the rows.
+// ---------------------------------------------------------------------------
+template <typename T, int P, int NB>
+struct BcSmem {
+    static constexpr int PR = P < 32 ? 32 : P;  // rows past P stay zero (k-step padding)
+    static constexpr int LDH = NB + 8;
+    static constexpr int LDW = 72;              // W columns of the slab
+    __host__ __device__ static int ldc(int Q) { return Q + 8; }  // W rows of the slab
+    __host__ __device__ static size_t phase1(int) { return (size_t)2 * PR * LDH * sizeof(T); }
+    __host__ __device__ static size_t phase2(int Q) { return ((size_t)64 * ldc(Q) + (size_t)Q * LDW) * sizeof(T); }
+    __host__ __device__ static size_t region(int Q) { return phase1(Q) > phase2(Q) ? phase1(Q) : phase2(Q); }
+    __host__ __device__ static size_t bytes(int Q) { return region(Q) + (size_t)5 * Q * sizeof(float); }
+};
+
+template <typename T, int P, int N, int NB>
+__global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, const T* __restrict__ dy,
+                                                     const T* __restrict__ bt, const T* __restrict__ ct,
+                                                     const T* __restrict__ hin, const T* __restrict__ rin,
+                                                     const float* __restrict__ A, const float* __restrict__ cdt,
+                                                     T* __restrict__ dB, T* __restrict__ dC, int64_t Tn, int H,
+                                                     int G, int Q, int nc) {
+    typedef typename V8<T>::type v8;
+    typedef typename V4<T>::type v4;
+    typedef BcSmem<T, P, NB> SM;
+    constexpr int PR = SM::PR, LDH = SM::LDH, LDW = SM::LDW, NBT = NB / 16, NR = N / NB;
+    constexpr int NTW = 15;  // W tiles per wave at Q = 256 (58 tiles over 4 waves)
+    constexpr float LOG2E = 1.4426950408889634f;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    T* Hs = reinterpret_cast<T*>(smem_raw);
+    T* Rs = Hs + PR * LDH;
+    T* Wc = reinterpret_cast<T*>(smem_raw);  // phase 2: [64][Q + 8]  W rows i of the slab, all j
+    T* Wb = Wc + 64 * SM::ldc(Q);            //          [Q][72]      W rows i >= slab start, columns of the slab
+    float* cdh = reinterpret_cast<float*>(smem_raw + SM::region(Q));
+    float* es = cdh + Q;   // exp(A (cdt_i - cdt_{i & ~15}))
+    float* ee = es + Q;    // exp(A (cdt_{j | 15} - cdt_j))
+    float* sci = ee + Q;   // exp(A cdt_i)
+    float* scj = sci + Q;  // exp(A (cdt_last - cdt_j))
+
+    const int nslab = Q / 64;
+    int64_t blk = blockIdx.x;
+    const int nr = (int)(blk % NR);
+    blk /= NR;
+    const int s = (int)(blk % nslab);
+    blk /= nslab;
+    const int g = (int)(blk % G);
+    blk /= G;
+    const int c = (int)(blk % nc);
+    const int64_t bi = blk / nc;
+    const int n0 = nr * NB;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, q = lane >> 4;
+    const int64_t tok0 = (int64_t)c * Q;
+    const int len = (int)((Tn - tok0) < Q ? (Tn - tok0) : Q);
+    const int hpg = H / G, hbeg = g * hpg;
+    const int NT = 16 * nslab - 6;  // W tiles the slab needs
+    const int s64 = 64 * s;
+
+    // tile u -> (I, J): first the rows of the slab (J <= I), then the columns of the slab
+    // below it
+    auto tile_ij = [&](int u, int& I, int& J) {
+        const int nA = 16 * s + 10;
+        if (u < nA) {
+            int a = 0, base = 0;
+            while (a < 3 && u >= base + 4 * s + a + 1) {
+                base += 4 * s + a + 1;
+                ++a;
+            }
+            I = 4 * s + a;
+            J = u - base;
+        } else {
+            const int v = u - nA;
+            I = 4 * s + 4 + v / 4;
+            J = 4 * s + (v & 3);
+        }
+    };
+
+    // rows past P of the staged tiles stay zero
+    for (int v = tid; v < (PR - P) * LDH; v += kThreads) {
+        Hs[P * LDH + v] = from_f<T>(0.f);
+        Rs[P * LDH + v] = from_f<T>(0.f);
+    }
+
+    constexpr int HV = P * NB / 8;
+    constexpr int HR = (HV + kThreads - 1) / kThreads;
+    v8 hv[HR], rv[HR];
+    float cv = 0.f, c0v = 0.f, c15v = 0.f, clv = 0.f;
+    auto prefetch = [&](int hh) {
+        const int64_t bhh = bi * H + hh;
+        const T* hb = hin + (bhh * nc + c) * (int64_t)(P * N) + n0;
+        const T* rb = rin + (bhh * nc + c) * (int64_t)(P * N) + n0;
+#pragma unroll
+        for (int r = 0; r < HR; ++r) {
+            const int v = tid + r * kThreads;
+            const int pp = v / (NB / 8), nn = (v - pp * (NB / 8)) * 8;
+            if (v < HV) {
+                hv[r] = ld8(hb + pp * N + nn);
+                rv[r] = ld8(rb + pp * N + nn);
+            }
+        }
+        const float* cd = cdt + (bhh * nc + c) * (int64_t)Q;
+        if (tid < Q) {
+            cv = cd[tid];
+            c0v = cd[tid & ~15];
+            c15v = cd[tid | 15];
+            clv = cd[Q - 1];
+        }
+    };
+    float ah2 = 0.f;
+    auto stage = [&](int hh) {
+#pragma unroll
+        for (int r = 0; r < HR; ++r) {
+            const int v = tid + r * kThreads;
+            const int pp = v / (NB / 8), nn = (v - pp * (NB / 8)) * 8;
+            if (v < HV) {
+                st8(&Hs[pp * LDH + nn], hv[r]);
+                st8(&Rs[pp * LDH + nn], rv[r]);
+            }
+        }
+        ah2 = A[hh] * LOG2E;
+        if (tid < Q) {
+            cdh[tid] = cv;
+            es[tid] = exp2f_fast(ah2 * (cv - c0v));
+            ee[tid] = exp2f_fast(ah2 * (c15v - cv));
+            sci[tid] = exp2f_fast(ah2 * cv);
+            scj[tid] = exp2f_fast(ah2 * (clv - cv));
+        }
+    };
+
+    f32x4 accW[NTW], accC[NBT], accB[NBT];
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) accW[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NBT; ++nt) accC[nt] = accB[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int iw = s64 + w * 16 + l16;  // this wave's row (dC) and column (dB) token
+
+    prefetch(hbeg);
+    for (int hh = hbeg; hh < hbeg + hpg; ++hh) {
+        __syncthreads();  // the previous head's tiles and tables are no longer read
+        stage(hh);
+        __syncthreads();
+        if (hh + 1 < hbeg + hpg) prefetch(hh + 1);
+        const T* xh = x + ((bi * Tn + tok0) * H + hh) * P;   // row j at + j * H * P
+        const T* dyh = dy + ((bi * Tn + tok0) * H + hh) * P;
+
+        // W tiles of this head, decay-masked, summed into accW
+#pragma unroll
+        for (int m = 0; m < NTW; ++m) {
+            const int u = w + 4 * m;
+            if (u < NT) {
+                int I, J;
+                tile_ij(u, I, J);
+                const int i = I * 16 + l16, j = J * 16 + l16;
+                f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p0 = 0; p0 < P; p0 += 32) {
+                    const int pp = p0 + 8 * q;
+                    const bool pv = (P % 32 == 0) || (pp < P);
+                    const v8 a = sel8(pv && i < len, ld8(dyh + (int64_t)(i < len ? i : 0) * H * P + (pv ? pp : 0)));
+                    const v8 b = sel8(pv && j < len, ld8(xh + (int64_t)(j < len ? j : 0) * H * P + (pv ? pp : 0)));
+                    t = mma(t, a, b);
+                }
+                // lane: W[I*16 + 4q + r][J*16 + l16]
+                if (I > J) {
+                    const float f = exp2f_fast(ah2 * (cdh[I * 16] - cdh[J * 16 + 15])) * ee[J * 16 + l16];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) accW[m][r] += t[r] * (es[I * 16 + 4 * q + r] * f);
+                } else {
+                    const float cj = cdh[J * 16 + l16];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int ii = I * 16 + 4 * q + r;
+                        const float L = exp2f_fast(fminf(ah2 * (cdh[ii] - cj), 0.f));
+                        accW[m][r] += (ii >= J * 16 + l16) ? t[r] * L : 0.f;
+                    }
+                }
+            }
+        }
+
+        // state terms: this wave's 16 tokens, all n tiles of the range
+        const float si = sci[iw], sj = scj[iw];
+#pragma unroll
+        for (int p0 = 0; p0 < PR; p0 += 32) {
+            const int pp = p0 + 8 * q;
+            const bool pv = (P % 32 == 0) || (pp < P);
+            v8 yb = sel8(pv && iw < len, ld8(dyh + (int64_t)(iw < len ? iw : 0) * H * P + (pv ? pp : 0)));
+            v8 xb8 = sel8(pv && iw < len, ld8(xh + (int64_t)(iw < len ? iw : 0) * H * P + (pv ? pp : 0)));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                yb[e] = from_f<T>(to_f(yb[e]) * si);
+                xb8[e] = from_f<T>(to_f(xb8[e]) * sj);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NBT; ++nt) {
+                accC[nt] = mma(accC[nt], frag_rows(Hs, LDH, p0, nt * 16, lane), yb);
+                accB[nt] = mma(accB[nt], frag_rows(Rs, LDH, p0, nt * 16, lane), xb8);
+            }
+        }
+    }
+
+    // ---- once per group: W through LDS, then the products with B^T and C^T ----
+    __syncthreads();  // every wave is done with the staged H and R tiles
+    {
+        const int nvec = (int)(SM::phase2(Q) / 16);
+        u32x4v* z = reinterpret_cast<u32x4v*>(smem_raw);
+        for (int v = tid; v < nvec; v += kThreads) z[v] = u32x4v{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    const int ldc = SM::ldc(Q);
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) {
+        const int u = w + 4 * m;
+        if (u < NT) {
+            int I, J;
+            tile_ij(u, I, J);
+            const int j = J * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = I * 16 + 4 * q + r;
+                const T v = from_f<T>(accW[m][r]);
+                if (I >= 4 * s && I < 4 * s + 4) Wc[(i - s64) * ldc + j] = v;
+                if (J >= 4 * s && J < 4 * s + 4) Wb[(i - s64) * LDW + (j - s64)] = v;
+            }
+        }
+    }
+    __syncthreads();
+    const T* btb = bt + ((bi * nc + c) * G + g) * (int64_t)N * Q + (int64_t)n0 * Q;  // [n][j]
+    const T* ctb = ct + ((bi * nc + c) * G + g) * (int64_t)N * Q + (int64_t)n0 * Q;
+    for (int j0 = 0; j0 < s64 + 64; j0 += 32) {
+        const v8 wf = ld8(&Wc[(iw - s64) * ldc + j0 + 8 * q]);
+#pragma unroll
+        for (int nt = 0; nt < NBT; ++nt)
+            accC[nt] = mma(accC[nt], ld8(btb + (int64_t)(nt * 16 + l16) * Q + j0 + 8 * q), wf);
+    }
+    for (int i0 = s64; i0 < Q; i0 += 32) {
+        const v8 wf = frag_rows(Wb, LDW, i0 - s64, w * 16, lane);
+#pragma unroll
+        for (int nt = 0; nt < NBT; ++nt)
+            accB[nt] = mma(accB[nt], ld8(ctb + (int64_t)(nt * 16 + l16) * Q + i0 + 8 * q), wf);
+    }
+    if (iw < len) {
+        T* dCr = dC + ((bi * Tn + tok0 + iw) * G + g) * N + n0;
+        T* dBr = dB + ((bi * Tn + tok0 + iw) * G + g) * N + n0;
+#pragma unroll
+        for (int nt = 0; nt < NBT; ++nt) {
+            v4 oc, ob;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                oc[r] = from_f<T>(accC[nt][r]);
+                ob[r] = from_f<T>(accB[nt][r]);
+            }
+            st4(dCr + nt * 16 + 4 * q, oc);
+            st4(dBr + nt * 16 + 4 * q, ob);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_dt: per (b, h), dl_t = dL/d(dt_t A) = sum_{u >= t} ds_u + <dhT, hT>, then
+// ddt_t = A dl_t and dAp[b, h] = sum_t dt_t dl_t.
+// The running sum restarts at every chunk: at the first token of chunk c + 1, dl equals
+// the inner product of the adjoint arriving at the end of chunk c from later tokens with
+// the state entering chunk c + 1, <R_c, H_{c+1}> (H_nc = hT, R_{nc-1} = dhT), so within
+// chunk c dl_t = <R_c, H_{c+1}> + sum_{u = t}^{chunk end} ds_u.  Rounding of the
+// per-token terms then accumulates over at most one chunk instead of the whole sequence.
+// The block forms the boundary products for BLOCK chunks at a time (coalesced reads of
+// rin and hin), then each thread walks one chunk backward.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_sum(float v, float* part) {  // part: >= 4 floats
+    v = sum_wave(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) t += part[k];
+    return t;
+}
+
+template <typename T, int BLOCK = kThreads>
+__global__ __launch_bounds__(BLOCK) void k_bwd_dt(const float* __restrict__ ds, const float* __restrict__ dt,
+                                                  const float* __restrict__ A, const float* __restrict__ dhT,
+                                                  const float* __restrict__ hTf, const T* __restrict__ hin,
+                                                  const T* __restrict__ rin, float* __restrict__ ddt,
+                                                  float* __restrict__ dAp, int64_t Tn, int H, int PN, int Q,
+                                                  int nc) {
+    typedef typename V8<T>::type v8;
+    __shared__ float part[16];
+    __shared__ float Ks[BLOCK];
+    const int64_t bh = blockIdx.x;
+    const int h = (int)(bh % H);
+    const int64_t bi = bh / H;
+    const int tid = threadIdx.x;
+    const float Ah = A[h];
+    const float* d = ds + bh * (int64_t)nc * Q;  // token t at d[t]
+    const T* rb = rin + bh * (int64_t)nc * PN;
+    const T* hb = hin + bh * (int64_t)nc * PN;
+    float da = 0.f;
+    for (int cg = 0; cg < nc; cg += BLOCK) {
+        const int cn = (nc - cg) < BLOCK ? (nc - cg) : BLOCK;
+        for (int cc = 0; cc < cn; ++cc) {
+            const int c = cg + cc;
+            float k = 0.f;
+            if (c + 1 < nc) {
+                for (int v = tid; v < PN / 8; v += BLOCK) {
+                    const v8 r = ld8(rb + (int64_t)c * PN + 8 * v), hv = ld8(hb + (int64_t)(c + 1) * PN + 8 * v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) k += to_f(r[e]) * to_f(hv[e]);
+                }
+            } else if (dhT) {  // the last chunk: <dhT, hT>
+                for (int e = tid; e < PN; e += BLOCK) k += dhT[bh * PN + e] * hTf[bh * PN + e];
+            }
+            k = block_sum(k, part);
+            if (tid == 0) Ks[cc] = k;
+        }
+        __syncthreads();
+        if (tid < cn) {
+            const int c = cg + tid;
+            const int64_t t0 = (int64_t)c * Q;
+            const int len = (int)((Tn - t0) < Q ? (Tn - t0) : Q);
+            float run = Ks[tid];
+            for (int i = len - 1; i >= 0; --i) {
+                run += d[t0 + i];
+                const int64_t o = (bi * Tn + t0 + i) * H + h;
+                ddt[o] = Ah * run;
+                da += dt[o] * run;
+            }
+        }
+        __syncthreads();
+    }
+    da = block_sum(da, part);
+    if (tid == 0) dAp[bh] = da;
+}
+
+// dA[h] = sum_b dAp[b, h];  dD[h] = sum_{b, c} dDp[b, h, c]  (fixed order)
+template <int BLOCK = kThreads>
+__global__ __launch_bounds__(BLOCK) void k_bwd_reduce(const float* __restrict__ dAp,
+                                                         const float* __restrict__ dDp, float* __restrict__ dA,
+                                                         float* __restrict__ dD, int64_t b, int H, int nc) {
+    const int h = blockIdx.x * BLOCK + threadIdx.x;
+    if (h >= H) return;
+    float a = 0.f, d = 0.f;
+    for (int64_t bi = 0; bi < b; ++bi) {
+        a += dAp[bi * H + h];
+        for (int c = 0; c < nc; ++c) d += dDp[(bi * H + h) * nc + c];
+    }
+    dA[h] = a;
+    if (dD) dD[h] = d;
+}
+
+}  // namespace ssd

@@ -1,0 +1,15 @@
+// Backward-pass kernel instantiations for float x/B/C/dy.
+#include "bwd_launch.hpp"
+#include "launch.hpp"
+
+namespace ssd {
+int run_bwd_f32(const BwdArgs& a) {
+    switch (a.P * 1000 + a.N) {
+#define SSD_CASE(P, N) \
+    case P * 1000 + N: return run_bwd<float, P, N>(a);
+        SSD_FOR_EACH_PN(SSD_CASE)
+#undef SSD_CASE
+        default: return 3;
+    }
+}
+}  // namespace ssd

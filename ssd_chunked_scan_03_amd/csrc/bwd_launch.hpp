@@ -1,0 +1,118 @@
+// bwd_launch.hpp -- enqueue the kernel sequence of one SSD backward pass on a stream.
+#pragma once
+
+#include "bwd.hpp"
+
+namespace ssd {
+
+// Everything one backward launch sequence needs; validated by the C ABI beforehand.
+struct BwdArgs {
+    int64_t b, T, H, P, N, G, Q, nc;
+    const void* x;
+    const float* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* h0;
+    const void* dy;
+    const float* dhT;
+    void* dx;
+    float* ddt;
+    float* dA;
+    void* dB;
+    void* dC;
+    float* dD;
+    float* dh0;
+    // workspace regions
+    float* cdt;     // [b,H,nc,Q]
+    void* cb;       // [b,nc,G,Q,Q]  C_c B_c^T, blocks on and below the diagonal
+    void* cbt;      // [b,nc,G,Q,Q]  its transpose, cbt[j][i] = B_j . C_i
+    void* bt;       // [b,nc,G,N,Q]  B per chunk, tokens contiguous
+    void* ct;       // [b,nc,G,N,Q]  C per chunk, tokens contiguous
+    float* states;  // [b,H,nc,P,N]  chunk states, then adjoint chunk inputs
+    void* hin;      // [b,H,nc,P,N]  forward state entering each chunk
+    void* rin;      // [b,H,nc,P,N]  adjoint arriving at each chunk's last token
+    float* hTf;     // [b,H,P,N]     forward final state (when dhT is given)
+    float* ds;      // [b,H,nc,Q]    per-token decay term
+    float* dDp;     // [b,H,nc]      D partial sums
+    float* dAp;     // [b,H]         A partial sums
+    hipStream_t stream;
+};
+
+// n range of one k_bwd_bc work-group
+template <int N> constexpr int bc_nb() { return N <= 128 ? N : 128; }
+
+template <typename T, int P, int N>
+int run_bwd(const BwdArgs& a) {
+    constexpr int NB = bc_nb<N>();
+    const int Q = (int)a.Q, nc = (int)a.nc, H = (int)a.H, G = (int)a.G;
+    const size_t sx = BxSmem<T, P>::bytes(Q), sbc = BcSmem<T, P, NB>::bytes(Q);
+    if (sx > 160 * 1024 || sbc > 160 * 1024) return 3;
+    hipStream_t s = a.stream;
+    const T* x = static_cast<const T*>(a.x);
+    const T* dy = static_cast<const T*>(a.dy);
+    const T* Bm = static_cast<const T*>(a.B);
+    const T* Cm = static_cast<const T*>(a.C);
+    T* cb = static_cast<T*>(a.cb);
+    T* cbt = static_cast<T*>(a.cbt);
+    T* bt = static_cast<T*>(a.bt);
+    T* ct = static_cast<T*>(a.ct);
+    T* hin = static_cast<T*>(a.hin);
+    T* rin = static_cast<T*>(a.rin);
+
+    Rows rows;
+    rows.ts = nullptr;
+    rows.kb = nullptr;
+    rows.T = a.T;
+    rows.nc = nc;
+    rows.nrows = (int)a.b;
+    rows.H = H;
+    rows.kcap = (int)(a.b * a.nc);
+    const unsigned kc = (unsigned)rows.kcap;
+
+    // the forward's tables and entering states
+    const dim3 g1(kc, 1, (H + 15) / 16);
+    switch (Q) {
+        case 64: k_cumsum<64><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
+        case 128: k_cumsum<128><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
+        case 256: k_cumsum<256><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
+        default: return 3;
+    }
+    const int nb = Q / 64;
+    const dim3 g2(kc, nb * (nb + 1) / 2, (unsigned)G);
+    k_cb<T, N, false><<<g2, kThreads, 0, s>>>(Bm, Cm, cb, rows, G, Q);
+    k_cb<T, N, true><<<g2, kThreads, 0, s>>>(Bm, Cm, cbt, rows, G, Q);
+    const dim3 g6(kc * (unsigned)(Q / 64), (unsigned)G);
+    k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, bt, rows, G, Q);
+    k_bt<T, N><<<g6, kThreads, 0, s>>>(Cm, ct, rows, G, Q);
+    const dim3 g3((unsigned)(a.b * H * nc));
+    k_state<T, P, N, false, false><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
+    const int per_head = (int)((a.P * a.N / 4 + kThreads - 1) / kThreads);
+    const int64_t BHPN = a.b * H * a.P * a.N;
+    const dim3 g4((unsigned)(a.b * H * per_head));
+    k_scan<T, false, 0><<<g4, kThreads, 0, s>>>(a.states, hin, a.dhT ? a.hTf : nullptr, a.h0, a.A, a.cdt, nullptr,
+                                                nullptr, H, (int)(a.P * a.N), (int)a.N, Q, nc, per_head, nc, BHPN);
+    // the adjoint: chunk inputs (into the chunk-state buffer, now free), reverse scan
+    k_state<T, P, N, false, true><<<g3, kThreads, 0, s>>>(dy, Cm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
+    k_scan_rev<T><<<g4, kThreads, 0, s>>>(a.states, rin, a.dh0, a.dhT, a.A, a.cdt, H, (int)(a.P * a.N), Q, nc,
+                                          per_head);
+    // gradients
+    (void)hipFuncSetAttribute((const void*)k_bwd_x<T, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sx);
+    k_bwd_x<T, P, N><<<g3, kThreads, sx, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
+                                              static_cast<T*>(a.dx), a.ds, a.dDp, a.T, H, G, Q, nc);
+    (void)hipFuncSetAttribute((const void*)k_bwd_bc<T, P, N, NB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sbc);
+    const dim3 g7((unsigned)(a.b * nc * G * (Q / 64) * (N / NB)));
+    k_bwd_bc<T, P, N, NB><<<g7, kThreads, sbc, s>>>(x, dy, bt, ct, hin, rin, a.A, a.cdt, static_cast<T*>(a.dB),
+                                                    static_cast<T*>(a.dC), a.T, H, G, Q, nc);
+    k_bwd_dt<T, kThreads><<<(unsigned)(a.b * H), kThreads, 0, s>>>(a.ds, a.dt, a.A, a.dhT, a.hTf, hin, rin, a.ddt,
+                                                                    a.dAp, a.T, H, (int)(a.P * a.N), Q, nc);
+    k_bwd_reduce<kThreads><<<(unsigned)((H + kThreads - 1) / kThreads), kThreads, 0, s>>>(a.dAp, a.dDp, a.dA, a.dD, a.b, H,
+                                                                                 nc);
+    return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+int run_bwd_bf16(const BwdArgs& a);
+int run_bwd_f32(const BwdArgs& a);
+
+}  // namespace ssd

@@ -205,8 +205,11 @@ __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ d
 // group.  Grid (chunks, nb(nb+1)/2, G) over the global chunk axis, nb = Q/64.  Each wave computes the transposed
 // tile cb^T[j][i] for 16 j x 64 i, so a lane ends up owning 4 consecutive j of one
 // row i and stores them as one vector.
+// TR = true writes the same blocks transposed, cbt[j][i] = B_j . C_i (i >= j blocks, i
+// contiguous), the layout the backward pass reads its input-gradient operand from: the
+// operands swap places in the matrix-core step, so a lane then owns 4 consecutive i.
 // ---------------------------------------------------------------------------
-template <typename T, int N>
+template <typename T, int N, bool TR = false>
 __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const T* __restrict__ Cm,
                                                  T* __restrict__ cb, Rows rows, int G, int Q) {
     typedef typename V8<T>::type v8;
@@ -257,14 +260,16 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
             if (ks + DEPTH < KS) load(ks + DEPTH);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) acc[ct] = mma(acc[ct], fb[ks], fc[ks][ct]);
+            for (int ct = 0; ct < 4; ++ct) acc[ct] = TR ? mma(acc[ct], fc[ks][ct], fb[ks]) : mma(acc[ct], fb[ks], fc[ks][ct]);
         }
         T* out = cb + ((int64_t)kg * G + g) * (int64_t)Q * Q;
         const int j0 = J * 64 + 16 * w + 4 * q;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             const int i = I * 64 + 16 * ct + l16;
-            st4(out + (int64_t)i * Q + j0, bf16x4{(bf16)acc[ct][0], (bf16)acc[ct][1], (bf16)acc[ct][2], (bf16)acc[ct][3]});
+            const bf16x4 v = bf16x4{(bf16)acc[ct][0], (bf16)acc[ct][1], (bf16)acc[ct][2], (bf16)acc[ct][3]};
+            if (TR) st4(out + (int64_t)(J * 64 + 16 * w + l16) * Q + I * 64 + 16 * ct + 4 * q, v);
+            else st4(out + (int64_t)i * Q + j0, v);
         }
         return;
     }
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
             const int ir = I * 64 + 16 * ct + l16;
             const bool iv = kv && tok0 + ir < Tn;
             const v8 b = iv ? ld8(Cm + ((bi * Tn + tok0 + ir) * G + g) * N + k0 + 8 * q) : zero8<T>();
-            acc[ct] = mma(acc[ct], a, b);
+            acc[ct] = TR ? mma(acc[ct], b, a) : mma(acc[ct], a, b);
         }
     }
     T* out = cb + ((int64_t)kg * G + g) * (int64_t)Q * Q;
@@ -293,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
         v4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = from_f<T>(acc[ct][r]);
-        st4(out + (int64_t)i * Q + j0, v);
+        if (TR) st4(out + (int64_t)(J * 64 + 16 * w + l16) * Q + I * 64 + 16 * ct + 4 * q, v);
+        else st4(out + (int64_t)i * Q + j0, v);
     }
 }
 
@@ -359,8 +365,11 @@ struct StateTiling {
 // The next slab's global loads are issued into registers before the current slab's
 // matrix-core work.  Waves compute S^T tiles [n][p], so each lane stores 4
 // consecutive n.
+// ADJ = true weights token j by its decay from the chunk start instead,
+// exp(A cdt_j): called with (dy, C) for (x, B) it gives the backward pass's adjoint
+// chunk input sum_{i in chunk} exp(A cdt_i) dy_i C_i^T.
 // ---------------------------------------------------------------------------
-template <typename T, int P, int N, bool DIAG>
+template <typename T, int P, int N, bool DIAG, bool ADJ = false>
 __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, const T* __restrict__ Bm,
                                                     const float* __restrict__ A,
                                                     const float* __restrict__ cdt,
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
                 const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
                 v8 o = xv[r];
                 if (!DIAG) {
-                    const float wj = exp2f_fast(ah2 * (last - cds[j0 + jj]));
+                    const float wj = exp2f_fast(ah2 * (ADJ ? cds[j0 + jj] : last - cds[j0 + jj]));
 #pragma unroll
                     for (int e = 0; e < 8; ++e) o[e] = from_f<T>(to_f(o[e]) * wj);
                 }
@@ -444,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
                 const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
                 v8 o = bv[r];
                 if (DIAG) {
-                    const float dc = last - cds[j0 + jj];
+                    const float dc = ADJ ? cds[j0 + jj] : last - cds[j0 + jj];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) o[e] = from_f<T>(to_f(o[e]) * exp2f_fast(an2[n0 + e] * dc));
                 }

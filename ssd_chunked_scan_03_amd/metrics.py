@@ -1,4 +1,4 @@
-"""Algorithmic work of one SSD forward: matrix-core flops and minimal HBM bytes.
+"""Algorithmic work of one SSD forward (and backward): matrix-core flops and minimal HBM bytes.
 
 Flops use the causal convention: a Q x Q block product counts only the L(L+1)/2
 entries on or below the diagonal (L = tokens in the chunk); C B^T counts once per
@@ -64,6 +64,42 @@ def kernel_bytes(b, T, H, P, N, G, Q, es, diag=False, h0=True) -> dict:
 def path_min_bytes(b, T, H, P, N, G, es, h0=True) -> int:
     return 2 * b * T * H * P * es + 2 * b * T * G * N * es + b * T * H * 4 + \
         (2 if h0 else 1) * b * H * P * N * 4
+
+
+def bwd_path_min_bytes(b, T, H, P, N, G, es, h0=True, dhT=True) -> int:
+    """Backward pass: x, dy, B, C, dt (h0, dhT when given) read once; dx, dB, dC, ddt and
+    dh0 written once (dA, dD are H floats)."""
+    x = b * T * H * P * es
+    bc = b * T * G * N * es
+    dt = b * T * H * 4
+    st = b * H * P * N * 4
+    return 3 * x + 4 * bc + 2 * dt + (st if h0 else 0) + (st if dhT else 0) + st
+
+
+def bwd_kernel_bytes(b, T, H, P, N, G, Q, es, h0=True, dhT=True) -> dict:
+    """Algorithmic bytes of each backward kernel (each operand it must touch, once)."""
+    nc = -(-T // Q)
+    nb = Q // 64
+    x = b * T * H * P * es
+    bc = b * T * G * N * es
+    dt = b * T * H * 4
+    cdt = b * H * nc * Q * 4
+    cbb = b * nc * G * (nb * (nb + 1) // 2) * 64 * 64 * es
+    st32 = b * H * nc * P * N * 4
+    stx = b * H * nc * P * N * es
+    hstate = b * H * P * N * 4
+    ds = b * H * nc * Q * 4
+    return {
+        "k_cumsum": dt + cdt,
+        "k_cb": 2 * bc + cbb,                      # each of the two launches (C B^T, B C^T)
+        "k_bt": 2 * bc,                            # each of the two launches (B, C)
+        "k_state": x + bc + cdt + st32,            # forward chunk states; the adjoint's reads dy, C
+        "k_scan": st32 + b * H * nc * 4 + (hstate if h0 else 0) + stx + (hstate if dhT else 0),
+        "k_scan_rev": st32 + b * H * nc * 4 + (hstate if dhT else 0) + stx + hstate,
+        "k_bwd_x": 2 * x + 2 * bc + 2 * cbb + 2 * stx + cdt + x + ds,
+        "k_bwd_bc": 2 * x + 2 * stx + cdt + 2 * bc + 2 * bc,
+        "k_bwd_dt": ds + dt + (2 * hstate if dhT else 0) + dt,
+    }
 
 
 KERNEL_SOURCES = ("kernels.hpp", "device.hpp", "fused.hpp", "launch.hpp")

@@ -277,3 +277,75 @@ def test_varlen_error_paths_return_before_any_launch():
     assert fn(None, *([None] * 11), 0, None) == ssd_status("SSD_ERR_NULL")
     # no sequences: nothing to do
     assert run(prob=ssd.make_problem(0, T, H, P, N, G, Q, ssd.SSD_BF16)) == 0
+
+
+# ---- backward pass (ssd_scan_bwd) ----
+
+def bwd_fake_ptrs(p):
+    b, T, H, P, N, G = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups
+    es = 2 if p.dtype == ssd.SSD_BF16 else 4
+    lay_bytes = max(ssd.bwd_workspace_bytes(p), 1)
+    xs, bc, st = b * T * H * P * es, b * T * G * N * es, b * H * P * N * 4
+    sizes = dict(x=xs, dt=b * T * H * 4, A=H * 4, B=bc, C=bc, D=H * 4, h0=st, dy=xs, dhT=st,
+                 dx=xs, ddt=b * T * H * 4, dA=H * 4, dB=bc, dC=bc, dD=H * 4, dh0=st, ws=lay_bytes)
+    ptrs, cur = {}, BASE
+    for k, n in sizes.items():
+        ptrs[k] = cur
+        cur += (n + (1 << 20)) // 4096 * 4096 + 4096
+    return ptrs, lay_bytes
+
+
+BWD_ARGS = ("x", "dt", "A", "B", "C", "D", "h0", "dy", "dhT", "dx", "ddt", "dA", "dB", "dC", "dD", "dh0")
+
+
+def call_bwd(p, **over):
+    """ssd_scan_bwd with fake well-formed pointers, some overridden; every use below is
+    invalid on purpose, so the host rejects it before any launch."""
+    ptrs, lay_bytes = bwd_fake_ptrs(p)
+    ws_bytes = over.pop("ws_bytes", lay_bytes)
+    ptrs.update(over)
+    v = lambda k: ctypes.c_void_p(ptrs[k]) if ptrs[k] else None
+    return ssd._load().ssd_scan_bwd(ctypes.byref(p), *(v(k) for k in BWD_ARGS), v("ws"), ws_bytes, None), ptrs
+
+
+def test_bwd_workspace_arithmetic():
+    p = prob()  # b2 T300 H4 P64 N128 G2 Q128 bf16: 3 chunks
+    b, H, P, N, G, Q, nc = 2, 4, 64, 128, 2, 128, 3
+    a = lambda n: (n + 255) // 256 * 256
+    want = (a(b * H * nc * Q * 4) + 2 * a(b * nc * G * Q * Q * 2) + 2 * a(b * nc * G * N * Q * 2)
+            + a(b * H * nc * P * N * 4) + 2 * a(b * H * nc * P * N * 2) + a(b * H * P * N * 4)
+            + a(b * H * nc * Q * 4) + a(b * H * nc * 4) + a(b * H * 4))
+    assert ssd.bwd_workspace_bytes(p) == want
+    assert ssd.bwd_workspace_bytes(prob(T=0)) == 0
+    assert ssd.bwd_workspace_bytes(prob(b=0)) == 0
+    assert ssd.bwd_workspace_bytes(prob(Q=96)) == 0
+    p.flags = ssd.SCHEDULE_SPLIT
+    assert ssd.bwd_workspace_bytes(p) == 0
+
+
+def test_bwd_error_paths_return_before_any_launch():
+    p = prob()
+    S = ssd_status
+    for k in ("x", "dt", "B", "C", "dy", "dx", "ddt", "dB", "dC", "A", "dA"):
+        assert call_bwd(p, **{k: 0})[0] == S("SSD_ERR_NULL"), k
+    assert call_bwd(p, ws=0)[0] == S("SSD_ERR_WORKSPACE")
+    assert call_bwd(p, ws_bytes=100)[0] == S("SSD_ERR_WORKSPACE")
+    for k, off in (("dy", 8), ("dx", 8), ("dB", 8), ("dhT", 4), ("dh0", 4), ("ddt", 2), ("dA", 2), ("ws", 16)):
+        assert call_bwd(p, **{k: BASE + off})[0] == S("SSD_ERR_ALIGN"), k
+    ptrs, _ = bwd_fake_ptrs(p)
+    for out, inp in (("dx", "x"), ("dx", "dy"), ("dB", "C"), ("dC", "ws"), ("dh0", "dhT"), ("dA", "A"),
+                     ("ddt", "dt"), ("dD", "dA"), ("dx", "dB"), ("dh0", "h0")):
+        assert call_bwd(p, **{out: ptrs[inp]})[0] == S("SSD_ERR_ALIAS"), (out, inp)
+    assert call_bwd(prob(H=6, G=4))[0] == S("SSD_ERR_SHAPE")
+    assert call_bwd(prob(Q=32))[0] == S("SSD_ERR_UNSUPPORTED")
+    assert call_bwd(prob(N=24))[0] == S("SSD_ERR_UNSUPPORTED")
+    p = prob()
+    p.flags = ssd.STAGE_CUMSUM
+    assert call_bwd(p)[0] == S("SSD_ERR_UNSUPPORTED")
+    assert ssd._load().ssd_scan_bwd(None, *([None] * 17), 0, None) == S("SSD_ERR_NULL")
+
+
+def test_bwd_empty_problem_aliasing_checked():
+    ptrs, _ = bwd_fake_ptrs(prob(T=0))
+    assert call_bwd(prob(T=0), dA=ptrs["A"])[0] == ssd_status("SSD_ERR_ALIAS")
+    assert call_bwd(prob(T=0), dh0=ptrs["dhT"])[0] == ssd_status("SSD_ERR_ALIAS")

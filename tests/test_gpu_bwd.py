@@ -1,0 +1,180 @@
+"""GPU parity of the backward pass (ssd_scan_bwd) against the fp64 oracle's gradients
+(O4, pinned by finite differences, autograd of the quadratic form and two identities).
+
+Every gradient is compared slice by slice with the metric of the forward tests: per
+(batch, head) for dx, ddt and dh0, per (batch, group) for dB and dC, and over the whole
+vector for dD, ||got - ref||_inf / ||ref||_inf against 1e-4 (float32 problems) or 2e-2
+(bfloat16).  dA_h = sum_{b,t} dt dl (dl = ddt / A_h) is a sum over every token with
+strong cancellation (sum |dt dl| is up to 10^3 times |dA| here), so its tolerance is
+derived from ddt's: if every slice of dl is within tol of its largest entry, then
+|dA_gpu - dA_ref|_h <= tol * sum_b max_t |dl| * sum_t |dt|, and that bound is the gate;
+the GPU's dA must also equal the reduction of its own ddt (float32 summation order
+only).  Outputs and workspace are NaN-poisoned before each call."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_chunked_scan_03_amd as ssd
+from gpu_common import TOL, torch_dtype, upload
+from helpers import max_rel_err
+from ssd_chunked_scan_03_amd.synth import make_grads, make_small
+
+pytestmark = pytest.mark.gpu
+
+SLICES = {"dx": (0, 2), "ddt": (0, 2), "dB": (0, 2), "dC": (0, 2), "dh0": (0, 1), "dD": ()}
+
+
+def vec_rel(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if np.isnan(got).any():
+        return float("inf")
+    den = np.abs(ref).max() if ref.size else 0.0
+    err = np.abs(got - ref).max() if ref.size else 0.0
+    return float(err / den) if den > 0 else float(err)
+
+
+def run_bwd(inp, gr, dtype, chunk, use_D=True, use_h0=True, use_dhT=True):
+    d = upload(inp, dtype)
+    td = torch_dtype(dtype)
+    dy = torch.from_numpy(np.ascontiguousarray(gr["dy"])).to("cuda").to(td).contiguous()
+    dhT = torch.from_numpy(np.ascontiguousarray(gr["dhT"])).to("cuda") if use_dhT else None
+    D = d["D"] if use_D else None
+    h0 = d["h0"] if use_h0 else None
+    x, B = d["x"], d["B"]
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    prob = ssd.make_problem(b, T, H, P, N, G, chunk, ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32)
+    nan = float("nan")
+    out = dict(dx=torch.full_like(x, nan), ddt=torch.full_like(d["dt"], nan), dA=torch.full_like(d["A"], nan),
+               dB=torch.full_like(B, nan), dC=torch.full_like(B, nan),
+               dD=torch.full((H,), nan, device="cuda"), dh0=torch.full((b, H, P, N), nan, device="cuda"))
+    ws = torch.full((max(ssd.bwd_workspace_bytes(prob), 1),), 0xFF, dtype=torch.uint8, device="cuda")
+    ssd.scan_bwd_into(prob, x, d["dt"], d["A"], B, d["C"], D, h0, dy, dhT, out["dx"], out["ddt"], out["dA"],
+                      out["dB"], out["dC"], out["dD"], out["dh0"], ws)
+    torch.cuda.synchronize()
+    got = {k: v.float().cpu().numpy() for k, v in out.items()}
+    ref = oracle.recurrence_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"] if use_D else None,
+                                inp["h0"] if use_h0 else None, dy=gr["dy"], dhT=gr["dhT"] if use_dhT else None)
+    got["_dt"] = ref["_dt"] = np.asarray(inp["dt"], np.float64)
+    got["_A"] = ref["_A"] = np.asarray(inp["A"], np.float64)
+    return got, ref
+
+
+def errors(got, ref):
+    e = {}
+    for k, axes in SLICES.items():
+        e[k] = vec_rel(got[k], ref[k]) if not axes else max_rel_err(got[k], ref[k], axes)
+    # dA against the bound that ddt's gate implies, per head
+    dt, A = ref["_dt"], ref["_A"]
+    dl = ref["ddt"] / A[None, None, :]
+    bound = np.sum(np.abs(dl).max(axis=1) * np.abs(dt).sum(axis=1), axis=0)     # sum_b max_t|dl| sum_t|dt|
+    err = np.abs(np.asarray(got["dA"], np.float64) - ref["dA"])
+    e["dA"] = float(np.max(np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), err))) \
+        if not np.isnan(got["dA"]).any() else float("inf")
+    # the GPU's dA is the reduction of its own ddt (float32 sums on the GPU)
+    terms = np.sum(np.abs(dt * dl), axis=(0, 1))
+    own = np.sum(dt * np.asarray(got["ddt"], np.float64) / A[None, None, :], axis=(0, 1))
+    e["dA_vs_own_ddt"] = float(np.max(np.abs(own - np.asarray(got["dA"], np.float64)) / np.maximum(terms, 1e-30)))
+    e["dA_cond"] = float(np.max(terms / np.maximum(np.abs(ref["dA"]), 1e-30)))  # reported, not gated
+    return e
+
+
+def check(got, ref, dtype, what):
+    e = errors(got, ref)
+    print(f"[bwd {what}] " + " ".join(f"{k}={v:.2e}" for k, v in e.items()), flush=True)
+    bad = {k: v for k, v in e.items() if k != "dA_cond" and not v < (1e-4 if k == "dA_vs_own_ddt" else TOL[dtype])}
+    assert not bad, f"{what}: {bad} (tol {TOL[dtype]})"
+
+
+CASES = [  # b, T, H, P, N, G, Q, dtype
+    (1, 200, 2, 16, 16, 1, 64, "f32"),
+    (2, 300, 4, 64, 64, 2, 64, "bf16"),
+    (2, 300, 4, 64, 64, 2, 128, "f32"),
+    (2, 517, 6, 32, 128, 3, 128, "bf16"),
+    (1, 257, 4, 128, 256, 2, 256, "bf16"),
+    (1, 130, 2, 64, 256, 1, 64, "f32"),
+    (3, 700, 4, 64, 128, 1, 256, "bf16"),
+    (1, 1, 2, 64, 128, 1, 256, "bf16"),
+    (2, 64, 4, 128, 32, 4, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}T{}H{}P{}N{}G{}Q{}{}".format(*c))
+def test_bwd_matches_oracle(case):
+    b, T, H, P, N, G, Q, dtype = case
+    print(f"[bwd case] {case}", flush=True)
+    inp = make_small(b, T, H, P, N, G, seed=31, dtype=dtype)
+    gr = make_grads(b, T, H, P, N, seed=31, dtype=dtype)
+    got, ref = run_bwd(inp, gr, dtype, Q)
+    check(got, ref, dtype, str(case))
+
+
+@pytest.mark.parametrize("use_D,use_h0,use_dhT", [(False, False, False), (True, False, True), (False, True, False)])
+def test_bwd_optional_inputs(use_D, use_h0, use_dhT):
+    inp = make_small(2, 333, 4, 64, 64, 2, seed=32, dtype="bf16")
+    gr = make_grads(2, 333, 4, 64, 64, seed=32, dtype="bf16")
+    got, ref = run_bwd(inp, gr, "bf16", 128, use_D, use_h0, use_dhT)
+    check(got, ref, "bf16", f"D={use_D} h0={use_h0} dhT={use_dhT}")
+
+
+def test_bwd_layer_shapes():
+    """The 780M layer shape in full (b2 T2048 H48 P64 N128 G1 Q256) and one batch row of
+    the 2.7B layer shape (T4096 H80 P64 N128 G1 Q256, nonzero h0): every gradient."""
+    for shape, seed in (((2, 2048, 48, 64, 128, 1), 1), ((1, 4096, 80, 64, 128, 1), 2)):
+        print(f"[bwd layer] {shape}", flush=True)
+        inp = make_small(*shape, seed=seed, dtype="bf16")
+        gr = make_grads(*shape[:5], seed=seed, dtype="bf16")
+        got, ref = run_bwd(inp, gr, "bf16", 256)
+        check(got, ref, "bf16", str(shape))
+
+
+def test_bwd_long_sequence_grouped():
+    """A long, slowly decaying sequence with grouped B/C (T16384 H32 P64 N256 G8 Q256,
+    dt in [1e-4, 1e-2], the long workload's distributions at a quarter of its length)."""
+    shape = (1, 16384, 32, 64, 256, 8)
+    inp = make_small(*shape, seed=3, dtype="bf16", dt_lo=1e-4, dt_hi=1e-2)
+    gr = make_grads(*shape[:5], seed=3, dtype="bf16")
+    got, ref = run_bwd(inp, gr, "bf16", 256)
+    check(got, ref, "bf16", str(shape))
+
+
+def test_bwd_empty():
+    """No tokens: dA = dD = 0, dh0 = dhT (hT is h0); batch 0 writes dA = dD = 0."""
+    H, P, N = 4, 64, 64
+    dhT = torch.randn(2, H, P, N, device="cuda")
+    for b, T in ((2, 0), (0, 5)):
+        prob = ssd.make_problem(b, T, H, P, N, 1, 64, ssd.SSD_BF16)
+        assert ssd.bwd_workspace_bytes(prob) == 0
+        dA = torch.full((H,), float("nan"), device="cuda")
+        dD = torch.full((H,), float("nan"), device="cuda")
+        dh0 = torch.full((max(b, 1), H, P, N), float("nan"), device="cuda")
+        A = torch.ones(H, device="cuda")
+        ssd.scan_bwd_into(prob, None, None, A, None, None, None, None, None, dhT[:max(b, 1)], None, None, dA, None,
+                          None, dD, dh0, None)
+        torch.cuda.synchronize()
+        assert torch.all(dA == 0) and torch.all(dD == 0)
+        if b > 0:
+            assert torch.equal(dh0, dhT[:b])
+
+
+def test_bwd_deterministic():
+    inp = make_small(2, 300, 4, 64, 128, 1, seed=33, dtype="bf16")
+    gr = make_grads(2, 300, 4, 64, 128, seed=33, dtype="bf16")
+    g1, _ = run_bwd(inp, gr, "bf16", 128)
+    g2, _ = run_bwd(inp, gr, "bf16", 128)
+    for k in g1:
+        np.testing.assert_array_equal(g1[k], g2[k], err_msg=k)
+
+
+def test_bwd_python_api_matches_into():
+    inp = make_small(1, 200, 4, 64, 64, 2, seed=34, dtype="bf16")
+    gr = make_grads(1, 200, 4, 64, 64, seed=34, dtype="bf16")
+    d = upload(inp, "bf16")
+    dy = torch.from_numpy(gr["dy"]).to("cuda").to(torch.bfloat16)
+    dhT = torch.from_numpy(gr["dhT"]).to("cuda")
+    out = ssd.scan_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], dy, D=d["D"], h0=d["h0"], dhT=dhT, chunk=64)
+    torch.cuda.synchronize()
+    got, ref = run_bwd(inp, gr, "bf16", 64)
+    for k in out:
+        np.testing.assert_array_equal(out[k].float().cpu().numpy(), got[k], err_msg=k)

@@ -139,3 +139,20 @@ def test_bwd_empty_sequence():
     np.testing.assert_array_equal(gr["dA"], 0.0)
     np.testing.assert_array_equal(gr["dD"], 0.0)
     assert gr["dx"].shape == (2, 0, 4, 3) and gr["dB"].shape == (2, 0, 2, 2)
+
+
+def test_bwd_log_decay_at_chunk_boundaries():
+    """dL/d(dt_t A) at the first token t of a chunk is the inner product of the adjoint
+    arriving there from later tokens, a_t g_t, with the state entering the chunk, h_{t-1}.
+    a_t g_t is dL/dh0 of the suffix problem that starts at t (its initial state is h_{t-1});
+    h_{t-1} is the final state of the prefix.  Both come from O1/O4 on sliced inputs."""
+    ins, dy, dhT = _inputs(2, 50, 4, 6, 5, 2, seed=16, diag=False)
+    full = oracle.recurrence_bwd(*(ins[k] for k in NAMES), dy=dy, dhT=dhT)
+    dl = full["ddt"] / ins["A"][None, None, :]
+    for t in (1, 16, 17, 33, 49):
+        pre = {k: (ins[k][:, :t] if k in ("x", "dt", "B", "C") else ins[k]) for k in NAMES}
+        _, h_prev = oracle.recurrence(*(pre[k] for k in NAMES))
+        suf = {k: (ins[k][:, t:] if k in ("x", "dt", "B", "C") else ins[k]) for k in NAMES}
+        suf["h0"] = h_prev
+        gs = oracle.recurrence_bwd(*(suf[k] for k in NAMES), dy=dy[:, t:], dhT=dhT)
+        np.testing.assert_allclose(dl[:, t, :], np.sum(gs["dh0"] * h_prev, axis=(2, 3)), rtol=1e-10, atol=1e-12)
