@@ -246,7 +246,8 @@ int ssd_diag_step(const ssd_problem* p, const void* x, const float* dt, const fl
  * float32; matrix-core operands in the problem dtype; each output rounded once.
  * `ws` must hold ssd_bwd_workspace_bytes(p) bytes (0 for an empty problem, where dA = dD = 0
  * and dh0 = dhT).  flags must be 0.  Same support set as ssd_scan_fwd (chunk, headdim,
- * dstate, dtype; SSD_ERR_UNSUPPORTED otherwise).  Alignment as for ssd_scan_fwd
+ * dstate, dtype) except float32 with headdim 128 at chunk 256, whose per-head LDS tiles
+ * do not fit one CU: SSD_ERR_UNSUPPORTED.  Alignment as for ssd_scan_fwd
  * (dy, dx, dB, dC 16 bytes; ddt, dA, dD 4; dhT, dh0 16); no output may overlap an input,
  * the workspace or another output (SSD_ERR_ALIAS).  Errors are reported before any HIP
  * call. */

@@ -427,20 +427,42 @@ __global__ __launch_bounds__(kThreads) void k_bwd_x(const T* __restrict__ x, con
 // head (the next head's prefetched into registers meanwhile) and read with the
 // transpose read, p running down the rows.
 // ---------------------------------------------------------------------------
+constexpr int kBcThreads = 512;  // k_bwd_bc work-groups: 8 waves
+
 template <typename T, int P, int NB>
 struct BcSmem {
     static constexpr int PR = P < 32 ? 32 : P;  // rows past P stay zero (k-step padding)
     static constexpr int LDH = NB + 8;
+    static constexpr int LDY = PR + 8;          // dy / x rows of one head
     static constexpr int LDW = 72;              // W columns of the slab
-    __host__ __device__ static int ldc(int Q) { return Q + 8; }  // W rows of the slab
-    __host__ __device__ static size_t phase1(int) { return (size_t)2 * PR * LDH * sizeof(T); }
-    __host__ __device__ static size_t phase2(int Q) { return ((size_t)64 * ldc(Q) + (size_t)Q * LDW) * sizeof(T); }
-    __host__ __device__ static size_t region(int Q) { return phase1(Q) > phase2(Q) ? phase1(Q) : phase2(Q); }
-    __host__ __device__ static size_t bytes(int Q) { return region(Q) + (size_t)5 * Q * sizeof(float); }
+    __host__ __device__ static constexpr int ldc(int Q) { return Q + 8; }  // W rows of the slab
+    // H and R tiles, then the head's dy rows [64 s, Q) and x rows [0, 64 s + 64)
+    __host__ __device__ static constexpr size_t phase1(int Q) {
+        return ((size_t)2 * PR * LDH + (size_t)(Q + 64) * LDY) * sizeof(T);
+    }
+    __host__ __device__ static constexpr size_t phase2(int Q) {
+        return ((size_t)64 * ldc(Q) + (size_t)Q * LDW) * sizeof(T);
+    }
+    __host__ __device__ static constexpr size_t region(int Q) { return phase1(Q) > phase2(Q) ? phase1(Q) : phase2(Q); }
+    __host__ __device__ static constexpr size_t bytes(int Q) { return region(Q) + (size_t)5 * Q * sizeof(float); }
 };
 
+// n range of one k_bwd_bc work-group: the widest (up to 128) whose LDS fits one CU at
+// chunk 256, else at chunk 128 (larger chunks are then reported unsupported)
+template <typename T, int P, int N>
+constexpr int bc_nb() {
+    constexpr size_t lim = 160 * 1024;
+    for (int Q = 256; Q >= 128; Q /= 2) {
+        if (N >= 128 && BcSmem<T, P, 128>::bytes(Q) <= lim) return 128;
+        if (N >= 64 && BcSmem<T, P, 64>::bytes(Q) <= lim) return 64;
+        if (N >= 32 && BcSmem<T, P, 32>::bytes(Q) <= lim) return 32;
+        if (BcSmem<T, P, 16>::bytes(Q) <= lim) return 16;
+    }
+    return 16;
+}
+
 template <typename T, int P, int N, int NB>
-__global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, const T* __restrict__ dy,
+__global__ __launch_bounds__(kBcThreads) void k_bwd_bc(const T* __restrict__ x, const T* __restrict__ dy,
                                                      const T* __restrict__ bt, const T* __restrict__ ct,
                                                      const T* __restrict__ hin, const T* __restrict__ rin,
                                                      const float* __restrict__ A, const float* __restrict__ cdt,
@@ -449,12 +471,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, co
     typedef typename V8<T>::type v8;
     typedef typename V4<T>::type v4;
     typedef BcSmem<T, P, NB> SM;
-    constexpr int PR = SM::PR, LDH = SM::LDH, LDW = SM::LDW, NBT = NB / 16, NR = N / NB;
-    constexpr int NTW = 15;  // W tiles per wave at Q = 256 (58 tiles over 4 waves)
+    constexpr int PR = SM::PR, LDH = SM::LDH, LDY = SM::LDY, LDW = SM::LDW, NBT = NB / 16, NR = N / NB;
+    constexpr int NW = kBcThreads / 64;           // 8 waves
+    constexpr int NTW = (58 + NW - 1) / NW;       // W tiles per wave at Q = 256 (58 tiles)
+    // state terms and products: wave w takes row tile w % 4 of the slab and half the n tiles
+    constexpr int NBH = NBT >= 2 ? NBT / 2 : 1;
     constexpr float LOG2E = 1.4426950408889634f;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     T* Hs = reinterpret_cast<T*>(smem_raw);
     T* Rs = Hs + PR * LDH;
+    T* Ys = Rs + PR * LDH;  // dy row i at Ys[(i - 64 s) * LDY], i in [64 s, Q)
     T* Wc = reinterpret_cast<T*>(smem_raw);  // phase 2: [64][Q + 8]  W rows i of the slab, all j
     T* Wb = Wc + 64 * SM::ldc(Q);            //          [Q][72]      W rows i >= slab start, columns of the slab
     float* cdh = reinterpret_cast<float*>(smem_raw + SM::region(Q));
@@ -480,6 +506,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, co
     const int hpg = H / G, hbeg = g * hpg;
     const int NT = 16 * nslab - 6;  // W tiles the slab needs
     const int s64 = 64 * s;
+    T* Xs = Ys + (Q - s64) * LDY;  // x row j at Xs[j * LDY], j in [0, 64 s + 64)
+    const int NY = Q - s64, NX = s64 + 64;  // staged dy rows, x rows
 
     // tile u -> (I, J): first the rows of the slab (J <= I), then the columns of the slab
     // below it
@@ -500,15 +528,21 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, co
         }
     };
 
-    // rows past P of the staged tiles stay zero
-    for (int v = tid; v < (PR - P) * LDH; v += kThreads) {
+    // rows past P of the staged tiles and columns past P of the staged rows stay zero
+    for (int v = tid; v < (PR - P) * LDH; v += kBcThreads) {
         Hs[P * LDH + v] = from_f<T>(0.f);
         Rs[P * LDH + v] = from_f<T>(0.f);
     }
+    if (PR > P)
+        for (int v = tid; v < (NY + NX) * (PR - P); v += kBcThreads)
+            Ys[(v / (PR - P)) * LDY + P + v % (PR - P)] = from_f<T>(0.f);
 
     constexpr int HV = P * NB / 8;
-    constexpr int HR = (HV + kThreads - 1) / kThreads;
-    v8 hv[HR], rv[HR];
+    constexpr int HR = (HV + kBcThreads - 1) / kBcThreads;
+    constexpr int RV = (256 + 64) * P / 8;          // dy + x row vectors at Q = 256 (at most)
+    constexpr int RR = (RV + kBcThreads - 1) / kBcThreads;
+    const int nrv = (NY + NX) * (P / 8);
+    v8 hv[HR], rv[HR], yv[RR];
     float cv = 0.f, c0v = 0.f, c15v = 0.f, clv = 0.f;
     auto prefetch = [&](int hh) {
         const int64_t bhh = bi * H + hh;
@@ -516,12 +550,25 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, co
         const T* rb = rin + (bhh * nc + c) * (int64_t)(P * N) + n0;
 #pragma unroll
         for (int r = 0; r < HR; ++r) {
-            const int v = tid + r * kThreads;
+            const int v = tid + r * kBcThreads;
             const int pp = v / (NB / 8), nn = (v - pp * (NB / 8)) * 8;
             if (v < HV) {
                 hv[r] = ld8(hb + pp * N + nn);
                 rv[r] = ld8(rb + pp * N + nn);
             }
+        }
+        // the head's dy rows [64 s, Q), then its x rows [0, 64 s + 64); rows past T are zero
+        const T* xh = x + ((bi * Tn + tok0) * H + hh) * P;
+        const T* dyh = dy + ((bi * Tn + tok0) * H + hh) * P;
+#pragma unroll
+        for (int r = 0; r < RR; ++r) {
+            const int v = tid + r * kBcThreads;
+            const int row = v / (P / 8), pp = (v - row * (P / 8)) * 8;
+            const bool isy = row < NY;
+            const int tok = isy ? s64 + row : row - NY;
+            const bool ok = v < nrv && tok < len;
+            const T* src = (isy ? dyh : xh) + (int64_t)(ok ? tok : 0) * H * P + pp;
+            yv[r] = sel8(ok, ld8(src));
         }
         const float* cd = cdt + (bhh * nc + c) * (int64_t)Q;
         if (tid < Q) {
@@ -535,12 +582,18 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, co
     auto stage = [&](int hh) {
 #pragma unroll
         for (int r = 0; r < HR; ++r) {
-            const int v = tid + r * kThreads;
+            const int v = tid + r * kBcThreads;
             const int pp = v / (NB / 8), nn = (v - pp * (NB / 8)) * 8;
             if (v < HV) {
                 st8(&Hs[pp * LDH + nn], hv[r]);
                 st8(&Rs[pp * LDH + nn], rv[r]);
             }
+        }
+#pragma unroll
+        for (int r = 0; r < RR; ++r) {
+            const int v = tid + r * kBcThreads;
+            const int row = v / (P / 8), pp = (v - row * (P / 8)) * 8;
+            if (v < nrv) st8(&Ys[row * LDY + pp], yv[r]);  // Xs follows Ys row for row
         }
         ah2 = A[hh] * LOG2E;
         if (tid < Q) {
@@ -552,12 +605,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, co
         }
     };
 
-    f32x4 accW[NTW], accC[NBT], accB[NBT];
+    f32x4 accW[NTW], accC[NBH], accB[NBH];
 #pragma unroll
     for (int m = 0; m < NTW; ++m) accW[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < NBT; ++nt) accC[nt] = accB[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int iw = s64 + w * 16 + l16;  // this wave's row (dC) and column (dB) token
+    for (int nt = 0; nt < NBH; ++nt) accC[nt] = accB[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int rt = w & 3, nh = w >> 2;             // row tile, n-tile half
+    const bool sact = NBT >= 2 || nh == 0;         // (one n tile: the second half idles)
+    const int nb0 = NBT >= 2 ? nh * NBH : 0;       // first n tile of this wave
+    const int iw = s64 + rt * 16 + l16;            // this wave's row (dC) and column (dB) token
 
     prefetch(hbeg);
     for (int hh = hbeg; hh < hbeg + hpg; ++hh) {
@@ -565,26 +621,19 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, co
         stage(hh);
         __syncthreads();
         if (hh + 1 < hbeg + hpg) prefetch(hh + 1);
-        const T* xh = x + ((bi * Tn + tok0) * H + hh) * P;   // row j at + j * H * P
-        const T* dyh = dy + ((bi * Tn + tok0) * H + hh) * P;
 
         // W tiles of this head, decay-masked, summed into accW
 #pragma unroll
         for (int m = 0; m < NTW; ++m) {
-            const int u = w + 4 * m;
+            const int u = w + NW * m;
             if (u < NT) {
                 int I, J;
                 tile_ij(u, I, J);
                 const int i = I * 16 + l16, j = J * 16 + l16;
                 f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int p0 = 0; p0 < P; p0 += 32) {
-                    const int pp = p0 + 8 * q;
-                    const bool pv = (P % 32 == 0) || (pp < P);
-                    const v8 a = sel8(pv && i < len, ld8(dyh + (int64_t)(i < len ? i : 0) * H * P + (pv ? pp : 0)));
-                    const v8 b = sel8(pv && j < len, ld8(xh + (int64_t)(j < len ? j : 0) * H * P + (pv ? pp : 0)));
-                    t = mma(t, a, b);
-                }
+                for (int p0 = 0; p0 < PR; p0 += 32)
+                    t = mma(t, ld8(&Ys[(i - s64) * LDY + p0 + 8 * q]), ld8(&Xs[j * LDY + p0 + 8 * q]));
                 // lane: W[I*16 + 4q + r][J*16 + l16]
                 if (I > J) {
                     const float f = exp2f_fast(ah2 * (cdh[I * 16] - cdh[J * 16 + 15])) * ee[J * 16 + l16];
@@ -602,23 +651,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, co
             }
         }
 
-        // state terms: this wave's 16 tokens, all n tiles of the range
+        // state terms: this wave's 16 tokens, its half of the n tiles of the range
         const float si = sci[iw], sj = scj[iw];
 #pragma unroll
         for (int p0 = 0; p0 < PR; p0 += 32) {
-            const int pp = p0 + 8 * q;
-            const bool pv = (P % 32 == 0) || (pp < P);
-            v8 yb = sel8(pv && iw < len, ld8(dyh + (int64_t)(iw < len ? iw : 0) * H * P + (pv ? pp : 0)));
-            v8 xb8 = sel8(pv && iw < len, ld8(xh + (int64_t)(iw < len ? iw : 0) * H * P + (pv ? pp : 0)));
+            if (!sact) break;
+            v8 yb = ld8(&Ys[(iw - s64) * LDY + p0 + 8 * q]);
+            v8 xb8 = ld8(&Xs[iw * LDY + p0 + 8 * q]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 yb[e] = from_f<T>(to_f(yb[e]) * si);
                 xb8[e] = from_f<T>(to_f(xb8[e]) * sj);
             }
 #pragma unroll
-            for (int nt = 0; nt < NBT; ++nt) {
-                accC[nt] = mma(accC[nt], frag_rows(Hs, LDH, p0, nt * 16, lane), yb);
-                accB[nt] = mma(accB[nt], frag_rows(Rs, LDH, p0, nt * 16, lane), xb8);
+            for (int nt = 0; nt < NBH; ++nt) {
+                accC[nt] = mma(accC[nt], frag_rows(Hs, LDH, p0, (nb0 + nt) * 16, lane), yb);
+                accB[nt] = mma(accB[nt], frag_rows(Rs, LDH, p0, (nb0 + nt) * 16, lane), xb8);
             }
         }
     }
@@ -628,13 +676,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, co
     {
         const int nvec = (int)(SM::phase2(Q) / 16);
         u32x4v* z = reinterpret_cast<u32x4v*>(smem_raw);
-        for (int v = tid; v < nvec; v += kThreads) z[v] = u32x4v{0u, 0u, 0u, 0u};
+        for (int v = tid; v < nvec; v += kBcThreads) z[v] = u32x4v{0u, 0u, 0u, 0u};
     }
     __syncthreads();
     const int ldc = SM::ldc(Q);
 #pragma unroll
     for (int m = 0; m < NTW; ++m) {
-        const int u = w + 4 * m;
+        const int u = w + NW * m;
         if (u < NT) {
             int I, J;
             tile_ij(u, I, J);
@@ -651,31 +699,32 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bc(const T* __restrict__ x, co
     __syncthreads();
     const T* btb = bt + ((bi * nc + c) * G + g) * (int64_t)N * Q + (int64_t)n0 * Q;  // [n][j]
     const T* ctb = ct + ((bi * nc + c) * G + g) * (int64_t)N * Q + (int64_t)n0 * Q;
+    if (!sact) return;
     for (int j0 = 0; j0 < s64 + 64; j0 += 32) {
         const v8 wf = ld8(&Wc[(iw - s64) * ldc + j0 + 8 * q]);
 #pragma unroll
-        for (int nt = 0; nt < NBT; ++nt)
-            accC[nt] = mma(accC[nt], ld8(btb + (int64_t)(nt * 16 + l16) * Q + j0 + 8 * q), wf);
+        for (int nt = 0; nt < NBH; ++nt)
+            accC[nt] = mma(accC[nt], ld8(btb + (int64_t)((nb0 + nt) * 16 + l16) * Q + j0 + 8 * q), wf);
     }
     for (int i0 = s64; i0 < Q; i0 += 32) {
-        const v8 wf = frag_rows(Wb, LDW, i0 - s64, w * 16, lane);
+        const v8 wf = frag_rows(Wb, LDW, i0 - s64, rt * 16, lane);
 #pragma unroll
-        for (int nt = 0; nt < NBT; ++nt)
-            accB[nt] = mma(accB[nt], ld8(ctb + (int64_t)(nt * 16 + l16) * Q + i0 + 8 * q), wf);
+        for (int nt = 0; nt < NBH; ++nt)
+            accB[nt] = mma(accB[nt], ld8(ctb + (int64_t)((nb0 + nt) * 16 + l16) * Q + i0 + 8 * q), wf);
     }
     if (iw < len) {
         T* dCr = dC + ((bi * Tn + tok0 + iw) * G + g) * N + n0;
         T* dBr = dB + ((bi * Tn + tok0 + iw) * G + g) * N + n0;
 #pragma unroll
-        for (int nt = 0; nt < NBT; ++nt) {
+        for (int nt = 0; nt < NBH; ++nt) {
             v4 oc, ob;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 oc[r] = from_f<T>(accC[nt][r]);
                 ob[r] = from_f<T>(accB[nt][r]);
             }
-            st4(dCr + nt * 16 + 4 * q, oc);
-            st4(dBr + nt * 16 + 4 * q, ob);
+            st4(dCr + (nb0 + nt) * 16 + 4 * q, oc);
+            st4(dBr + (nb0 + nt) * 16 + 4 * q, ob);
         }
     }
 }

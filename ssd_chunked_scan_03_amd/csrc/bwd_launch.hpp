@@ -40,12 +40,9 @@ struct BwdArgs {
     hipStream_t stream;
 };
 
-// n range of one k_bwd_bc work-group
-template <int N> constexpr int bc_nb() { return N <= 128 ? N : 128; }
-
 template <typename T, int P, int N>
 int run_bwd(const BwdArgs& a) {
-    constexpr int NB = bc_nb<N>();
+    constexpr int NB = bc_nb<T, P, N>();
     const int Q = (int)a.Q, nc = (int)a.nc, H = (int)a.H, G = (int)a.G;
     const size_t sx = BxSmem<T, P>::bytes(Q), sbc = BcSmem<T, P, NB>::bytes(Q);
     if (sx > 160 * 1024 || sbc > 160 * 1024) return 3;
@@ -103,7 +100,7 @@ int run_bwd(const BwdArgs& a) {
                                               static_cast<T*>(a.dx), a.ds, a.dDp, a.T, H, G, Q, nc);
     (void)hipFuncSetAttribute((const void*)k_bwd_bc<T, P, N, NB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sbc);
     const dim3 g7((unsigned)(a.b * nc * G * (Q / 64) * (N / NB)));
-    k_bwd_bc<T, P, N, NB><<<g7, kThreads, sbc, s>>>(x, dy, bt, ct, hin, rin, a.A, a.cdt, static_cast<T*>(a.dB),
+    k_bwd_bc<T, P, N, NB><<<g7, kBcThreads, sbc, s>>>(x, dy, bt, ct, hin, rin, a.A, a.cdt, static_cast<T*>(a.dB),
                                                     static_cast<T*>(a.dC), a.T, H, G, Q, nc);
     k_bwd_dt<T, kThreads><<<(unsigned)(a.b * H), kThreads, 0, s>>>(a.ds, a.dt, a.A, a.dhT, a.hTf, hin, rin, a.ddt,
                                                                     a.dAp, a.T, H, (int)(a.P * a.N), Q, nc);
