@@ -14,6 +14,12 @@
 
   python -m ssd_chunked_scan_03_amd.profsum counters DIR [--kernel REGEX]
       mean value per (kernel, counter) of any `--pmc` run, as a markdown table.
+
+  python -m ssd_chunked_scan_03_amd.profsum mfma DIR --trace DIR --command "..."
+      matrix-core use per kernel from a `--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+      SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE` run: counted flops (MOPS x 512), busy
+      cycles as a share of GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs, and counted TFLOP/s over
+      the kernel's average duration in the trace run.
 """
 from __future__ import annotations
 
@@ -140,6 +146,44 @@ def cmd_counters(args):
         print(f"| {k} | {c} | {len(d)} | {statistics.mean(d.values()):.6g} |")
 
 
+CUS, SIMDS = 256, 4
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def cmd_mfma(args):
+    agg = {}
+    for name, disp, cname, val in pmc_rows(args.dir):
+        agg.setdefault(short_name(name), {}).setdefault(cname, {}).setdefault(disp, 0.0)
+        agg[short_name(name)][cname][disp] += val
+    durs = {}
+    if args.trace:
+        rows, _ = trace_rows(args.trace)
+        for short, _full, calls, total, avg, pct in rows:
+            durs.setdefault(short, []).append((calls, avg))
+    print(f"Command (from the repository root on one MI355X):\n\n    {args.command}\n")
+    print(f"Kernel sources hash: `{kernel_source_hash()}`\n")
+    print("Counted flops are the bf16 matrix-core operations the kernel issued (MOPS x 512).  The busy column is "
+          "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs) x 8: GRBM_GUI_ACTIVE reads as the sum "
+          "over the 8 XCDs, and with that factor the busy share agrees with the flop-based share.\n")
+    print("| kernel | dispatches | counted GFLOP (MOPS x 512) | MFMA busy share | "
+          "avg us (trace) | counted TFLOP/s | % of bf16 peak |")
+    print("|---|---|---|---|---|---|---|")
+    for k, cs in sorted(agg.items()):
+        mops = cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        busy = cs.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        act = cs.get("GRBM_GUI_ACTIVE")
+        if not mops or not busy or not act or statistics.median(mops.values()) == 0:
+            continue
+        gf = statistics.median(mops.values()) * 512 / 1e9
+        util = 8 * statistics.median(busy.values()) / (statistics.median(act.values()) * CUS * SIMDS)
+        avg = None
+        if k in durs:
+            calls, avg = max(durs[k])  # the most-called instance of that kernel name
+        tf = gf / (avg * 1e-6) / 1e3 if avg else None
+        print(f"| {k} | {len(mops)} | {gf:.2f} | {100 * util:.1f}% | {avg if avg else float('nan'):.1f} | "
+              f"{tf if tf else float('nan'):.1f} | {100 * tf / BF16_PEAK_TFLOPS if tf else float('nan'):.1f}% |")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="profsum")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -158,8 +202,12 @@ def main(argv=None):
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.add_argument("--kernel", default=None)
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--trace", default=None)
+    m.add_argument("--command", required=True)
     args = ap.parse_args(argv)
-    {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters}[args.cmd](args)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "counters": cmd_counters, "mfma": cmd_mfma}[args.cmd](args)
 
 
 if __name__ == "__main__":
