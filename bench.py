@@ -139,9 +139,10 @@ def main():
     kb = metrics.kernel_bytes(b, T, H, P, N, G, Q, 2 if w.dtype == "bf16" else 4, w.diag, h0 is not None)
     ksteps = args.kernel_steps or max(10, args.steps)
     schedule = ssd.schedule_of(prob, w.diag)
-    names = [k for k in (ssd.FUSED_KERNELS if schedule == "fused" else ssd.SPLIT_KERNELS)
-             if not (w.diag and k == "k_cb")]
-    staged = [ssd.make_problem(b, T, H, P, N, G, Q, dcode, flags=ssd.STAGES[k] | sched_flag) for k in names]
+    plan = ssd.schedule_kernels(schedule, w.diag)
+    names = [k for k, _ in plan]
+    staged = [ssd.make_problem(b, T, H, P, N, G, Q, dcode, flags=m | sched_flag) for _, m in plan]
+    kb["k_prep"] = kb["k_cumsum"] + kb["k_cb"] + (kb["k_bt"] if schedule == "fused" else 0)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(ksteps)]
     for _ in range(2):
         for pk in staged:

@@ -109,6 +109,16 @@ SPLIT_KERNELS = ("k_cumsum", "k_cb", "k_state", "k_scan", "k_out")
 FUSED_KERNELS = ("k_cumsum", "k_cb", "k_bt", "k_fused")
 
 
+def schedule_kernels(schedule: str, diag: bool):
+    """(kernel name, stage mask) in the order a whole forward launches them.  A whole
+    forward runs its preparation (cumsum, C B^T, and B^T on the fused schedule) as one
+    launch, k_prep; a stage mask that holds all of those bits runs that same launch."""
+    if schedule == "fused":
+        return [("k_prep", STAGE_CUMSUM | STAGE_CB | STAGE_BT), ("k_fused", STAGE_FUSED)]
+    first = [("k_cumsum", STAGE_CUMSUM)] if diag else [("k_prep", STAGE_CUMSUM | STAGE_CB)]
+    return first + [("k_state", STAGE_STATE), ("k_scan", STAGE_SCAN), ("k_out", STAGE_OUT)]
+
+
 def fused_supported(dtype_code, diag, P, N) -> bool:
     """Whether the fused per-(batch, head) kernel exists for this problem."""
     return dtype_code == SSD_BF16 and not diag and P == 64 and N in (64, 128)

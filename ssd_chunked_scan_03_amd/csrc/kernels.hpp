@@ -139,17 +139,16 @@ __global__ __launch_bounds__(BLOCK) void k_rows(const int* __restrict__ cu, int 
 // wave prefix sum.
 // ---------------------------------------------------------------------------
 template <int Q>
-__global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ dt,
-                                                     float* __restrict__ cdt, Rows rows) {
+__device__ __forceinline__ void cumsum_body(const float* __restrict__ dt, float* __restrict__ cdt, Rows rows,
+                                            int k, int hz) {
     constexpr int HS = 16, QPL = Q / 64;
     __shared__ float s[HS][Q + 1];
-    const int k = blockIdx.x;
     if (k >= rows.total_chunks()) return;
     const int r = rows.row_of(k);
     const int c = k - rows.kbase(r);
     const int64_t T = rows.len(r), rt0 = rows.tok0(r);
     const int H = rows.H;
-    const int hbase = blockIdx.z * HS;
+    const int hbase = hz * HS;
     const int tid = threadIdx.x;
     for (int idx = tid; idx < Q * HS; idx += kThreads) {
         const int t = idx / HS, hh = idx - t * HS;
@@ -198,6 +197,12 @@ __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ d
     }
 }
 
+template <int Q>
+__global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ dt,
+                                                     float* __restrict__ cdt, Rows rows) {
+    cumsum_body<Q>(dt, cdt, rows, blockIdx.x, blockIdx.z);
+}
+
 // ---------------------------------------------------------------------------
 // k_cb: cb[b,c,g][i][j] = sum_n C[b,cQ+i,g,n] B[b,cQ+j,g,n] for the 64x64 blocks on
 // and below the diagonal (block row >= block column); tokens past T read as 0.
@@ -210,11 +215,10 @@ __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ d
 // operands swap places in the matrix-core step, so a lane then owns 4 consecutive i.
 // ---------------------------------------------------------------------------
 template <typename T, int N, bool TR = false>
-__global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const T* __restrict__ Cm,
-                                                 T* __restrict__ cb, Rows rows, int G, int Q) {
+__device__ __forceinline__ void cb_body(const T* __restrict__ Bm, const T* __restrict__ Cm, T* __restrict__ cb,
+                                        Rows rows, int G, int Q, int kg, int pidx, int g) {
     typedef typename V8<T>::type v8;
     typedef typename V4<T>::type v4;
-    const int kg = blockIdx.x;  // global chunk
     if (kg >= rows.total_chunks()) return;
     const int rr = rows.row_of(kg);
     const int c = kg - rows.kbase(rr);
@@ -224,10 +228,8 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
     Cm += rows.tok0(rr) * G * N;
     const int64_t bi = 0;
     int I = 0;
-    const int pidx = blockIdx.y;
     while ((I + 1) * (I + 2) / 2 <= pidx) ++I;
     const int J = pidx - I * (I + 1) / 2;
-    const int g = blockIdx.z;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l16 = lane & 15, q = lane >> 4;
     const int64_t tok0 = (int64_t)c * Q;
@@ -303,6 +305,12 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
     }
 }
 
+template <typename T, int N, bool TR = false>
+__global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                                 T* __restrict__ cb, Rows rows, int G, int Q) {
+    cb_body<T, N, TR>(Bm, Cm, cb, rows, G, Q, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
 // ---------------------------------------------------------------------------
 // k_bt: Bt[b,c,g][n][j] = B[b, cQ+j, g, n] (0 past T): each chunk's B with tokens
 // contiguous, the layout the fused kernel reads its chunk-state A operand from.
@@ -310,20 +318,17 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
 // work-group, transposed through LDS.
 // ---------------------------------------------------------------------------
 template <typename T, int N>
-__global__ __launch_bounds__(kThreads) void k_bt(const T* __restrict__ Bm, T* __restrict__ Bt, Rows rows,
-                                                 int G, int Q) {
+__device__ __forceinline__ void bt_body(const T* __restrict__ Bm, T* __restrict__ Bt, Rows rows, int G, int Q,
+                                        int kg, int j0, int g) {
     typedef typename V8<T>::type v8;
     constexpr int JB = 64, LD = JB + 8;
     __shared__ __attribute__((aligned(16))) T s[N * LD];
-    const int slabs = Q / JB;
-    const int kg = blockIdx.x / slabs, j0 = (blockIdx.x - kg * slabs) * JB;
     if (kg >= rows.total_chunks()) return;
     const int rr = rows.row_of(kg);
     const int c = kg - rows.kbase(rr);
     const int64_t Tn = rows.len(rr);
     Bm += rows.tok0(rr) * G * N;
     const int64_t bi = 0;
-    const int g = blockIdx.y;
     const int64_t tok0 = (int64_t)c * Q + j0;
     for (int v = threadIdx.x; v < JB * N / 8; v += kThreads) {
         const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
@@ -337,6 +342,43 @@ __global__ __launch_bounds__(kThreads) void k_bt(const T* __restrict__ Bm, T* __
         const int n = v / (JB / 8), jv = (v - n * (JB / 8)) * 8;
         st8(out + (int64_t)n * Q + jv, ld8(&s[n * LD + jv]));
     }
+}
+
+template <typename T, int N>
+__global__ __launch_bounds__(kThreads) void k_bt(const T* __restrict__ Bm, T* __restrict__ Bt, Rows rows,
+                                                 int G, int Q) {
+    const int slabs = Q / 64;
+    const int kg = blockIdx.x / slabs;
+    bt_body<T, N>(Bm, Bt, rows, G, Q, kg, (blockIdx.x - kg * slabs) * 64, blockIdx.y);
+}
+
+// ---------------------------------------------------------------------------
+// k_prep: the per-chunk preparation of a forward in one launch.  The three tables do
+// not depend on one another, so one grid (chunks, tasks) runs them side by side:
+//   y in [0, nh)                       k_cumsum's work for heads 16 y .. 16 y + 15
+//   y in [nh, nh + npair G)            k_cb's work for block pair (y - nh) % npair, group (y - nh) / npair
+//   y in [nh + npair G, + nslab G)     k_bt's work for 64-token slab, group (when BT)
+// (nh = ceil(H / 16), npair = nb (nb + 1) / 2 with nb = Q / 64, nslab = Q / 64.)
+// ---------------------------------------------------------------------------
+template <typename T, int N, int Q, bool BT>
+__global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ dt, float* __restrict__ cdt,
+                                                   const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                                   T* __restrict__ cb, T* __restrict__ Bt, Rows rows, int G) {
+    constexpr int nb = Q / 64, npair = nb * (nb + 1) / 2, nslab = Q / 64;
+    const int nh = (rows.H + 15) / 16;
+    const int k = blockIdx.x;
+    int y = blockIdx.y;
+    if (y < nh) {
+        cumsum_body<Q>(dt, cdt, rows, k, y);
+        return;
+    }
+    y -= nh;
+    if (y < npair * G) {
+        cb_body<T, N, false>(Bm, Cm, cb, rows, G, Q, k, y % npair, y / npair);
+        return;
+    }
+    y -= npair * G;
+    if (BT) bt_body<T, N>(Bm, Bt, rows, G, Q, k, (y % nslab) * 64, y / nslab);
 }
 
 // ---------------------------------------------------------------------------

@@ -94,7 +94,7 @@ int run(const RunArgs& a) {
     if (a.force_fused && !fused_supported(a, kBF16)) return 3;
     const bool fused = fused_applies(a, kBF16);
     if (a.ts && (!fused || a.force_split)) return 3;  // packed rows: fused schedule only
-    const int st = a.stages ? a.stages : (fused ? (1 | 2 | 32 | 64) : (1 | 2 | 4 | 8 | 16));
+    int st = a.stages ? a.stages : (fused ? (1 | 2 | 32 | 64) : (1 | 2 | 4 | 8 | 16));
     const int Q = (int)a.Q, nc = (int)a.nc, H = (int)a.H, G = (int)a.G;
     hipStream_t s = a.stream;
     const T* x = static_cast<const T*>(a.x);
@@ -111,6 +111,21 @@ int run(const RunArgs& a) {
     // the prep kernels run over the global chunk axis (blocks past the last chunk exit)
     const Rows rows = rows_of(a);
     const unsigned kc = (unsigned)rows.kcap;
+    // the whole preparation of a forward (cumsum, C B^T, and B^T for the fused schedule)
+    // in one launch; a stage mask that asks for part of it runs the separate kernels
+    const int prep_bits = fused ? (1 | 2 | 32) : (1 | 2);
+    if (!a.diag && (st & prep_bits) == prep_bits) {
+        const int nb = Q / 64;
+        const dim3 gp(kc, (unsigned)((H + 15) / 16 + (nb * (nb + 1) / 2) * G + (fused ? nb * G : 0)));
+        switch (Q * 2 + (fused ? 1 : 0)) {
+#define SSD_PREP(QQ, F) \
+    case QQ * 2 + F: k_prep<T, N, QQ, F><<<gp, kThreads, 0, s>>>(a.dt, a.cdt, Bm, Cm, cb, static_cast<T*>(a.bt), rows, G); break;
+            SSD_PREP(64, 0) SSD_PREP(64, 1) SSD_PREP(128, 0) SSD_PREP(128, 1) SSD_PREP(256, 0) SSD_PREP(256, 1)
+#undef SSD_PREP
+            default: return 3;
+        }
+        st &= ~prep_bits;
+    }
     const dim3 g1(kc, 1, (H + 15) / 16);
     if (st & 1) switch (Q) {
         case 64: k_cumsum<64><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
