@@ -224,8 +224,10 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         bms = e0.elapsed_time(e1) / bsteps
-        bmin = metrics.bwd_path_min_bytes(b, T, H, P, N, G, 2 if w.dtype == "bf16" else 4, h0 is not None, True)
+        es_ = 2 if w.dtype == "bf16" else 4
+        bmin = metrics.bwd_path_min_bytes(b, T, H, P, N, G, es_, h0 is not None, True)
         backward = {"ms": round(bms, 5), "tokens_per_s": round(b * T / (bms * 1e-3), 1), "steps": bsteps,
+                    "inputs": "x, dt, A, B, C, D, h0, dy, dhT (y is recomputed, not stored)",
                     "path_min_bytes": bmin,
                     "path_hbm_frac": round(bmin / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "workspace_bytes": int(bws.numel())}

@@ -319,7 +319,7 @@ int step(const ssd_problem* p, int diag, const void* x, const float* dt, const f
 
 // ---- backward pass (ssd_scan_bwd) ----
 struct BwdLayout {
-    size_t cdt, cb, cbt, bt, ct, states, hin, rin, hTf, ds, dDp, dAp, total;
+    size_t cdt, cb, cbt, bt, ct, states, hin, rin, hTf, ds, dDp, dAp, kpart, total;
 };
 
 BwdLayout bwd_layout_of(const ssd_problem* p) {
@@ -344,7 +344,8 @@ BwdLayout bwd_layout_of(const ssd_problem* p) {
     take(L.hTf, (size_t)(b * H * P * N) * 4);
     take(L.ds, bhc * (size_t)Q * 4);
     take(L.dDp, bhc * 4);
-    take(L.dAp, (size_t)(b * H) * 4);
+    take(L.dAp, bhc * 4);
+    take(L.kpart, bhc * (size_t)(4 * ((P * N / 4 + 255) / 256)) * 4);
     L.total = (b == 0 || p->seqlen == 0) ? 0 : off;
     return L;
 }
@@ -437,6 +438,7 @@ int scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* 
     a.ds = reinterpret_cast<float*>(w + L.ds);
     a.dDp = reinterpret_cast<float*>(w + L.dDp);
     a.dAp = reinterpret_cast<float*>(w + L.dAp);
+    a.kpart = reinterpret_cast<float*>(w + L.kpart);
     a.stream = s;
     return p->dtype == SSD_BF16 ? ssd::run_bwd_bf16(a) : ssd::run_bwd_f32(a);
 }

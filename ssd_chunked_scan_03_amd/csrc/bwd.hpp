@@ -36,11 +36,11 @@
 // Kernels, in launch order after the forward's k_cumsum, k_cb (both orientations), k_bt
 // (B and C), k_state and k_scan (entering states H_c, final state hT):
 //   k_state<ADJ>  adjoint chunk inputs S'_c                        -> states (reused)
-//   k_scan_rev    R_c per chunk, dh0                               -> rin, dh0
+//   k_scan_rev    R_c per chunk, dh0, partials of <R_c, H_{c+1}>     -> rin, dh0, kpart
 //   k_bwd_x       dx, per-token decay term, D partial sums, per (b, h, c)
 //   k_bwd_bc      dB and dC per (b, c, group, 64-row slab, n range)
-//   k_bwd_dt      chunk-boundary values <R_c, H_{c+1}>, reverse running sums within
-//                 each chunk -> ddt, per-(b, h) A partial sums
+//   k_bwd_dt      reverse running sums within each chunk from the boundary values
+//                 <R_c, H_{c+1}> -> ddt, per-(b, h, c) A partial sums
 //   k_bwd_reduce  dA, dD
 #pragma once
 
@@ -64,42 +64,66 @@ __device__ __forceinline__ float sum_wave(float v) {
 // k_scan_rev: the adjoint carried across chunks, last chunk first:
 //   R = dhT;  for c = nc-1 .. 0: rin[c] = R;  R = exp(A cdt_last(c)) R + S'_c;  dh0 = R
 // Parallel over b x H x P x N like k_scan (4 consecutive elements per thread), loads
-// issued 8 chunks ahead.
+// issued 8 chunks ahead.  On the way it forms the decay gradient's value at the start of
+// chunk c + 1, <R_c, H_{c+1}> (H_nc = hT, the forward's final state, when dhT is given):
+// each wave reduces its elements' share and writes one partial per chunk,
+// kpart[b, h, c, (block part) * 4 + wave], summed in that order by k_bwd_dt.  (P N / 4
+// is a multiple of 64, so every wave is either whole or absent.)
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_scan_rev(const float* __restrict__ S, T* __restrict__ rin,
                                                        float* __restrict__ dh0, const float* __restrict__ dhT,
                                                        const float* __restrict__ A, const float* __restrict__ cdt,
-                                                       int H, int PN, int Q, int nc, int per_head) {
+                                                       const T* __restrict__ hin, const float* __restrict__ hTf,
+                                                       float* __restrict__ kpart, int H, int PN, int Q, int nc,
+                                                       int per_head) {
     typedef typename V4<T>::type v4;
     const int64_t bh = blockIdx.x / per_head;
     const int part = (int)(blockIdx.x - bh * per_head);
     const int h = (int)(bh % H);
     const int e0 = (part * kThreads + threadIdx.x) * 4;
     if (e0 >= PN) return;
+    const int lane = threadIdx.x & 63, slot = part * 4 + (int)(threadIdx.x >> 6), nslot = per_head * 4;
     const float a = A[h];
     f32x4 st = dhT ? ld4(dhT + bh * PN + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
     const float* cl = cdt + bh * (int64_t)nc * Q + (Q - 1);
     const float* sp = S + bh * (int64_t)nc * PN + e0;
     T* rp = rin + bh * (int64_t)nc * PN + e0;
+    const T* hp = hin + bh * (int64_t)nc * PN + e0;
+    float* kp = kpart + bh * (int64_t)nc * nslot + slot;
     constexpr int DEPTH = 8;
     for (int c0 = nc - 1; c0 >= 0; c0 -= DEPTH) {
         f32x4 s[DEPTH];
         float Lc[DEPTH];
+        f32x4 hn[DEPTH];  // H_{c+1}: the state entering the next chunk
 #pragma unroll
         for (int k = 0; k < DEPTH; ++k) {
-            if (c0 - k >= 0) {
-                s[k] = ld4(sp + (int64_t)(c0 - k) * PN);
-                Lc[k] = cl[(int64_t)(c0 - k) * Q];
+            const int c = c0 - k;
+            if (c >= 0) {
+                s[k] = ld4(sp + (int64_t)c * PN);
+                Lc[k] = cl[(int64_t)c * Q];
+                if (c + 1 < nc) {
+                    const v4 hv = ld4(hp + (int64_t)(c + 1) * PN);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) hn[k][r] = to_f(hv[r]);
+                } else {
+                    hn[k] = dhT ? ld4(hTf + bh * PN + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             }
         }
 #pragma unroll
         for (int k = 0; k < DEPTH; ++k) {
-            if (c0 - k >= 0) {
+            const int c = c0 - k;
+            if (c >= 0) {
                 v4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = from_f<T>(st[r]);
-                st4(rp + (int64_t)(c0 - k) * PN, o);
+                st4(rp + (int64_t)c * PN, o);
+                float dot = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dot += st[r] * hn[k][r];
+                dot = sum_wave(dot);
+                if (lane == 0) kp[(int64_t)c * nslot] = dot;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) st[r] = exp_f(a * Lc[k]) * st[r] + s[k][r];
             }
@@ -111,7 +135,9 @@ __global__ __launch_bounds__(kThreads) void k_scan_rev(const float* __restrict__
 // ---------------------------------------------------------------------------
 // k_bwd_x: one (b, h, c) chunk of the input gradient and of the decay term.
 //   phase 1  yhat^T[p][i] = sum_{j <= i} (L o C B^T)_ij x_j[p] + exp(A cdt_i) (H_c C_i)[p]
-//            (y without the D term, fp32), then dy_i . yhat_i and dy_i . x_i
+//            (y without the D term, fp32), then dy_i . yhat_i and dy_i . x_i.  (Not the
+//            forward's stored y: y - D x from a bf16 y loses the bits of the state-space
+//            part whenever D x dominates y.)
 //   phase 2  dxhat^T[p][j] = sum_{i >= j} (L o C B^T)_ij dy_i[p] + exp(A (cdt_last - cdt_j)) (R_c B_j)[p]
 //            then x_j . dxhat_j; ds_j = dy_j . yhat_j - x_j . dxhat_j; dx = dxhat + D dy
 // One 64-token-major LDS tile holds x in phase 1 and dy in phase 2 (both read back as
@@ -221,6 +247,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_x(const T* __restrict__ x, con
         }
     };
 
+    float p1[4];
+    float dd = 0.f;
     // ---- phase 1: yhat ----
     load_rows(xb);
     const float cdv = tid < Q ? cd[tid] : 0.f;
@@ -281,8 +309,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_x(const T* __restrict__ x, con
         }
     }
     // dy_i . yhat_i per row (lane (i, q) holds p = 16 pt + 4 q + r), and dy . x for dD
-    float p1[4];
-    float dd = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         p1[k] = 0.f;
@@ -730,17 +756,62 @@ __global__ __launch_bounds__(kBcThreads) void k_bwd_bc(const T* __restrict__ x, 
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_dt: per (b, h), dl_t = dL/d(dt_t A) = sum_{u >= t} ds_u + <dhT, hT>, then
-// ddt_t = A dl_t and dAp[b, h] = sum_t dt_t dl_t.
+// k_bwd_dt: dl_t = dL/d(dt_t A) = sum_{u >= t} ds_u + <dhT, hT>, ddt_t = A dl_t, and
+// partials sum_t dt_t dl_t of dA.
 // The running sum restarts at every chunk: at the first token of chunk c + 1, dl equals
 // the inner product of the adjoint arriving at the end of chunk c from later tokens with
 // the state entering chunk c + 1, <R_c, H_{c+1}> (H_nc = hT, R_{nc-1} = dhT), so within
 // chunk c dl_t = <R_c, H_{c+1}> + sum_{u = t}^{chunk end} ds_u.  Rounding of the
 // per-token terms then accumulates over at most one chunk instead of the whole sequence.
-// The block forms the boundary products for BLOCK chunks at a time (coalesced reads of
-// rin and hin), then each thread walks one chunk backward.
+// k_scan_rev leaves the boundary products as per-wave partials.  One work-group per
+// (batch, chunk), one thread per head walking the chunk backward, so each step writes
+// the heads of one token side by side.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_sum(float v, float* part) {  // part: >= 4 floats
+template <int BLOCK = 128>
+__global__ __launch_bounds__(BLOCK) void k_bwd_dt(const float* __restrict__ ds, const float* __restrict__ dt,
+                                                  const float* __restrict__ A, const float* __restrict__ kpart,
+                                                  float* __restrict__ ddt, float* __restrict__ dAp, int64_t Tn,
+                                                  int H, int Q, int nc, int nslot, int nvalid) {
+    const int c = (int)(blockIdx.x % nc);
+    const int64_t bi = blockIdx.x / nc;
+    const int64_t t0 = (int64_t)c * Q;
+    const int len = (int)((Tn - t0) < Q ? (Tn - t0) : Q);
+    for (int h = threadIdx.x; h < H; h += BLOCK) {
+        const int64_t bh = bi * H + h;
+        const float* kp = kpart + (bh * nc + c) * (int64_t)nslot;
+        float run = 0.f;
+        for (int i = 0; i < nvalid; ++i) run += kp[i];
+        const float* d = ds + (bh * nc + c) * (int64_t)Q;
+        const float Ah = A[h];
+        float da = 0.f;
+        // the running sum is serial; its operands are requested DEPTH tokens at a time
+        constexpr int DEPTH = 16;
+        for (int i0 = len - 1; i0 >= 0; i0 -= DEPTH) {
+            float dv[DEPTH], tv[DEPTH];
+#pragma unroll
+            for (int k = 0; k < DEPTH; ++k) {
+                const int i = i0 - k >= 0 ? i0 - k : 0;
+                dv[k] = d[i];
+                tv[k] = dt[(bi * Tn + t0 + i) * H + h];
+            }
+#pragma unroll
+            for (int k = 0; k < DEPTH; ++k) {
+                if (i0 - k >= 0) {
+                    run += dv[k];
+                    const int64_t o = (bi * Tn + t0 + i0 - k) * H + h;
+                    ddt[o] = Ah * run;
+                    da += tv[k] * run;
+                }
+            }
+        }
+        dAp[bh * nc + c] = da;
+    }
+}
+
+// dA[h] = sum_{b, c} dAp[b, h, c];  dD[h] = sum_{b, c} dDp[b, h, c].  One work-group per
+// head; each thread sums a fixed strided subset, then a fixed reduction tree, so the
+// result does not depend on scheduling.
+__device__ __forceinline__ float block_sum(float v, float* part) {  // part: >= 16 floats
     v = sum_wave(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
@@ -750,75 +821,25 @@ __device__ __forceinline__ float block_sum(float v, float* part) {  // part: >= 
     return t;
 }
 
-template <typename T, int BLOCK = kThreads>
-__global__ __launch_bounds__(BLOCK) void k_bwd_dt(const float* __restrict__ ds, const float* __restrict__ dt,
-                                                  const float* __restrict__ A, const float* __restrict__ dhT,
-                                                  const float* __restrict__ hTf, const T* __restrict__ hin,
-                                                  const T* __restrict__ rin, float* __restrict__ ddt,
-                                                  float* __restrict__ dAp, int64_t Tn, int H, int PN, int Q,
-                                                  int nc) {
-    typedef typename V8<T>::type v8;
-    __shared__ float part[16];
-    __shared__ float Ks[BLOCK];
-    const int64_t bh = blockIdx.x;
-    const int h = (int)(bh % H);
-    const int64_t bi = bh / H;
-    const int tid = threadIdx.x;
-    const float Ah = A[h];
-    const float* d = ds + bh * (int64_t)nc * Q;  // token t at d[t]
-    const T* rb = rin + bh * (int64_t)nc * PN;
-    const T* hb = hin + bh * (int64_t)nc * PN;
-    float da = 0.f;
-    for (int cg = 0; cg < nc; cg += BLOCK) {
-        const int cn = (nc - cg) < BLOCK ? (nc - cg) : BLOCK;
-        for (int cc = 0; cc < cn; ++cc) {
-            const int c = cg + cc;
-            float k = 0.f;
-            if (c + 1 < nc) {
-                for (int v = tid; v < PN / 8; v += BLOCK) {
-                    const v8 r = ld8(rb + (int64_t)c * PN + 8 * v), hv = ld8(hb + (int64_t)(c + 1) * PN + 8 * v);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) k += to_f(r[e]) * to_f(hv[e]);
-                }
-            } else if (dhT) {  // the last chunk: <dhT, hT>
-                for (int e = tid; e < PN; e += BLOCK) k += dhT[bh * PN + e] * hTf[bh * PN + e];
-            }
-            k = block_sum(k, part);
-            if (tid == 0) Ks[cc] = k;
-        }
-        __syncthreads();
-        if (tid < cn) {
-            const int c = cg + tid;
-            const int64_t t0 = (int64_t)c * Q;
-            const int len = (int)((Tn - t0) < Q ? (Tn - t0) : Q);
-            float run = Ks[tid];
-            for (int i = len - 1; i >= 0; --i) {
-                run += d[t0 + i];
-                const int64_t o = (bi * Tn + t0 + i) * H + h;
-                ddt[o] = Ah * run;
-                da += dt[o] * run;
-            }
-        }
-        __syncthreads();
-    }
-    da = block_sum(da, part);
-    if (tid == 0) dAp[bh] = da;
-}
-
-// dA[h] = sum_b dAp[b, h];  dD[h] = sum_{b, c} dDp[b, h, c]  (fixed order)
 template <int BLOCK = kThreads>
 __global__ __launch_bounds__(BLOCK) void k_bwd_reduce(const float* __restrict__ dAp,
                                                          const float* __restrict__ dDp, float* __restrict__ dA,
                                                          float* __restrict__ dD, int64_t b, int H, int nc) {
-    const int h = blockIdx.x * BLOCK + threadIdx.x;
-    if (h >= H) return;
+    __shared__ float part[16];
+    const int h = blockIdx.x;
+    const int64_t n = b * nc;  // (batch, chunk) terms of this head
     float a = 0.f, d = 0.f;
-    for (int64_t bi = 0; bi < b; ++bi) {
-        a += dAp[bi * H + h];
-        for (int c = 0; c < nc; ++c) d += dDp[(bi * H + h) * nc + c];
+    for (int64_t k = threadIdx.x; k < n; k += BLOCK) {
+        const int64_t bi = k / nc, c = k - bi * nc;
+        a += dAp[(bi * H + h) * nc + c];
+        d += dDp[(bi * H + h) * nc + c];
     }
-    dA[h] = a;
-    if (dD) dD[h] = d;
+    a = block_sum(a, part);
+    d = block_sum(d, part);
+    if (threadIdx.x == 0) {
+        dA[h] = a;
+        if (dD) dD[h] = d;
+    }
 }
 
 }  // namespace ssd

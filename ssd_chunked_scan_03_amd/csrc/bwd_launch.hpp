@@ -36,7 +36,8 @@ struct BwdArgs {
     float* hTf;     // [b,H,P,N]     forward final state (when dhT is given)
     float* ds;      // [b,H,nc,Q]    per-token decay term
     float* dDp;     // [b,H,nc]      D partial sums
-    float* dAp;     // [b,H]         A partial sums
+    float* dAp;     // [b,H,nc]      A partial sums
+    float* kpart;   // [b,H,nc,4 * ceil(P N / 1024)]  per-wave partials of <R_c, H_{c+1}>
     hipStream_t stream;
 };
 
@@ -92,8 +93,8 @@ int run_bwd(const BwdArgs& a) {
                                                 nullptr, H, (int)(a.P * a.N), (int)a.N, Q, nc, per_head, nc, BHPN);
     // the adjoint: chunk inputs (into the chunk-state buffer, now free), reverse scan
     k_state<T, P, N, false, true><<<g3, kThreads, 0, s>>>(dy, Cm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
-    k_scan_rev<T><<<g4, kThreads, 0, s>>>(a.states, rin, a.dh0, a.dhT, a.A, a.cdt, H, (int)(a.P * a.N), Q, nc,
-                                          per_head);
+    k_scan_rev<T><<<g4, kThreads, 0, s>>>(a.states, rin, a.dh0, a.dhT, a.A, a.cdt, hin, a.hTf, a.kpart, H,
+                                          (int)(a.P * a.N), Q, nc, per_head);
     // gradients
     (void)hipFuncSetAttribute((const void*)k_bwd_x<T, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sx);
     k_bwd_x<T, P, N><<<g3, kThreads, sx, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
@@ -102,10 +103,10 @@ int run_bwd(const BwdArgs& a) {
     const dim3 g7((unsigned)(a.b * nc * G * (Q / 64) * (N / NB)));
     k_bwd_bc<T, P, N, NB><<<g7, kBcThreads, sbc, s>>>(x, dy, bt, ct, hin, rin, a.A, a.cdt, static_cast<T*>(a.dB),
                                                     static_cast<T*>(a.dC), a.T, H, G, Q, nc);
-    k_bwd_dt<T, kThreads><<<(unsigned)(a.b * H), kThreads, 0, s>>>(a.ds, a.dt, a.A, a.dhT, a.hTf, hin, rin, a.ddt,
-                                                                    a.dAp, a.T, H, (int)(a.P * a.N), Q, nc);
-    k_bwd_reduce<kThreads><<<(unsigned)((H + kThreads - 1) / kThreads), kThreads, 0, s>>>(a.dAp, a.dDp, a.dA, a.dD, a.b, H,
-                                                                                 nc);
+    const int nvalid = (int)(a.P * a.N / 4 / 64);  // waves that hold elements
+    k_bwd_dt<128><<<(unsigned)(a.b * nc), 128, 0, s>>>(a.ds, a.dt, a.A, a.kpart, a.ddt, a.dAp, a.T, H, Q, nc,
+                                                       per_head * 4, nvalid);
+    k_bwd_reduce<kThreads><<<(unsigned)H, kThreads, 0, s>>>(a.dAp, a.dDp, a.dA, a.dD, a.b, H, nc);
     return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 

@@ -314,7 +314,8 @@ def test_bwd_workspace_arithmetic():
     a = lambda n: (n + 255) // 256 * 256
     want = (a(b * H * nc * Q * 4) + 2 * a(b * nc * G * Q * Q * 2) + 2 * a(b * nc * G * N * Q * 2)
             + a(b * H * nc * P * N * 4) + 2 * a(b * H * nc * P * N * 2) + a(b * H * P * N * 4)
-            + a(b * H * nc * Q * 4) + a(b * H * nc * 4) + a(b * H * 4))
+            + a(b * H * nc * Q * 4) + a(b * H * nc * 4) + a(b * H * nc * 4)
+            + a(b * H * nc * 4 * ((P * N // 4 + 255) // 256) * 4))
     assert ssd.bwd_workspace_bytes(p) == want
     assert ssd.bwd_workspace_bytes(prob(T=0)) == 0
     assert ssd.bwd_workspace_bytes(prob(b=0)) == 0
