@@ -453,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_x(const T* __restrict__ x, con
 // head (the next head's prefetched into registers meanwhile) and read with the
 // transpose read, p running down the rows.
 // ---------------------------------------------------------------------------
-constexpr int kBcThreads = 512;  // k_bwd_bc work-groups: 8 waves
+constexpr int kBcThreads = 512;  // k_bwd_bc work-groups: 8 waves (16 measured slower: spills at 128 VGPRs)
 
 template <typename T, int P, int NB>
 struct BcSmem {
@@ -500,8 +500,10 @@ __global__ __launch_bounds__(kBcThreads) void k_bwd_bc(const T* __restrict__ x, 
     constexpr int PR = SM::PR, LDH = SM::LDH, LDY = SM::LDY, LDW = SM::LDW, NBT = NB / 16, NR = N / NB;
     constexpr int NW = kBcThreads / 64;           // 8 waves
     constexpr int NTW = (58 + NW - 1) / NW;       // W tiles per wave at Q = 256 (58 tiles)
-    // state terms and products: wave w takes row tile w % 4 of the slab and half the n tiles
-    constexpr int NBH = NBT >= 2 ? NBT / 2 : 1;
+    // state terms and products: wave w takes row tile w % 4 of the slab and n tiles
+    // [nb0, nb0 + NBH) of the range, NBH = NBT / NSP (one tile when NBT < NSP)
+    constexpr int NSP = NW / 4;                   // n-tile splits
+    constexpr int NBH = NBT >= NSP ? NBT / NSP : 1;
     constexpr float LOG2E = 1.4426950408889634f;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     T* Hs = reinterpret_cast<T*>(smem_raw);
@@ -636,9 +638,9 @@ __global__ __launch_bounds__(kBcThreads) void k_bwd_bc(const T* __restrict__ x, 
     for (int m = 0; m < NTW; ++m) accW[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < NBH; ++nt) accC[nt] = accB[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int rt = w & 3, nh = w >> 2;             // row tile, n-tile half
-    const bool sact = NBT >= 2 || nh == 0;         // (one n tile: the second half idles)
-    const int nb0 = NBT >= 2 ? nh * NBH : 0;       // first n tile of this wave
+    const int rt = w & 3, nh = w >> 2;             // row tile, n-tile split
+    const bool sact = nh < NBT / NBH;              // (fewer n tiles than splits: the rest idle)
+    const int nb0 = nh * NBH;                      // first n tile of this wave
     const int iw = s64 + rt * 16 + l16;            // this wave's row (dC) and column (dB) token
 
     prefetch(hbeg);
