@@ -77,7 +77,7 @@ def main():
                          "(calibrates the byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: this benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is a design note, not an implementation", file=sys.stderr)
         sys.exit(2)
 
