@@ -138,11 +138,14 @@ __global__ __launch_bounds__(BLOCK) void k_rows(const int* __restrict__ cu, int 
 // scans one head at a time: Q/64 consecutive tokens per lane, a lane-serial sum and a
 // wave prefix sum.
 // ---------------------------------------------------------------------------
+constexpr int kCumsumHeads = 16;  // heads per cumsum work-group
+template <int Q>
+constexpr size_t cumsum_smem() { return (size_t)kCumsumHeads * (Q + 1) * sizeof(float); }
+
 template <int Q>
 __device__ __forceinline__ void cumsum_body(const float* __restrict__ dt, float* __restrict__ cdt, Rows rows,
-                                            int k, int hz) {
-    constexpr int HS = 16, QPL = Q / 64;
-    __shared__ float s[HS][Q + 1];
+                                            int k, int hz, float (*s)[Q + 1]) {
+    constexpr int HS = kCumsumHeads, QPL = Q / 64;
     if (k >= rows.total_chunks()) return;
     const int r = rows.row_of(k);
     const int c = k - rows.kbase(r);
@@ -200,7 +203,8 @@ __device__ __forceinline__ void cumsum_body(const float* __restrict__ dt, float*
 template <int Q>
 __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ dt,
                                                      float* __restrict__ cdt, Rows rows) {
-    cumsum_body<Q>(dt, cdt, rows, blockIdx.x, blockIdx.z);
+    __shared__ float s[kCumsumHeads][Q + 1];
+    cumsum_body<Q>(dt, cdt, rows, blockIdx.x, blockIdx.z, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -214,9 +218,15 @@ __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ d
 // contiguous), the layout the backward pass reads its input-gradient operand from: the
 // operands swap places in the matrix-core step, so a lane then owns 4 consecutive i.
 // ---------------------------------------------------------------------------
+// dstate from which the 64 C rows of a block are staged in LDS once (shared by its 4 waves)
+// rather than loaded by every wave
+constexpr int kCbStageN = 256;
+template <typename T, int N>
+constexpr size_t cb_smem() { return (sizeof(T) == 2 && N >= kCbStageN) ? (size_t)64 * (N + 8) * sizeof(T) : 0; }
+
 template <typename T, int N, bool TR = false>
 __device__ __forceinline__ void cb_body(const T* __restrict__ Bm, const T* __restrict__ Cm, T* __restrict__ cb,
-                                        Rows rows, int G, int Q, int kg, int pidx, int g) {
+                                        Rows rows, int G, int Q, int kg, int pidx, int g, T* __restrict__ cs) {
     typedef typename V8<T>::type v8;
     typedef typename V4<T>::type v4;
     if (kg >= rows.total_chunks()) return;
@@ -245,11 +255,22 @@ __device__ __forceinline__ void cb_body(const T* __restrict__ Bm, const T* __res
         const int s0 = __builtin_amdgcn_readfirstlane((int)(tok0 * rowb + g * N * 2));
         const int vb = jr * rowb + 16 * q;                     // B row jr, k-group q
         const int vc = (I * 64 + l16) * rowb + 16 * q;          // C row I*64 + l16 (+ 16 ct rows)
+        constexpr bool STAGE = N >= kCbStageN;
+        constexpr int LDC = N + 8;
+        if constexpr (STAGE) {
+            for (int v = threadIdx.x; v < 64 * N / 8; v += kThreads) {
+                const int r = v / (N / 8), n0 = (v - r * (N / 8)) * 8;
+                st8(cs + r * LDC + n0, bload8(rc, r * (int)rowb + n0 * 2, s0 + I * 64 * (int)rowb));
+            }
+            __syncthreads();
+        }
         bf16x8 fb[KS], fc[KS][4];
         auto load = [&](int ks) {
             fb[ks] = bload8(rb, vb, s0 + ks * 64);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) fc[ks][ct] = bload8(rc, vc, s0 + ks * 64 + ct * 16 * (int)rowb);
+            for (int ct = 0; ct < 4; ++ct)
+                fc[ks][ct] = STAGE ? ld8(reinterpret_cast<const bf16*>(cs) + (16 * ct + l16) * LDC + ks * 32 + 8 * q)
+                                   : bload8(rc, vc, s0 + ks * 64 + ct * 16 * (int)rowb);
         };
         f32x4 acc[4];
 #pragma unroll
@@ -308,7 +329,8 @@ __device__ __forceinline__ void cb_body(const T* __restrict__ Bm, const T* __res
 template <typename T, int N, bool TR = false>
 __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const T* __restrict__ Cm,
                                                  T* __restrict__ cb, Rows rows, int G, int Q) {
-    cb_body<T, N, TR>(Bm, Cm, cb, rows, G, Q, blockIdx.x, blockIdx.y, blockIdx.z);
+    __shared__ __attribute__((aligned(16))) unsigned char cs[cb_smem<T, N>() > 0 ? cb_smem<T, N>() : 16];
+    cb_body<T, N, TR>(Bm, Cm, cb, rows, G, Q, blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<T*>(cs));
 }
 
 // ---------------------------------------------------------------------------
@@ -318,11 +340,13 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
 // work-group, transposed through LDS.
 // ---------------------------------------------------------------------------
 template <typename T, int N>
+constexpr size_t bt_smem() { return (size_t)N * (64 + 8) * sizeof(T); }
+
+template <typename T, int N>
 __device__ __forceinline__ void bt_body(const T* __restrict__ Bm, T* __restrict__ Bt, Rows rows, int G, int Q,
-                                        int kg, int j0, int g) {
+                                        int kg, int j0, int g, T* __restrict__ s) {
     typedef typename V8<T>::type v8;
     constexpr int JB = 64, LD = JB + 8;
-    __shared__ __attribute__((aligned(16))) T s[N * LD];
     if (kg >= rows.total_chunks()) return;
     const int rr = rows.row_of(kg);
     const int c = kg - rows.kbase(rr);
@@ -347,9 +371,10 @@ __device__ __forceinline__ void bt_body(const T* __restrict__ Bm, T* __restrict_
 template <typename T, int N>
 __global__ __launch_bounds__(kThreads) void k_bt(const T* __restrict__ Bm, T* __restrict__ Bt, Rows rows,
                                                  int G, int Q) {
+    __shared__ __attribute__((aligned(16))) T s[N * (64 + 8)];
     const int slabs = Q / 64;
     const int kg = blockIdx.x / slabs;
-    bt_body<T, N>(Bm, Bt, rows, G, Q, kg, (blockIdx.x - kg * slabs) * 64, blockIdx.y);
+    bt_body<T, N>(Bm, Bt, rows, G, Q, kg, (blockIdx.x - kg * slabs) * 64, blockIdx.y, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -365,20 +390,24 @@ __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ dt,
                                                    const T* __restrict__ Bm, const T* __restrict__ Cm,
                                                    T* __restrict__ cb, T* __restrict__ Bt, Rows rows, int G) {
     constexpr int nb = Q / 64, npair = nb * (nb + 1) / 2, nslab = Q / 64;
-    const int nh = (rows.H + 15) / 16;
+    // one LDS buffer for whichever task the work-group runs
+    constexpr size_t s1 = cumsum_smem<Q>(), s2 = cb_smem<T, N>(), s3 = BT ? bt_smem<T, N>() : 0;
+    constexpr size_t SB = s1 > s2 ? (s1 > s3 ? s1 : s3) : (s2 > s3 ? s2 : s3);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SB];
+    const int nh = (rows.H + kCumsumHeads - 1) / kCumsumHeads;
     const int k = blockIdx.x;
     int y = blockIdx.y;
     if (y < nh) {
-        cumsum_body<Q>(dt, cdt, rows, k, y);
+        cumsum_body<Q>(dt, cdt, rows, k, y, reinterpret_cast<float(*)[Q + 1]>(smem));
         return;
     }
     y -= nh;
     if (y < npair * G) {
-        cb_body<T, N, false>(Bm, Cm, cb, rows, G, Q, k, y % npair, y / npair);
+        cb_body<T, N, false>(Bm, Cm, cb, rows, G, Q, k, y % npair, y / npair, reinterpret_cast<T*>(smem));
         return;
     }
     y -= npair * G;
-    if (BT) bt_body<T, N>(Bm, Bt, rows, G, Q, k, (y % nslab) * 64, y / nslab);
+    if (BT) bt_body<T, N>(Bm, Bt, rows, G, Q, k, (y % nslab) * 64, y / nslab, reinterpret_cast<T*>(smem));
 }
 
 // ---------------------------------------------------------------------------
