@@ -34,7 +34,8 @@
 // and dx - D dy; k_bwd_dt takes the reverse running sum.
 //
 // Kernels, in launch order after the forward's k_cumsum, k_cb (both orientations), k_bt
-// (B and C), k_state and k_scan (entering states H_c, final state hT):
+// (B and C), and the entering states H_c and final state hT (k_state + k_scan, or with
+// many (b, h) chains k_states walking each chain's chunks with the state in registers):
 //   k_state<ADJ>  adjoint chunk inputs S'_c                        -> states (reused)
 //   k_scan_rev    R_c per chunk, dh0, partials of <R_c, H_{c+1}>     -> rin, dh0, kpart
 //   k_bwd_x       dx, per-token decay term, D partial sums, per (b, h, c)
@@ -130,6 +131,156 @@ __global__ __launch_bounds__(kThreads) void k_scan_rev(const float* __restrict__
         }
     }
     if (dh0) st4(dh0 + bh * PN + e0, st);
+}
+
+// ---------------------------------------------------------------------------
+// k_states: the forward state recurrence of one (b, h), walked chunk by chunk with the
+// state held in registers: what k_state + k_scan compute, without the float32 chunk
+// states going to HBM and back.
+//   H = h0;  for c = 0 .. nc-1:  Hout[c] = H;  H = e^{A cdt_last} H + sum_j e^{A (cdt_last - cdt_j)} x_j B_j^T
+//   fin = H (the final state)
+// One work-group per (b, h), so it pays only with many (b, h) chains.  Within a chunk,
+// 64-token slabs of x (weight applied while staging) and of B go through LDS as in
+// k_state; the next slab's loads, across chunk boundaries too, are in flight during the
+// current slab's matrix-core work.  (Walking the adjoint this way, with the boundary
+// products, spilled and measured slower than k_state<ADJ> + k_scan_rev.)
+// ---------------------------------------------------------------------------
+template <typename T, int P, int N>
+__global__ __launch_bounds__(kThreads, P * N <= 8192 ? 3 : 1) void k_states(const T* __restrict__ xin,
+                                                                            const T* __restrict__ Bm,
+                                                                            const float* __restrict__ A,
+                                                                            const float* __restrict__ cdt,
+                                                                            const float* __restrict__ init,
+                                                                            T* __restrict__ Hout, float* __restrict__ fin,
+                                                                            int64_t Tn, int H, int G, int Q, int nc) {
+    typedef typename V8<T>::type v8;
+    typedef typename V4<T>::type v4;
+    typedef StateTiling<P, N> TL;
+    constexpr int JB = 64, LDX = P + 8, LDB = N + 8, PN = P * N;
+    constexpr int XV = JB * P / 8, BV = JB * N / 8;
+    constexpr int XR = (XV + kThreads - 1) / kThreads, BR = (BV + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) T Xs[JB * LDX];
+    __shared__ __attribute__((aligned(16))) T Bs[JB * LDB];
+    __shared__ float cds[256];
+    const int64_t bh = blockIdx.x;
+    const int h = (int)(bh % H);
+    const int64_t bi = bh / H;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, q = lane >> 4;
+    const float ah2 = A[h] * 1.4426950408889634f;
+    const bool wact = TL::active(w);
+    const int wn0 = TL::n0(w), wp0 = TL::p0(w);
+    auto len_of = [&](int c) { return (int)((Tn - (int64_t)c * Q) < Q ? (Tn - (int64_t)c * Q) : Q); };
+
+    // the state, in k_state's tile layout: lane holds S^T[n][p] for its tiles
+    f32x4 acc[TL::WN][TL::WP];
+#pragma unroll
+    for (int a = 0; a < TL::WN; ++a)
+#pragma unroll
+        for (int b = 0; b < TL::WP; ++b) {
+            const int p = (wp0 + b) * 16 + l16, n = (wn0 + a) * 16 + 4 * q;
+            acc[a][b] = (wact && init) ? ld4(init + bh * PN + p * N + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+    v8 xv[XR], bv[BR];
+    float cdv = 0.f;
+    auto prefetch = [&](int c, int j0) {
+        const int64_t tok0 = (int64_t)c * Q;
+        const int len = len_of(c);
+        const T* xb = xin + ((bi * Tn + tok0) * H + h) * P;
+        const T* bb = Bm + ((bi * Tn + tok0) * G + g) * N;
+#pragma unroll
+        for (int r = 0; r < XR; ++r) {
+            const int v = tid + r * kThreads;
+            const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
+            const int jr = j0 + jj < len ? j0 + jj : len - 1;
+            xv[r] = sel8(v < XV && j0 + jj < len, ld8(xb + (int64_t)jr * H * P + p0));
+        }
+#pragma unroll
+        for (int r = 0; r < BR; ++r) {
+            const int v = tid + r * kThreads;
+            const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
+            const int jr = j0 + jj < len ? j0 + jj : len - 1;
+            bv[r] = sel8(v < BV && j0 + jj < len, ld8(bb + (int64_t)jr * G * N + n0));
+        }
+        if (j0 == 0 && tid < Q) cdv = cdt[(bh * nc + c) * (int64_t)Q + tid];
+    };
+
+    if (nc > 0) prefetch(0, 0);
+    for (int c = 0; c < nc; ++c) {
+        const int len = len_of(c);
+        __syncthreads();  // the previous chunk is done with cds, Xs and Bs
+        if (tid < Q) cds[tid] = cdv;
+        // the state entering chunk c
+        if (wact) {
+            T* ho = Hout + (bh * nc + c) * (int64_t)PN;
+#pragma unroll
+            for (int a = 0; a < TL::WN; ++a)
+#pragma unroll
+                for (int b = 0; b < TL::WP; ++b) {
+                    v4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = from_f<T>(acc[a][b][r]);
+                    st4(ho + ((wp0 + b) * 16 + l16) * N + (wn0 + a) * 16 + 4 * q, o);
+                }
+        }
+        __syncthreads();  // cds in place
+        const float last = cds[Q - 1];
+        const float dch = exp2f_fast(ah2 * last);
+#pragma unroll
+        for (int a = 0; a < TL::WN; ++a)
+#pragma unroll
+            for (int b = 0; b < TL::WP; ++b) acc[a][b] *= dch;
+        for (int j0 = 0; j0 < len; j0 += JB) {
+            // slab j0 -> LDS, the weight of each token applied to its input row
+#pragma unroll
+            for (int r = 0; r < XR; ++r) {
+                const int v = tid + r * kThreads;
+                if (v < XV) {
+                    const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
+                    v8 o = xv[r];
+                    const float wj = exp2f_fast(ah2 * (last - cds[j0 + jj]));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] = from_f<T>(to_f(o[e]) * wj);
+                    st8(&Xs[jj * LDX + p0], o);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < BR; ++r) {
+                const int v = tid + r * kThreads;
+                if (v < BV) {
+                    const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
+                    st8(&Bs[jj * LDB + n0], bv[r]);
+                }
+            }
+            __syncthreads();
+            // the next slab: this chunk's, else the next chunk's first
+            if (j0 + JB < len) prefetch(c, j0 + JB);
+            else if (c + 1 < nc) prefetch(c + 1, 0);
+            if (wact) {
+#pragma unroll
+                for (int kk = 0; kk < JB; kk += 32) {
+                    v8 bf[TL::WP];
+#pragma unroll
+                    for (int b = 0; b < TL::WP; ++b) bf[b] = frag_rows(Xs, LDX, kk, (wp0 + b) * 16, lane);
+#pragma unroll
+                    for (int a = 0; a < TL::WN; ++a) {
+                        const v8 af = frag_rows(Bs, LDB, kk, (wn0 + a) * 16, lane);
+#pragma unroll
+                        for (int b = 0; b < TL::WP; ++b) acc[a][b] = mma(acc[a][b], af, bf[b]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (fin && wact) {
+#pragma unroll
+        for (int a = 0; a < TL::WN; ++a)
+#pragma unroll
+            for (int b = 0; b < TL::WP; ++b)
+                st4(fin + bh * PN + ((wp0 + b) * 16 + l16) * N + (wn0 + a) * 16 + 4 * q, acc[a][b]);
+    }
 }
 
 // ---------------------------------------------------------------------------

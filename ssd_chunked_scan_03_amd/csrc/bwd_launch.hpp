@@ -85,16 +85,26 @@ int run_bwd(const BwdArgs& a) {
     k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, bt, rows, G, Q);
     k_bt<T, N><<<g6, kThreads, 0, s>>>(Cm, ct, rows, G, Q);
     const dim3 g3((unsigned)(a.b * H * nc));
-    k_state<T, P, N, false, false><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
     const int per_head = (int)((a.P * a.N / 4 + kThreads - 1) / kThreads);
-    const int64_t BHPN = a.b * H * a.P * a.N;
+    // the forward states: with many (b, h) chains, each chain's chunks walked with the state
+    // in registers; else chunk states, then the scan
+    if (a.b * H >= 512) {
+        k_states<T, P, N><<<(unsigned)(a.b * H), kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.h0, hin,
+                                                                   a.dhT ? a.hTf : nullptr, a.T, H, G, Q, nc);
+    } else {
+        k_state<T, P, N, false, false><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
+        const int64_t BHPN = a.b * H * a.P * a.N;
+        const dim3 g4((unsigned)(a.b * H * per_head));
+        k_scan<T, false, 0><<<g4, kThreads, 0, s>>>(a.states, hin, a.dhT ? a.hTf : nullptr, a.h0, a.A, a.cdt,
+                                                    nullptr, nullptr, H, (int)(a.P * a.N), (int)a.N, Q, nc,
+                                                    per_head, nc, BHPN);
+    }
+    // the adjoint: chunk inputs (into the chunk-state buffer), reverse scan
     const dim3 g4((unsigned)(a.b * H * per_head));
-    k_scan<T, false, 0><<<g4, kThreads, 0, s>>>(a.states, hin, a.dhT ? a.hTf : nullptr, a.h0, a.A, a.cdt, nullptr,
-                                                nullptr, H, (int)(a.P * a.N), (int)a.N, Q, nc, per_head, nc, BHPN);
-    // the adjoint: chunk inputs (into the chunk-state buffer, now free), reverse scan
     k_state<T, P, N, false, true><<<g3, kThreads, 0, s>>>(dy, Cm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
     k_scan_rev<T><<<g4, kThreads, 0, s>>>(a.states, rin, a.dh0, a.dhT, a.A, a.cdt, hin, a.hTf, a.kpart, H,
                                           (int)(a.P * a.N), Q, nc, per_head);
+    const int nslot = per_head * 4, nvalid = (int)(a.P * a.N / 4 / 64);  // partials per chunk; waves with elements
     // gradients
     (void)hipFuncSetAttribute((const void*)k_bwd_x<T, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sx);
     k_bwd_x<T, P, N><<<g3, kThreads, sx, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
@@ -103,9 +113,8 @@ int run_bwd(const BwdArgs& a) {
     const dim3 g7((unsigned)(a.b * nc * G * (Q / 64) * (N / NB)));
     k_bwd_bc<T, P, N, NB><<<g7, kBcThreads, sbc, s>>>(x, dy, bt, ct, hin, rin, a.A, a.cdt, static_cast<T*>(a.dB),
                                                     static_cast<T*>(a.dC), a.T, H, G, Q, nc);
-    const int nvalid = (int)(a.P * a.N / 4 / 64);  // waves that hold elements
     k_bwd_dt<128><<<(unsigned)(a.b * nc), 128, 0, s>>>(a.ds, a.dt, a.A, a.kpart, a.ddt, a.dAp, a.T, H, Q, nc,
-                                                       per_head * 4, nvalid);
+                                                       nslot, nvalid);
     k_bwd_reduce<kThreads><<<(unsigned)H, kThreads, 0, s>>>(a.dAp, a.dDp, a.dA, a.dD, a.b, H, nc);
     return hipGetLastError() == hipSuccess ? 0 : 7;
 }
