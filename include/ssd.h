@@ -154,7 +154,13 @@ int ssd_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const flo
                  void* y, float* hT, void* ws, size_t ws_bytes, void* stream);
 
 /* Diagonal-decay SSD forward: A is [nheads, dstate].  Same conventions;
- * `ws` must hold ssd_workspace_bytes(p, 1) bytes. */
+ * `ws` must hold ssd_workspace_bytes(p, 1) bytes.
+ * The output kernel keeps a chunk's x rows and its rescaled C and B rows in LDS:
+ * (chunk * (headdim + 8) + 2 * chunk * (dstate + 8)) elements plus (2 * chunk + dstate)
+ * floats must fit the 160 KiB of one CU (for bfloat16 at chunk 256 that allows dstate up
+ * to 64 at headdim 64, for example); larger problems return SSD_ERR_UNSUPPORTED before
+ * any launch.  (The scalar decay's tile, chunk * (headdim + 8) elements plus 2 * chunk
+ * floats, always fits.) */
 int ssd_diag_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const float* A,
                       const void* B, const void* C, const float* D, const float* h0,
                       void* y, float* hT, void* ws, size_t ws_bytes, void* stream);

@@ -97,7 +97,7 @@ CASES = [  # b, T, H, P, N, G, Q, dtype
     (3, 700, 4, 64, 128, 1, 256, "bf16"),
     (1, 1, 2, 64, 128, 1, 256, "bf16"),
     (2, 64, 4, 128, 32, 4, 64, "f32"),
-    # 512 (batch, head) chains: the forward and adjoint states walk each chain's chunks
+    # 512 (batch, head) chains: the forward states walk each chain's chunks (k_states)
     (8, 300, 64, 32, 64, 4, 128, "bf16"),
     (8, 200, 64, 16, 32, 2, 64, "f32"),
 ]
