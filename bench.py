@@ -196,23 +196,23 @@ def main():
               "hbm_frac": round(sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
               "tokens_per_s": round(b / (sms * 1e-3), 1)}
 
-    # the backward pass (scalar decay) at the same workload: gradients of every input for
+    # the backward pass (either decay) at the same workload: gradients of every input for
     # seeded output gradients dy, dhT, timed as a whole with HIP events on the launch stream
     backward = None
-    if not w.diag and not args.no_bwd:
+    if not args.no_bwd:
         print("[bench] timing the backward pass", file=sys.stderr, flush=True)
         gr = make_grads(b, T, H, P, N, w.seed, dtype=w.dtype)
         dy = torch.from_numpy(gr["dy"]).to(dev).to(td).contiguous()
         dhT = torch.from_numpy(gr["dhT"]).to(dev)
         bprob = ssd.make_problem(b, T, H, P, N, G, Q, dcode)
-        bws = torch.empty(max(ssd.bwd_workspace_bytes(bprob), 1), dtype=torch.uint8, device=dev)
+        bws = torch.empty(max(ssd.bwd_workspace_bytes(bprob, w.diag), 1), dtype=torch.uint8, device=dev)
         g = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dA=torch.empty_like(A), dB=torch.empty_like(B),
                  dC=torch.empty_like(C), dD=torch.empty_like(D),
                  dh0=torch.empty((b, H, P, N), dtype=torch.float32, device=dev))
 
         def bstep():
             ssd.scan_bwd_into(bprob, x, dt, A, B, C, D, h0, dy, dhT, g["dx"], g["ddt"], g["dA"], g["dB"], g["dC"],
-                              g["dD"], g["dh0"], bws, stream.cuda_stream)
+                              g["dD"], g["dh0"], bws, stream.cuda_stream, diag=w.diag)
 
         for _ in range(3):
             bstep()

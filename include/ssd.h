@@ -263,6 +263,31 @@ int ssd_scan_bwd(const ssd_problem* p, const void* x, const float* dt, const flo
                  const float* dhT, void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
                  float* dh0, void* ws, size_t ws_bytes, void* stream);
 
+/* Backward pass of ssd_diag_scan_fwd (a_{t,n} = exp(dt_t A_{h,n}), A [nheads, dstate]):
+ * the same gradients as ssd_scan_bwd with the decay taken per state dimension
+ * ("Structured State Space Duality" concept page, the diagonal generalisation of the
+ * scalar decay):
+ *
+ *     dx_t  = sum_n g_t[:, n] B_{t,n} + D_h dy_t      dB_{t,n} = sum over heads of x_t . g_t[:, n]
+ *     dC_{t,n} = sum over heads of dy_t . h_t[:, n]   dh0 = (a_{0,n} g_0[:, n])_n
+ *     ddt_t = sum_n A_{h,n} dl_{t,n},   dA_{h,n} = sum_{b,t} dt_t dl_{t,n},
+ *     dl_{t,n} = sum_{u >= t} [C_{u,n} dy_u . h_u[:, n] - B_{u,n} x_u . g_u[:, n]] + <dhT, hT>_n
+ *
+ * with h_t the state after token t and g_t = dy_t C_t^T + a_{t+1} g_{t+1} its gradient.
+ * Across chunks it runs the forward's chunk states and scan and the same scan backward for
+ * the adjoint; within a chunk every (batch, head) walks its tokens forward and backward
+ * from the chunk's boundary states, all in float32.  Arguments, layouts, outputs and
+ * alignment as for ssd_scan_bwd, except A and dA, which are [nheads, dstate] float32.
+ * `ws` must hold ssd_diag_bwd_workspace_bytes(p) bytes (0 for an empty problem, where
+ * dA = dD = 0 and dh0 = dhT).  flags must be 0.  Every chunk, headdim, dstate and dtype
+ * of ssd_scan_fwd's support set; errors as for ssd_scan_bwd, reported before any HIP
+ * call. */
+size_t ssd_diag_bwd_workspace_bytes(const ssd_problem* p);
+int ssd_diag_scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* A,
+                      const void* B, const void* C, const float* D, const float* h0, const void* dy,
+                      const float* dhT, void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
+                      float* dh0, void* ws, size_t ws_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* ssd_status_string(int status);
 

@@ -32,6 +32,7 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPP
 EXPORTS = ("ssd_workspace_bytes", "ssd_get_workspace_layout", "ssd_scan_fwd", "ssd_diag_scan_fwd",
            "ssd_varlen_workspace_bytes", "ssd_scan_fwd_varlen",
            "ssd_step", "ssd_diag_step", "ssd_bwd_workspace_bytes", "ssd_scan_bwd",
+           "ssd_diag_bwd_workspace_bytes", "ssd_diag_scan_bwd",
            "ssd_status_string", "ssd_version")
 
 
@@ -80,10 +81,12 @@ def _load():
     for f in (lib.ssd_step, lib.ssd_diag_step):
         f.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, vp]
         f.restype = ci
-    lib.ssd_bwd_workspace_bytes.argtypes = [P]
-    lib.ssd_bwd_workspace_bytes.restype = sz
-    lib.ssd_scan_bwd.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, fp, fp, vp, vp, fp, fp, vp, sz, vp]
-    lib.ssd_scan_bwd.restype = ci
+    for f in (lib.ssd_bwd_workspace_bytes, lib.ssd_diag_bwd_workspace_bytes):
+        f.argtypes = [P]
+        f.restype = sz
+    for f in (lib.ssd_scan_bwd, lib.ssd_diag_scan_bwd):
+        f.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, fp, fp, vp, vp, fp, fp, vp, sz, vp]
+        f.restype = ci
     lib.ssd_status_string.argtypes = [ci]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_version.argtypes = []
@@ -298,29 +301,28 @@ def step(x, dt, A, B, C, h, D=None, diag=None):
     return y
 
 
-def bwd_workspace_bytes(prob: Problem) -> int:
-    return int(_load().ssd_bwd_workspace_bytes(ctypes.byref(prob)))
+def bwd_workspace_bytes(prob: Problem, diag: bool = False) -> int:
+    f = _load().ssd_diag_bwd_workspace_bytes if diag else _load().ssd_bwd_workspace_bytes
+    return int(f(ctypes.byref(prob)))
 
 
 def scan_bwd_into(prob: Problem, x, dt, A, B, C, D, h0, dy, dhT, dx, ddt, dA, dB, dC, dD, dh0, ws,
-                  stream=None) -> None:
-    """Enqueue one backward pass into caller-provided gradients and workspace (no allocation)."""
+                  stream=None, diag: bool = False) -> None:
+    """Enqueue one backward pass (diag: of the diagonal-decay forward, A and dA [H, N]) into
+    caller-provided gradients and workspace (no allocation)."""
     import torch
     if stream is None:
         stream = torch.cuda.current_stream(dA.device).cuda_stream
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    st = _load().ssd_scan_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
-                              _ptr(dy), _ptr(dhT), _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD),
-                              _ptr(dh0), _ptr(ws), nbytes, ctypes.c_void_p(int(stream)))
+    f, name = (_load().ssd_diag_scan_bwd, "ssd_diag_scan_bwd") if diag else (_load().ssd_scan_bwd, "ssd_scan_bwd")
+    st = f(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dy), _ptr(dhT),
+           _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD), _ptr(dh0), _ptr(ws), nbytes,
+           ctypes.c_void_p(int(stream)))
     if st:
-        raise SSDError(st, "ssd_scan_bwd")
+        raise SSDError(st, name)
 
 
-def scan_bwd(x, dt, A, B, C, dy, D=None, h0=None, dhT=None, chunk=256, workspace=None):
-    """Backward pass of the scalar-decay forward: gradients of a loss with respect to every
-    input, given dy (like x) and dhT ([b, H, P, N] float32, None = 0).  Returns a dict with
-    dx (x's dtype), ddt (float32), dA (float32 [H]), dB and dC (B's dtype), dD (float32 [H])
-    and dh0 (float32 [b, H, P, N])."""
+def _backward(diag, x, dt, A, B, C, dy, D, h0, dhT, chunk, workspace):
     import torch
     for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D), ("h0", h0), ("dy", dy),
                     ("dhT", dhT)):
@@ -333,17 +335,31 @@ def scan_bwd(x, dt, A, B, C, dy, D=None, h0=None, dhT=None, chunk=256, workspace
             raise TypeError(f"{name} must be float32")
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    if (B.shape != (b, T, G, N) or C.shape != B.shape or dt.shape != (b, T, H) or A.shape != (H,)
-            or dy.shape != x.shape):
-        raise ValueError("shape mismatch among x, dt, A [H], B, C, dy")
+    if (B.shape != (b, T, G, N) or C.shape != B.shape or dt.shape != (b, T, H)
+            or A.shape != ((H, N) if diag else (H,)) or dy.shape != x.shape):
+        raise ValueError("shape mismatch among x, dt, A ([H] or [H, N] for diag), B, C, dy")
     prob = make_problem(b, T, H, P, N, G, chunk, _dtype_code(x))
     dev = x.device
     out = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dA=torch.empty_like(A), dB=torch.empty_like(B),
                dC=torch.empty_like(C), dD=torch.empty((H,), dtype=torch.float32, device=dev),
                dh0=torch.empty((b, H, P, N), dtype=torch.float32, device=dev))
-    need = bwd_workspace_bytes(prob)
+    need = bwd_workspace_bytes(prob, diag)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     scan_bwd_into(prob, x, dt, A, B, C, D, h0, dy, dhT, out["dx"], out["ddt"], out["dA"], out["dB"], out["dC"],
-                  out["dD"], out["dh0"], workspace)
+                  out["dD"], out["dh0"], workspace, diag=diag)
     return out
+
+
+def scan_bwd(x, dt, A, B, C, dy, D=None, h0=None, dhT=None, chunk=256, workspace=None):
+    """Backward pass of the scalar-decay forward: gradients of a loss with respect to every
+    input, given dy (like x) and dhT ([b, H, P, N] float32, None = 0).  Returns a dict with
+    dx (x's dtype), ddt (float32), dA (float32 [H]), dB and dC (B's dtype), dD (float32 [H])
+    and dh0 (float32 [b, H, P, N])."""
+    return _backward(False, x, dt, A, B, C, dy, D, h0, dhT, chunk, workspace)
+
+
+def diag_scan_bwd(x, dt, A, B, C, dy, D=None, h0=None, dhT=None, chunk=128, workspace=None):
+    """Backward pass of the diagonal-decay forward (A [H, N]): as scan_bwd, with dA
+    float32 [H, N]."""
+    return _backward(True, x, dt, A, B, C, dy, D, h0, dhT, chunk, workspace)

@@ -319,13 +319,18 @@ int step(const ssd_problem* p, int diag, const void* x, const float* dt, const f
 
 // ---- backward pass (ssd_scan_bwd) ----
 struct BwdLayout {
-    size_t cdt, cb, cbt, bt, ct, states, hin, rin, hTf, ds, dDp, dAp, kpart, total;
+    size_t cdt, cb, cbt, bt, ct, states, hin, rin, hTf, ds, dDp, dAp, kpart, zh, yh, dxp, ddtp, total;
 };
 
-BwdLayout bwd_layout_of(const ssd_problem* p) {
+// Scalar decay: C B^T tables, per-token decay terms and boundary partials.  Diagonal decay:
+// per-token Zh / Yh of every head and, when dstate is split over several waves, per-slice
+// partials of dx and ddt.  Both: cumulative dt, chunk states, H_c, R_c, hT and the
+// per-chunk partial sums of dA and dD.
+BwdLayout bwd_layout_of(const ssd_problem* p, int diag) {
     BwdLayout L;
     memset(&L, 0, sizeof(L));
-    const int64_t b = p->batch, H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups, Q = p->chunk;
+    const int64_t b = p->batch, T = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups,
+                  Q = p->chunk;
     const int64_t nc = (p->seqlen + Q - 1) / Q;
     const size_t es = esize(p->dtype), bhc = (size_t)(b * H * nc), bgc = (size_t)(b * nc * G);
     size_t off = 0;
@@ -333,6 +338,24 @@ BwdLayout bwd_layout_of(const ssd_problem* p) {
         at = off;
         off += align_up(bytes);
     };
+    if (diag) {
+        const int nsl = ssd::diag_bwd_slices(P, N);
+        take(L.cdt, bhc * (size_t)Q * 4);
+        take(L.states, bhc * (size_t)(P * N) * 4);
+        take(L.hin, bhc * (size_t)(P * N) * es);
+        take(L.rin, bhc * (size_t)(P * N) * es);
+        take(L.hTf, (size_t)(b * H * P * N) * 4);
+        take(L.zh, bhc * (size_t)(Q * N) * 4);
+        take(L.yh, bhc * (size_t)(Q * N) * 4);
+        if (nsl > 1) {
+            take(L.dxp, (size_t)nsl * (size_t)(b * T * H * P) * 4);
+            take(L.ddtp, (size_t)nsl * (size_t)(b * T * H) * 4);
+        }
+        take(L.dDp, bhc * 4);
+        take(L.dAp, bhc * (size_t)N * 4);
+        L.total = (b == 0 || T == 0) ? 0 : off;
+        return L;
+    }
     take(L.cdt, bhc * (size_t)Q * 4);
     take(L.cb, bgc * (size_t)(Q * Q) * es);
     take(L.cbt, bgc * (size_t)(Q * Q) * es);
@@ -350,34 +373,44 @@ BwdLayout bwd_layout_of(const ssd_problem* p) {
     return L;
 }
 
-int check_bwd(const ssd_problem* p) {
+int check_bwd(const ssd_problem* p, int diag) {
     const int st = check_problem(p);
     if (st) return st;
     if (p->flags != 0) return SSD_ERR_UNSUPPORTED;
     const int64_t nc = (p->seqlen + p->chunk - 1) / p->chunk;
+    if (diag) {
+        // one-dimensional grids: the walks (4 waves per work-group) and the element-wise
+        // reductions (4 elements per thread)
+        const int64_t walks = p->batch * p->nheads * nc * ssd::diag_bwd_slices(p->headdim, p->dstate);
+        const int64_t elems = p->batch * p->seqlen * p->nheads * (p->headdim > p->dstate ? p->headdim : p->dstate);
+        if ((walks + 3) / 4 > 0x7fffffffLL || elems / 4 / 256 + 1 > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
+        return SSD_OK;
+    }
     // k_bwd_bc's grid: (batch, chunk, group, 64-token slab, n range)
     if (p->batch * (nc > 0 ? nc : 1) * p->ngroups * (p->chunk / 64) * 2 > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
-int scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* A, const void* B, const void* C,
-             const float* D, const float* h0, const void* dy, const float* dhT, void* dx, float* ddt, float* dA,
-             void* dB, void* dC, float* dD, float* dh0, void* ws, size_t ws_bytes, void* stream) {
-    int st = check_bwd(p);
+int scan_bwd(const ssd_problem* p, int diag, const void* x, const float* dt, const float* A, const void* B,
+             const void* C, const float* D, const float* h0, const void* dy, const float* dhT, void* dx,
+             float* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0, void* ws, size_t ws_bytes,
+             void* stream) {
+    int st = check_bwd(p, diag);
     if (st) return st;
     const int64_t b = p->batch, T = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups,
                   Q = p->chunk;
     const size_t es = esize(p->dtype);
     const size_t state_bytes = (size_t)(b * H * P * N) * 4;
+    const size_t a_bytes = (size_t)(diag ? H * N : H) * 4;  // A and dA
     if (!A || !dA) return SSD_ERR_NULL;
     if (!aligned(A, 4) || !aligned(dA, 4) || (D && !aligned(D, 4)) || (dD && !aligned(dD, 4)) ||
         (h0 && !aligned(h0, 16)) || (dhT && !aligned(dhT, 16)) || (dh0 && !aligned(dh0, 16)))
         return SSD_ERR_ALIGN;
-    const Range rdA = {dA, (size_t)H * 4}, rdD = {dD, dD ? (size_t)H * 4 : 0}, rdh0 = {dh0, dh0 ? state_bytes : 0};
+    const Range rdA = {dA, a_bytes}, rdD = {dD, dD ? (size_t)H * 4 : 0}, rdh0 = {dh0, dh0 ? state_bytes : 0};
     hipStream_t s = (hipStream_t)stream;
     if (b == 0 || T == 0) {
         // no tokens: dA = dD = 0 and dh0 = dhT (hT is h0 itself); nothing else to write
-        const Range small_in[] = {{A, (size_t)H * 4}, {D, D ? (size_t)H * 4 : 0}, {h0, h0 ? state_bytes : 0},
+        const Range small_in[] = {{A, a_bytes}, {D, D ? (size_t)H * 4 : 0}, {h0, h0 ? state_bytes : 0},
                                   {dhT, dhT ? state_bytes : 0}};
         const Range small_out[] = {rdA, rdD, rdh0};
         for (const Range& o : small_out) {
@@ -386,7 +419,7 @@ int scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* 
             for (const Range& o2 : small_out)
                 if (&o != &o2 && overlap(o, o2)) return SSD_ERR_ALIAS;
         }
-        k_zero<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(dA, H);
+        k_zero<<<(unsigned)((a_bytes / 4 + 255) / 256), 256, 0, s>>>(dA, (int64_t)(a_bytes / 4));
         if (dD) k_zero<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(dD, H);
         if (dh0 && b > 0) {
             const int64_t n = b * H * P * N;
@@ -398,13 +431,13 @@ int scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* 
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(dy, 16) || !aligned(dx, 16) ||
         !aligned(dB, 16) || !aligned(dC, 16) || !aligned(dt, 4) || !aligned(ddt, 4))
         return SSD_ERR_ALIGN;
-    const BwdLayout L = bwd_layout_of(p);
+    const BwdLayout L = bwd_layout_of(p, diag);
     if (!ws || ws_bytes < L.total) return SSD_ERR_WORKSPACE;
     if (!aligned(ws, kAlign)) return SSD_ERR_ALIGN;
     const size_t xb = (size_t)(b * T * H * P) * es, bcb = (size_t)(b * T * G * N) * es;
     const Range ins[] = {{x, xb},
                          {dt, (size_t)(b * T * H) * 4},
-                         {A, (size_t)H * 4},
+                         {A, a_bytes},
                          {B, bcb},
                          {C, bcb},
                          {D, D ? (size_t)H * 4 : 0},
@@ -439,7 +472,12 @@ int scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* 
     a.dDp = reinterpret_cast<float*>(w + L.dDp);
     a.dAp = reinterpret_cast<float*>(w + L.dAp);
     a.kpart = reinterpret_cast<float*>(w + L.kpart);
+    a.zh = reinterpret_cast<float*>(w + L.zh);
+    a.yh = reinterpret_cast<float*>(w + L.yh);
+    a.dxp = reinterpret_cast<float*>(w + L.dxp);
+    a.ddtp = reinterpret_cast<float*>(w + L.ddtp);
     a.stream = s;
+    if (diag) return p->dtype == SSD_BF16 ? ssd::run_bwd_diag_bf16(a) : ssd::run_bwd_diag_f32(a);
     return p->dtype == SSD_BF16 ? ssd::run_bwd_bf16(a) : ssd::run_bwd_f32(a);
 }
 
@@ -494,15 +532,27 @@ int ssd_scan_fwd_varlen(const ssd_problem* p, const int32_t* cu_seqlens, const v
 }
 
 size_t ssd_bwd_workspace_bytes(const ssd_problem* p) {
-    if (check_bwd(p)) return 0;
-    return bwd_layout_of(p).total;
+    if (check_bwd(p, 0)) return 0;
+    return bwd_layout_of(p, 0).total;
 }
 
 int ssd_scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* A, const void* B,
                  const void* C, const float* D, const float* h0, const void* dy, const float* dhT, void* dx,
                  float* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0, void* ws, size_t ws_bytes,
                  void* stream) {
-    return scan_bwd(p, x, dt, A, B, C, D, h0, dy, dhT, dx, ddt, dA, dB, dC, dD, dh0, ws, ws_bytes, stream);
+    return scan_bwd(p, 0, x, dt, A, B, C, D, h0, dy, dhT, dx, ddt, dA, dB, dC, dD, dh0, ws, ws_bytes, stream);
+}
+
+size_t ssd_diag_bwd_workspace_bytes(const ssd_problem* p) {
+    if (check_bwd(p, 1)) return 0;
+    return bwd_layout_of(p, 1).total;
+}
+
+int ssd_diag_scan_bwd(const ssd_problem* p, const void* x, const float* dt, const float* A, const void* B,
+                      const void* C, const float* D, const float* h0, const void* dy, const float* dhT, void* dx,
+                      float* ddt, float* dA, void* dB, void* dC, float* dD, float* dh0, void* ws, size_t ws_bytes,
+                      void* stream) {
+    return scan_bwd(p, 1, x, dt, A, B, C, D, h0, dy, dhT, dx, ddt, dA, dB, dC, dD, dh0, ws, ws_bytes, stream);
 }
 
 const char* ssd_status_string(int status) {

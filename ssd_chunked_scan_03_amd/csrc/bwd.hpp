@@ -69,15 +69,17 @@ __device__ __forceinline__ float sum_wave(float v) {
 // chunk c + 1, <R_c, H_{c+1}> (H_nc = hT, the forward's final state, when dhT is given):
 // each wave reduces its elements' share and writes one partial per chunk,
 // kpart[b, h, c, (block part) * 4 + wave], summed in that order by k_bwd_dt.  (P N / 4
-// is a multiple of 64, so every wave is either whole or absent.)
+// is a multiple of 64, so every wave is either whole or absent.)  DIAG: each element
+// decays at its own rate exp(A_{h,n} cdt_last); no boundary products (the diagonal
+// backward forms them per dimension itself).
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool DIAG = false>
 __global__ __launch_bounds__(kThreads) void k_scan_rev(const float* __restrict__ S, T* __restrict__ rin,
                                                        float* __restrict__ dh0, const float* __restrict__ dhT,
                                                        const float* __restrict__ A, const float* __restrict__ cdt,
                                                        const T* __restrict__ hin, const float* __restrict__ hTf,
-                                                       float* __restrict__ kpart, int H, int PN, int Q, int nc,
-                                                       int per_head) {
+                                                       float* __restrict__ kpart, int H, int PN, int N, int Q,
+                                                       int nc, int per_head) {
     typedef typename V4<T>::type v4;
     const int64_t bh = blockIdx.x / per_head;
     const int part = (int)(blockIdx.x - bh * per_head);
@@ -85,13 +87,16 @@ __global__ __launch_bounds__(kThreads) void k_scan_rev(const float* __restrict__
     const int e0 = (part * kThreads + threadIdx.x) * 4;
     if (e0 >= PN) return;
     const int lane = threadIdx.x & 63, slot = part * 4 + (int)(threadIdx.x >> 6), nslot = per_head * 4;
-    const float a = A[h];
+    // decay rate of each of the thread's 4 elements (4 consecutive n of one p)
+    float a4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a4[r] = DIAG ? A[(int64_t)h * N + (e0 + r) % N] : A[h];
     f32x4 st = dhT ? ld4(dhT + bh * PN + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
     const float* cl = cdt + bh * (int64_t)nc * Q + (Q - 1);
     const float* sp = S + bh * (int64_t)nc * PN + e0;
     T* rp = rin + bh * (int64_t)nc * PN + e0;
     const T* hp = hin + bh * (int64_t)nc * PN + e0;
-    float* kp = kpart + bh * (int64_t)nc * nslot + slot;
+    float* kp = DIAG ? nullptr : kpart + bh * (int64_t)nc * nslot + slot;
     constexpr int DEPTH = 8;
     for (int c0 = nc - 1; c0 >= 0; c0 -= DEPTH) {
         f32x4 s[DEPTH];
@@ -103,7 +108,9 @@ __global__ __launch_bounds__(kThreads) void k_scan_rev(const float* __restrict__
             if (c >= 0) {
                 s[k] = ld4(sp + (int64_t)c * PN);
                 Lc[k] = cl[(int64_t)c * Q];
-                if (c + 1 < nc) {
+                if (DIAG) {
+                    hn[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                } else if (c + 1 < nc) {
                     const v4 hv = ld4(hp + (int64_t)(c + 1) * PN);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) hn[k][r] = to_f(hv[r]);
@@ -120,13 +127,15 @@ __global__ __launch_bounds__(kThreads) void k_scan_rev(const float* __restrict__
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = from_f<T>(st[r]);
                 st4(rp + (int64_t)c * PN, o);
-                float dot = 0.f;
+                if (!DIAG) {
+                    float dot = 0.f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dot += st[r] * hn[k][r];
-                dot = sum_wave(dot);
-                if (lane == 0) kp[(int64_t)c * nslot] = dot;
+                    for (int r = 0; r < 4; ++r) dot += st[r] * hn[k][r];
+                    dot = sum_wave(dot);
+                    if (lane == 0) kp[(int64_t)c * nslot] = dot;
+                }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) st[r] = exp_f(a * Lc[k]) * st[r] + s[k][r];
+                for (int r = 0; r < 4; ++r) st[r] = exp_f(a4[r] * Lc[k]) * st[r] + s[k][r];
             }
         }
     }

@@ -1,0 +1,15 @@
+// Diagonal-decay backward instantiations for bf16 x/B/C/dy.
+#include "bwd_launch.hpp"
+#include "launch.hpp"
+
+namespace ssd {
+int run_bwd_diag_bf16(const BwdArgs& a) {
+    switch (a.P * 1000 + a.N) {
+#define SSD_CASE(P, N) \
+    case P * 1000 + N: return run_bwd_diag<bf16, P, N>(a);
+        SSD_FOR_EACH_PN(SSD_CASE)
+#undef SSD_CASE
+        default: return 3;
+    }
+}
+}  // namespace ssd

@@ -2,6 +2,7 @@
 #pragma once
 
 #include "bwd.hpp"
+#include "bwd_diag.hpp"
 
 namespace ssd {
 
@@ -38,6 +39,11 @@ struct BwdArgs {
     float* dDp;     // [b,H,nc]      D partial sums
     float* dAp;     // [b,H,nc]      A partial sums
     float* kpart;   // [b,H,nc,4 * ceil(P N / 1024)]  per-wave partials of <R_c, H_{c+1}>
+    // diagonal decay only (dAp is then [b,H,nc,N])
+    float* zh;      // [b,H,nc,Q,N]  dy_t . h_t per dimension
+    float* yh;      // [b,H,nc,Q,N]  x_t . g_t per dimension
+    float* dxp;     // [nsl,b,T,H,P] per-slice partials of dx (dstate split over nsl waves)
+    float* ddtp;    // [nsl,b,T,H]   per-slice partials of ddt
     hipStream_t stream;
 };
 
@@ -103,7 +109,7 @@ int run_bwd(const BwdArgs& a) {
     const dim3 g4((unsigned)(a.b * H * per_head));
     k_state<T, P, N, false, true><<<g3, kThreads, 0, s>>>(dy, Cm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
     k_scan_rev<T><<<g4, kThreads, 0, s>>>(a.states, rin, a.dh0, a.dhT, a.A, a.cdt, hin, a.hTf, a.kpart, H,
-                                          (int)(a.P * a.N), Q, nc, per_head);
+                                          (int)(a.P * a.N), (int)a.N, Q, nc, per_head);
     const int nslot = per_head * 4, nvalid = (int)(a.P * a.N / 4 / 64);  // partials per chunk; waves with elements
     // gradients
     (void)hipFuncSetAttribute((const void*)k_bwd_x<T, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sx);
@@ -119,7 +125,75 @@ int run_bwd(const BwdArgs& a) {
     return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 
+// The diagonal-decay backward (bwd_diag.hpp): forward chunk states and their scan, the
+// adjoint's chunk inputs and reverse scan, the per-chunk walks, then the head and
+// (batch, chunk) reductions.
+template <typename T, int P, int N>
+int run_bwd_diag(const BwdArgs& a) {
+    typedef DiagSplit<P, N> SP;
+    const int Q = (int)a.Q, nc = (int)a.nc, H = (int)a.H, G = (int)a.G;
+    hipStream_t s = a.stream;
+    const T* x = static_cast<const T*>(a.x);
+    const T* dy = static_cast<const T*>(a.dy);
+    const T* Bm = static_cast<const T*>(a.B);
+    const T* Cm = static_cast<const T*>(a.C);
+    T* hin = static_cast<T*>(a.hin);
+    T* rin = static_cast<T*>(a.rin);
+
+    Rows rows;
+    rows.ts = nullptr;
+    rows.kb = nullptr;
+    rows.T = a.T;
+    rows.nc = nc;
+    rows.nrows = (int)a.b;
+    rows.H = H;
+    rows.kcap = (int)(a.b * a.nc);
+    const dim3 g1((unsigned)rows.kcap, 1, (H + 15) / 16);
+    switch (Q) {
+        case 64: k_cumsum<64><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
+        case 128: k_cumsum<128><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
+        case 256: k_cumsum<256><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
+        default: return 3;
+    }
+    const dim3 g3((unsigned)(a.b * H * nc));
+    const int PN = (int)(a.P * a.N);
+    const int per_head = (PN / 4 + kThreads - 1) / kThreads;
+    const dim3 g4((unsigned)(a.b * H * per_head));
+    const int64_t BHPN = a.b * H * a.P * a.N;
+    // entering states H_c and the final state
+    k_state<T, P, N, true, false><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
+    k_scan<T, true, 0><<<g4, kThreads, 0, s>>>(a.states, hin, a.dhT ? a.hTf : nullptr, a.h0, a.A, a.cdt, nullptr,
+                                               nullptr, H, PN, N, Q, nc, per_head, nc, BHPN);
+    // the adjoint: chunk inputs sum_i e^{A_n cdt_i} dy_i C_i^T, reverse scan -> R_c, dh0
+    k_state<T, P, N, true, true><<<g3, kThreads, 0, s>>>(dy, Cm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
+    k_scan_rev<T, true><<<g4, kThreads, 0, s>>>(a.states, rin, a.dh0, a.dhT, a.A, a.cdt, hin, a.hTf, nullptr, H,
+                                                PN, N, Q, nc, per_head);
+    // the walks of every chunk
+    const int64_t nwaves = a.b * H * nc * SP::NSL;
+    k_bwd_diag<T, P, N><<<(unsigned)((nwaves + 3) / 4), kThreads, 0, s>>>(
+        x, dy, Bm, Cm, a.dt, a.A, a.D, hin, rin, a.hTf, a.dhT != nullptr, a.zh, a.yh, static_cast<T*>(a.dx), a.dxp,
+        a.ddt, a.ddtp, a.dAp, a.dDp, a.b, a.T, H, G, Q, nc, nwaves);
+    const int64_t bc4 = a.b * a.T * G * N / 4;
+    k_bwd_diag_bc<T><<<(unsigned)((bc4 + kThreads - 1) / kThreads), kThreads, 0, s>>>(
+        a.zh, a.yh, static_cast<T*>(a.dB), static_cast<T*>(a.dC), a.T, H, G, N, Q, nc, bc4);
+    if (SP::NSL > 1) {
+        const int64_t x4 = a.b * a.T * H * a.P / 4;
+        k_bwd_diag_fin<T><<<(unsigned)((x4 + kThreads - 1) / kThreads), kThreads, 0, s>>>(
+            a.dxp, a.ddtp, dy, a.D, static_cast<T*>(a.dx), a.ddt, H, (int)a.P, SP::NSL, x4);
+    }
+    k_bwd_diag_reduce<kThreads><<<(unsigned)H, kThreads, 0, s>>>(a.dAp, a.dDp, a.dA, a.dD, a.b, H, N, nc);
+    return hipGetLastError() == hipSuccess ? 0 : 7;
+}
+
+// dstate slices of the diagonal backward's walks (host side of DiagSplit)
+inline int diag_bwd_slices(int64_t P, int64_t N) {
+    const int64_t ns = N < 64 ? (N < 4096 / P ? N : 4096 / P) : (64 < 4096 / P ? 64 : 4096 / P);
+    return (int)(N / ns);
+}
+
 int run_bwd_bf16(const BwdArgs& a);
 int run_bwd_f32(const BwdArgs& a);
+int run_bwd_diag_bf16(const BwdArgs& a);
+int run_bwd_diag_f32(const BwdArgs& a);
 
 }  // namespace ssd

@@ -281,13 +281,14 @@ def test_varlen_error_paths_return_before_any_launch():
 
 # ---- backward pass (ssd_scan_bwd) ----
 
-def bwd_fake_ptrs(p):
+def bwd_fake_ptrs(p, diag=False):
     b, T, H, P, N, G = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups
     es = 2 if p.dtype == ssd.SSD_BF16 else 4
-    lay_bytes = max(ssd.bwd_workspace_bytes(p), 1)
+    lay_bytes = max(ssd.bwd_workspace_bytes(p, diag), 1)
     xs, bc, st = b * T * H * P * es, b * T * G * N * es, b * H * P * N * 4
-    sizes = dict(x=xs, dt=b * T * H * 4, A=H * 4, B=bc, C=bc, D=H * 4, h0=st, dy=xs, dhT=st,
-                 dx=xs, ddt=b * T * H * 4, dA=H * 4, dB=bc, dC=bc, dD=H * 4, dh0=st, ws=lay_bytes)
+    an = H * N * 4 if diag else H * 4
+    sizes = dict(x=xs, dt=b * T * H * 4, A=an, B=bc, C=bc, D=H * 4, h0=st, dy=xs, dhT=st,
+                 dx=xs, ddt=b * T * H * 4, dA=an, dB=bc, dC=bc, dD=H * 4, dh0=st, ws=lay_bytes)
     ptrs, cur = {}, BASE
     for k, n in sizes.items():
         ptrs[k] = cur
@@ -298,14 +299,15 @@ def bwd_fake_ptrs(p):
 BWD_ARGS = ("x", "dt", "A", "B", "C", "D", "h0", "dy", "dhT", "dx", "ddt", "dA", "dB", "dC", "dD", "dh0")
 
 
-def call_bwd(p, **over):
-    """ssd_scan_bwd with fake well-formed pointers, some overridden; every use below is
-    invalid on purpose, so the host rejects it before any launch."""
-    ptrs, lay_bytes = bwd_fake_ptrs(p)
+def call_bwd(p, diag=False, **over):
+    """ssd_scan_bwd / ssd_diag_scan_bwd with fake well-formed pointers, some overridden;
+    every use below is invalid on purpose, so the host rejects it before any launch."""
+    ptrs, lay_bytes = bwd_fake_ptrs(p, diag)
     ws_bytes = over.pop("ws_bytes", lay_bytes)
     ptrs.update(over)
     v = lambda k: ctypes.c_void_p(ptrs[k]) if ptrs[k] else None
-    return ssd._load().ssd_scan_bwd(ctypes.byref(p), *(v(k) for k in BWD_ARGS), v("ws"), ws_bytes, None), ptrs
+    f = ssd._load().ssd_diag_scan_bwd if diag else ssd._load().ssd_scan_bwd
+    return f(ctypes.byref(p), *(v(k) for k in BWD_ARGS), v("ws"), ws_bytes, None), ptrs
 
 
 def test_bwd_workspace_arithmetic():
@@ -350,3 +352,45 @@ def test_bwd_empty_problem_aliasing_checked():
     ptrs, _ = bwd_fake_ptrs(prob(T=0))
     assert call_bwd(prob(T=0), dA=ptrs["A"])[0] == ssd_status("SSD_ERR_ALIAS")
     assert call_bwd(prob(T=0), dh0=ptrs["dhT"])[0] == ssd_status("SSD_ERR_ALIAS")
+
+
+# ---- backward pass of the diagonal decay (ssd_diag_scan_bwd) ----
+
+def test_diag_bwd_workspace_arithmetic():
+    a = lambda n: (n + 255) // 256 * 256
+    for (b, T, H, P, N, G, Q, nsl) in ((2, 300, 4, 64, 64, 2, 128, 1), (2, 300, 4, 64, 128, 2, 128, 2),
+                                       (1, 70, 2, 128, 256, 1, 64, 8), (1, 70, 2, 16, 256, 1, 64, 4)):
+        p = ssd.make_problem(b, T, H, P, N, G, Q, ssd.SSD_BF16)
+        nc = -(-T // Q)
+        bhc = b * H * nc
+        want = (a(bhc * Q * 4) + a(bhc * P * N * 4) + 2 * a(bhc * P * N * 2) + a(b * H * P * N * 4)
+                + 2 * a(bhc * Q * N * 4) + ((a(nsl * b * T * H * P * 4) + a(nsl * b * T * H * 4)) if nsl > 1 else 0)
+                + a(bhc * 4) + a(bhc * N * 4))
+        assert ssd.bwd_workspace_bytes(p, diag=True) == want, (P, N)
+    assert ssd.bwd_workspace_bytes(prob(T=0), diag=True) == 0
+    assert ssd.bwd_workspace_bytes(prob(Q=96), diag=True) == 0
+    p = prob()
+    p.flags = ssd.SCHEDULE_SPLIT
+    assert ssd.bwd_workspace_bytes(p, diag=True) == 0
+
+
+def test_diag_bwd_error_paths_return_before_any_launch():
+    p = prob()
+    S = ssd_status
+    for k in ("x", "dt", "B", "C", "dy", "dx", "ddt", "dB", "dC", "A", "dA"):
+        assert call_bwd(p, True, **{k: 0})[0] == S("SSD_ERR_NULL"), k
+    assert call_bwd(p, True, ws_bytes=ssd.bwd_workspace_bytes(p, True) - 1)[0] == S("SSD_ERR_WORKSPACE")
+    for k, off in (("dy", 8), ("dx", 8), ("dB", 8), ("dhT", 4), ("dh0", 4), ("ddt", 2), ("dA", 2), ("ws", 16)):
+        assert call_bwd(p, True, **{k: BASE + off})[0] == S("SSD_ERR_ALIGN"), k
+    ptrs, _ = bwd_fake_ptrs(p, True)
+    # dA is [H, N]: an overlap past the first H floats of A is still an overlap
+    assert call_bwd(p, True, dA=ptrs["A"] + 4 * p.nheads)[0] == S("SSD_ERR_ALIAS")
+    assert call_bwd(p, True, dD=ptrs["dA"] + 4 * p.nheads)[0] == S("SSD_ERR_ALIAS")
+    for out, inp in (("dx", "x"), ("dB", "C"), ("dC", "ws"), ("dh0", "dhT"), ("ddt", "dt")):
+        assert call_bwd(p, True, **{out: ptrs[inp]})[0] == S("SSD_ERR_ALIAS"), (out, inp)
+    assert call_bwd(prob(H=6, G=4), True)[0] == S("SSD_ERR_SHAPE")
+    assert call_bwd(prob(Q=32), True)[0] == S("SSD_ERR_UNSUPPORTED")
+    assert ssd._load().ssd_diag_scan_bwd(None, *([None] * 17), 0, None) == S("SSD_ERR_NULL")
+    # an empty problem checks dA against A over [H, N] too
+    ptrs0, _ = bwd_fake_ptrs(prob(T=0), True)
+    assert call_bwd(prob(T=0), True, dA=ptrs0["A"] + 4 * p.nheads)[0] == S("SSD_ERR_ALIAS")

@@ -34,7 +34,7 @@ def vec_rel(got, ref):
     return float(err / den) if den > 0 else float(err)
 
 
-def run_bwd(inp, gr, dtype, chunk, use_D=True, use_h0=True, use_dhT=True):
+def run_bwd(inp, gr, dtype, chunk, use_D=True, use_h0=True, use_dhT=True, diag=False):
     d = upload(inp, dtype)
     td = torch_dtype(dtype)
     dy = torch.from_numpy(np.ascontiguousarray(gr["dy"])).to("cuda").to(td).contiguous()
@@ -49,13 +49,14 @@ def run_bwd(inp, gr, dtype, chunk, use_D=True, use_h0=True, use_dhT=True):
     out = dict(dx=torch.full_like(x, nan), ddt=torch.full_like(d["dt"], nan), dA=torch.full_like(d["A"], nan),
                dB=torch.full_like(B, nan), dC=torch.full_like(B, nan),
                dD=torch.full((H,), nan, device="cuda"), dh0=torch.full((b, H, P, N), nan, device="cuda"))
-    ws = torch.full((max(ssd.bwd_workspace_bytes(prob), 1),), 0xFF, dtype=torch.uint8, device="cuda")
+    ws = torch.full((max(ssd.bwd_workspace_bytes(prob, diag), 1),), 0xFF, dtype=torch.uint8, device="cuda")
     ssd.scan_bwd_into(prob, x, d["dt"], d["A"], B, d["C"], D, h0, dy, dhT, out["dx"], out["ddt"], out["dA"],
-                      out["dB"], out["dC"], out["dD"], out["dh0"], ws)
+                      out["dB"], out["dC"], out["dD"], out["dh0"], ws, diag=diag)
     torch.cuda.synchronize()
     got = {k: v.float().cpu().numpy() for k, v in out.items()}
     ref = oracle.recurrence_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"] if use_D else None,
-                                inp["h0"] if use_h0 else None, dy=gr["dy"], dhT=gr["dhT"] if use_dhT else None)
+                                inp["h0"] if use_h0 else None, dy=gr["dy"], dhT=gr["dhT"] if use_dhT else None,
+                                diag=diag)
     got["_dt"] = ref["_dt"] = np.asarray(inp["dt"], np.float64)
     got["_A"] = ref["_A"] = np.asarray(inp["A"], np.float64)
     return got, ref
