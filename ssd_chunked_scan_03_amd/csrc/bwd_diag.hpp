@@ -371,24 +371,48 @@ __global__ __launch_bounds__(kThreads) void k_bwd_diag_fin(const float* __restri
     }
 }
 
-// dA[h, n] = sum over (batch, chunk) of dAp, dD[h] = sum of dDp, in (batch, chunk) order;
-// one work-group per head
+// dA[h, n] = sum over (batch, chunk) of dAp, dD[h] = sum of dDp; one work-group per head.
+// The (batch, chunk) list is cut into RP contiguous parts, each summed by its own thread
+// with eight loads in flight, and the parts are added in part order: a fixed order.
 template <int BLOCK>
 __global__ __launch_bounds__(BLOCK) void k_bwd_diag_reduce(const float* __restrict__ dAp,
                                                            const float* __restrict__ dDp, float* __restrict__ dA,
                                                            float* __restrict__ dD, int64_t nb, int H, int N, int nc) {
+    __shared__ float part[BLOCK];
     const int h = blockIdx.x;
-    for (int n = threadIdx.x; n < N; n += BLOCK) {
+    const int64_t nbc = nb * nc;  // (batch, chunk) pairs, index bi * nc + c
+    // columns: n = 0 .. N-1 for dA, and one more for dD
+    const int cols = N + 1;
+    const int RP = BLOCK / cols > 0 ? BLOCK / cols : 1;
+    for (int c0 = 0; c0 < cols; c0 += BLOCK / RP) {
+        const int col = c0 + (int)threadIdx.x % (BLOCK / RP), rp = (int)threadIdx.x / (BLOCK / RP);
         float s = 0.f;
-        for (int64_t bi = 0; bi < nb; ++bi)
-            for (int c = 0; c < nc; ++c) s += dAp[((bi * H + h) * nc + c) * N + n];
-        dA[(int64_t)h * N + n] = s;
-    }
-    if (dD && threadIdx.x == 0) {
-        float s = 0.f;
-        for (int64_t bi = 0; bi < nb; ++bi)
-            for (int c = 0; c < nc; ++c) s += dDp[(bi * H + h) * nc + c];
-        dD[h] = s;
+        if (col < cols && rp < RP) {
+            const int64_t lo = nbc * rp / RP, hi = nbc * (rp + 1) / RP;
+            auto at = [&](int64_t k) {
+                const int64_t bi = k / nc, c = k - bi * nc;
+                const int64_t bhc = (bi * H + h) * nc + c;
+                return col < N ? dAp[bhc * N + col] : (dDp ? dDp[bhc] : 0.f);
+            };
+            int64_t k = lo;
+            for (; k + 8 <= hi; k += 8) {
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = at(k + u);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) s += v[u];
+            }
+            for (; k < hi; ++k) s += at(k);
+        }
+        part[threadIdx.x] = s;
+        __syncthreads();
+        if (rp == 0 && col < cols) {
+            float t = 0.f;
+            for (int r = 0; r < RP; ++r) t += part[r * (BLOCK / RP) + (int)threadIdx.x];
+            if (col < N) dA[(int64_t)h * N + col] = t;
+            else if (dD) dD[h] = t;
+        }
+        __syncthreads();
     }
 }
 
