@@ -8,8 +8,8 @@ seqlen 1 to three chunks and more (ragged tails included), 1-6 heads with every 
 count that divides them, headdim 16-128, dstate 16-256, chunk 64/128/256.  A draw
 outside the supported set must be refused with SSD_ERR_UNSUPPORTED and nothing else:
 the output kernel's LDS tile (chunk rows of x, plus the rescaled C and B rows for the
-diagonal decay) has to fit the 160 KiB of one CU, and the backward has no float32
-headdim 128 at chunk 256."""
+diagonal decay) has to fit the 160 KiB of one CU, and the scalar backward has no float32
+headdim 128 at chunk 256 (the diagonal backward takes every shape)."""
 import numpy as np
 import pytest
 import torch
@@ -40,6 +40,7 @@ def _draw(n, seed, diag_ok):
 
 FWD = _draw(24, 20261203, diag_ok=True)
 BWD = _draw(12, 4051, diag_ok=False)
+BWD_DIAG = [dict(c, diag=True) for c in _draw(10, 9176, diag_ok=False)]
 
 
 def _fwd_lds_fits(c):
@@ -90,6 +91,17 @@ def test_random_backward_matches_oracle(c):
     check_bwd(got, ref, c["dtype"], _ident(c))
 
 
+@pytest.mark.parametrize("c", BWD_DIAG, ids=_ident)
+def test_random_diag_backward_matches_oracle(c):
+    from test_gpu_bwd_diag import check_diag
+    print(f"[random bwd diag] {_ident(c)} h0={c['h0']} D={c['D']}", flush=True)
+    inp = make_small(c["b"], c["T"], c["H"], c["P"], c["N"], c["G"], seed=c["T"] + 13 * c["N"], diag=True,
+                     dtype=c["dtype"])
+    gr = make_grads(c["b"], c["T"], c["H"], c["P"], c["N"], seed=c["T"] + 1, dtype=c["dtype"])
+    got, ref = run_bwd(inp, gr, c["dtype"], c["Q"], use_D=c["D"], use_h0=c["h0"], diag=True)
+    check_diag(got, ref, c["dtype"], _ident(c))
+
+
 def test_random_draws_cover_the_support_set():
     """The draws reach every chunk, headdim, dstate and dtype, both decays, and refused
     as well as accepted forward problems (a host-only check of the lists above)."""
@@ -99,3 +111,6 @@ def test_random_draws_cover_the_support_set():
     assert {c["diag"] for c in FWD} == {False, True}
     assert any(not _fwd_lds_fits(c) for c in FWD) and sum(_fwd_lds_fits(c) for c in FWD) >= 18
     assert any(c["G"] > 1 for c in FWD + BWD) and any(c["T"] % c["Q"] for c in FWD + BWD)
+    # the diagonal backward's draws reach every headdim and chunk, and dstate split into slices
+    assert {c["P"] for c in BWD_DIAG} == {16, 32, 64, 128} and {c["Q"] for c in BWD_DIAG} == {64, 128, 256}
+    assert any(c["P"] * c["N"] > 4096 or c["N"] > 64 for c in BWD_DIAG)
