@@ -63,8 +63,9 @@ def cpu_baseline(w, inp, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed forwards first (about 40 ms at the default workload: the GPU clock settles)")
     ap.add_argument("--workload", default=None, help="workload name (default: the 2.7B layer shape)")
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
