@@ -114,19 +114,25 @@ struct DiagSplit {
     static_assert(NS % 16 == 0 && NSL * NS == N && PP >= 2, "dstate slice");
 };
 
+// Lane sums without LDS memory: DPP moves within a row of 16 lanes (quad_perm [1,0,3,2]
+// and [2,3,0,1] pair lanes l ^ 1 and l ^ 2; row_half_mirror pairs the two quads of each
+// 8-lane half, whose quad sums are by then uniform; row_ror:8 pairs l ^ 8), a ds_swizzle
+// for l ^ 16 within each 32-lane half, and a cross-half permute for l ^ 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 // sum over the 8 lanes of one dimension group (lanes ng, ng + 8, ..., ng + 56)
 __device__ __forceinline__ float sum_pg(float v) {
-    v += __shfl_xor(v, 8, 64);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    v += dpp_f<0x128>(v);  // row_ror:8
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));  // l ^ 16
+    return v + __shfl_xor(v, 32, 64);
 }
 // sum over the 8 lanes of one channel group (lanes 8 pg .. 8 pg + 7)
 __device__ __forceinline__ float sum_ng(float v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    return v;
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    return v + dpp_f<0x141>(v);  // row_half_mirror
 }
 
 // ---------------------------------------------------------------------------
