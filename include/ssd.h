@@ -147,6 +147,10 @@ typedef struct {
 } ssd_workspace_layout;
 int ssd_get_workspace_layout(const ssd_problem* p, int diag, ssd_workspace_layout* out);
 
+/* Stream capture: no entry point allocates, sets memory with a memset, synchronises the
+ * host or reads device memory on the host, so every call can be captured into a HIP
+ * graph on the caller's stream and replayed (with the same arguments and workspace). */
+
 /* Scalar-decay SSD forward: A is [nheads].  Writes y (and hT if non-NULL).
  * `ws` must hold ssd_workspace_bytes(p, 0) bytes. */
 int ssd_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const float* A,
