@@ -326,6 +326,77 @@ __device__ __forceinline__ void cb_body(const T* __restrict__ Bm, const T* __res
     }
 }
 
+// One 64-row block row I of a chunk's C B^T (tiles J = 0 .. I, I < 4) for bfloat16 with
+// dstate >= kCbStageN: the block row's C rows are staged in LDS once and serve every
+// tile; each tile's B rows are in flight while the previous tile computes.  Same
+// output as cb_body on each tile (the same products in the same order).  (Taking the
+// tiles in pairs, so that each C fragment read from LDS feeds two matrix-core steps,
+// measured slower: 214 against 194 us at the long workload.)
+template <int N>
+__device__ __forceinline__ void cb_row_body(const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
+                                            bf16* __restrict__ cb, Rows rows, int G, int Q, int kg, int I, int g,
+                                            bf16* __restrict__ cs) {
+    static_assert(N % 32 == 0 && N >= kCbStageN, "staged block rows");
+    if (kg >= rows.total_chunks()) return;
+    const int rr = rows.row_of(kg);
+    const int c = kg - rows.kbase(rr);
+    const int64_t Tn = rows.len(rr);
+    Bm += rows.tok0(rr) * G * N;
+    Cm += rows.tok0(rr) * G * N;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int l16 = lane & 15, q = lane >> 4;
+    const int64_t tok0 = (int64_t)c * Q;
+    constexpr int KS = N / 32, LDC = N + 8;
+    const uint32_t rowb = (uint32_t)(G * N * 2);
+    const uint32_t span = (uint32_t)(Tn * G * N * 2);  // the caller checks it is under 2 GiB
+    const brsrc rb = make_rsrc(Bm, span);
+    const brsrc rc = make_rsrc(Cm, span);
+    const int s0 = __builtin_amdgcn_readfirstlane((int)(tok0 * rowb + g * N * 2));
+    for (int v = threadIdx.x; v < 64 * N / 8; v += kThreads) {
+        const int r = v / (N / 8), n0 = (v - r * (N / 8)) * 8;
+        st8(cs + r * LDC + n0, bload8(rc, r * (int)rowb + n0 * 2, s0 + I * 64 * (int)rowb));
+    }
+    __syncthreads();
+    bf16* out = cb + ((int64_t)kg * G + g) * (int64_t)Q * Q;
+    // B rows of tile J + 1 are requested while tile J computes (two register sets; the
+    // tile loop is unrolled so both are indexed statically)
+    bf16x8 fb[2][KS];
+    auto load = [&](int J, int set) {
+        const int vb = (J * 64 + 16 * w + l16) * rowb + 16 * q;  // B row of this wave's column, k-group q
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) fb[set][ks] = bload8(rb, vb, s0 + ks * 64);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        if (J > I) break;
+        __builtin_amdgcn_sched_barrier(0);
+        if (J + 1 <= I) load(J + 1, (J + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                acc[ct] = mma(acc[ct], fb[J & 1][ks], ld8(cs + (16 * ct + l16) * LDC + ks * 32 + 8 * q));
+        const int j0 = J * 64 + 16 * w + 4 * q;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const int i = I * 64 + 16 * ct + l16;
+            st4(out + (int64_t)i * Q + j0, bf16x4{(bf16)acc[ct][0], (bf16)acc[ct][1], (bf16)acc[ct][2], (bf16)acc[ct][3]});
+        }
+    }
+}
+
+// C B^T work items of one chunk and group in k_prep: a block row per work-group where
+// the staged path applies (bfloat16, dstate >= kCbStageN), else one 64 x 64 tile each
+template <typename T, int N>
+__host__ __device__ constexpr bool prep_cb_rows() { return sizeof(T) == 2 && N >= kCbStageN && N % 32 == 0; }
+template <typename T, int N>
+__host__ __device__ constexpr int prep_cb_tasks(int nb) { return prep_cb_rows<T, N>() ? nb : nb * (nb + 1) / 2; }
+
 template <typename T, int N, bool TR = false>
 __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const T* __restrict__ Cm,
                                                  T* __restrict__ cb, Rows rows, int G, int Q) {
@@ -389,7 +460,7 @@ template <typename T, int N, int Q, bool BT>
 __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ dt, float* __restrict__ cdt,
                                                    const T* __restrict__ Bm, const T* __restrict__ Cm,
                                                    T* __restrict__ cb, T* __restrict__ Bt, Rows rows, int G) {
-    constexpr int nb = Q / 64, npair = nb * (nb + 1) / 2, nslab = Q / 64;
+    constexpr int nb = Q / 64, nslab = Q / 64;
     // one LDS buffer for whichever task the work-group runs
     constexpr size_t s1 = cumsum_smem<Q>(), s2 = cb_smem<T, N>(), s3 = BT ? bt_smem<T, N>() : 0;
     constexpr size_t SB = s1 > s2 ? (s1 > s3 ? s1 : s3) : (s2 > s3 ? s2 : s3);
@@ -402,11 +473,27 @@ __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ dt,
         return;
     }
     y -= nh;
-    if (y < npair * G) {
-        cb_body<T, N, false>(Bm, Cm, cb, rows, G, Q, k, y % npair, y / npair, reinterpret_cast<T*>(smem));
+    constexpr int ncb = prep_cb_tasks<T, N>(nb);
+    if (y < ncb * G) {
+        if constexpr (prep_cb_rows<T, N>()) {
+            // block rows need the batch row's B / C to span under 2 GiB (32-bit buffer offsets)
+            const int64_t span = rows.len(rows.row_of(k < rows.total_chunks() ? k : 0)) * G * N * 2;
+            if (span < ((int64_t)1 << 31)) {
+                cb_row_body<N>(Bm, Cm, cb, rows, G, Q, k, y % ncb, y / ncb, reinterpret_cast<bf16*>(smem));
+                return;
+            }
+            // otherwise each tile of the block row, as k_cb computes it
+            const int I = y % ncb;
+            for (int J = 0; J <= I; ++J) {
+                cb_body<T, N, false>(Bm, Cm, cb, rows, G, Q, k, I * (I + 1) / 2 + J, y / ncb, reinterpret_cast<T*>(smem));
+                __syncthreads();
+            }
+        } else {
+            cb_body<T, N, false>(Bm, Cm, cb, rows, G, Q, k, y % ncb, y / ncb, reinterpret_cast<T*>(smem));
+        }
         return;
     }
-    y -= npair * G;
+    y -= ncb * G;
     if (BT) bt_body<T, N>(Bm, Bt, rows, G, Q, k, (y % nslab) * 64, y / nslab, reinterpret_cast<T*>(smem));
 }
 

@@ -116,7 +116,7 @@ int run(const RunArgs& a) {
     const int prep_bits = fused ? (1 | 2 | 32) : (1 | 2);
     if (!a.diag && (st & prep_bits) == prep_bits) {
         const int nb = Q / 64;
-        const dim3 gp(kc, (unsigned)((H + 15) / 16 + (nb * (nb + 1) / 2) * G + (fused ? nb * G : 0)));
+        const dim3 gp(kc, (unsigned)((H + 15) / 16 + prep_cb_tasks<T, N>(nb) * G + (fused ? nb * G : 0)));
         switch (Q * 2 + (fused ? 1 : 0)) {
 #define SSD_PREP(QQ, F) \
     case QQ * 2 + F: k_prep<T, N, QQ, F><<<gp, kThreads, 0, s>>>(a.dt, a.cdt, Bm, Cm, cb, static_cast<T*>(a.bt), rows, G); break;

@@ -255,27 +255,29 @@ def test_segmented_state_scan_matches_oracle(case):
     assert max_rel_err(Hc, st["Hc"], (0, 1, 2)) < TOL[dtype]
 
 
-@pytest.mark.parametrize("schedule", ["fused", "split"])
-def test_prep_launch_matches_separate_stage_kernels(schedule):
+@pytest.mark.parametrize("schedule,N,Q", [("fused", 128, 128), ("split", 128, 128), ("split", 256, 256),
+                                          ("split", 256, 128)])
+def test_prep_launch_matches_separate_stage_kernels(schedule, N, Q):
     """A whole forward runs its preparation (cumsum, C B^T, and B^T on the fused schedule)
     as one k_prep launch; a forward enqueued one kernel per stage runs the separate
-    kernels.  Same arithmetic per element, so y and hT agree bit for bit."""
+    kernels (at dstate 256 k_prep takes a whole 64-row block row of C B^T per work-group,
+    k_cb one tile).  Same arithmetic per element, so y and hT agree bit for bit."""
     from gpu_common import upload
-    inp = make_small(2, 700, 8, 64, 128, 2, seed=41, dtype="bf16")
+    inp = make_small(2, 700, 8, 64, N, 2, seed=41, dtype="bf16")
     d = upload(inp, "bf16")
     b, T, H, P = d["x"].shape
     G, N = d["B"].shape[2], d["B"].shape[3]
     sf = ssd.SCHEDULE_FUSED if schedule == "fused" else ssd.SCHEDULE_SPLIT
     outs = []
     for staged in (False, True):
-        base = ssd.make_problem(b, T, H, P, N, G, 128, ssd.SSD_BF16, sf)
+        base = ssd.make_problem(b, T, H, P, N, G, Q, ssd.SSD_BF16, sf)
         y = torch.full_like(d["x"], float("nan"))
         hT = torch.full((b, H, P, N), float("nan"), device="cuda")
         ws = torch.full((ssd.workspace_bytes(base),), 0xFF, dtype=torch.uint8, device="cuda")
         kernels = ssd.FUSED_KERNELS if schedule == "fused" else ssd.SPLIT_KERNELS
         masks = [ssd.STAGES[k] for k in kernels] if staged else [0]
         for m in masks:
-            p = ssd.make_problem(b, T, H, P, N, G, 128, ssd.SSD_BF16, sf | m)
+            p = ssd.make_problem(b, T, H, P, N, G, Q, ssd.SSD_BF16, sf | m)
             ssd.scan_fwd_into(p, False, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], y, hT, ws)
         torch.cuda.synchronize()
         outs.append((y.float().cpu().numpy(), hT.cpu().numpy()))
