@@ -845,6 +845,18 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
     for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // C B^T fragments of a row tile (scalar decay): the first tile's are requested before
+    // the state term, each next tile's while the current one computes
+    const T* cbb_pf = cb + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
+    auto load_gf = [&](int k, v8* gf) {
+        const int rt = row_tile(k);
+        const int nks = rt / 2 + 1;
+        const T* cbrow = cbb_pf + (int64_t)(rt * 16 + l16) * Q;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbrow + (ks < nks ? ks : nks - 1) * 32 + 8 * q);
+    };
+    v8 gfa[8], gfb[8];
+    if (!DIAG) load_gf(0, gfa);
 
     // 2. scalar decay: state term y^T[p][i] += sum_n H[p][n] C[i][n] from raw fragments
     if (!DIAG) {
@@ -916,17 +928,14 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                 for (int pt = 0; pt < PT; ++pt) acc[k][pt] *= sc;
             }
         // 5. diagonal block
-        const T* cbb = cb + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (k < rpw) {
                 const int rt = row_tile(k);
                 const int i = rt * 16 + l16;
-                const T* cbrow = cbb + (int64_t)i * Q;
                 const int nks = rt / 2 + 1;  // k-steps of 32 tokens up to this row tile
-                v8 gf[8];
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbrow + (ks < nks ? ks : nks - 1) * 32 + 8 * q);
+                v8* gf = (k & 1) ? gfb : gfa;
+                if (k + 1 < rpw) load_gf(k + 1, (k & 1) ? gfa : gfb);
                 const float ci = cds[i];
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks) {
