@@ -68,6 +68,7 @@ def main():
                     help="untimed forwards first (about 40 ms at the default workload: the GPU clock settles)")
     ap.add_argument("--workload", default=None, help="workload name (default: the 2.7B layer shape)")
     ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--seqlen", type=int, default=None, help="override the workload's sequence length (scaling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--kernel-steps", type=int, default=None, help="launches per kernel timing")
     ap.add_argument("--schedule", choices=["auto", "split", "fused"], default="auto",
@@ -93,6 +94,8 @@ def main():
         w = {x.name: x for x in configs.WORKLOADS}[args.workload]
     if args.chunk:
         w = w.with_(chunk=args.chunk)
+    if args.seqlen:
+        w = w.with_(seqlen=args.seqlen, name=f"{w.name}_T{args.seqlen}")
     dev = torch.device("cuda:0")
     t0 = time.time()
     inp = make_inputs(w)
