@@ -4,18 +4,22 @@
 
 One step = one full forward (every kernel of the path) over the Mamba-2 2.7B layer
 shape (b8 T4096 H80 P64 N128 G1 Q256, bf16 x/B/C, fp32 dt/A/D/h0, nonzero h0), with
-seeded synthetic inputs already resident in HBM.  Prints one JSON line with
-tokens/s, TFLOP/s (causal flop count) against the bf16 matrix-core peak, the
-roofline of the dominant kernel (timed live with HIP events on the launch stream
-through the library's per-stage mask), per-kernel times, the decode step and the
-backward pass at the same shape, and the fp64 oracle timed on a bounded sample of the
-same workload on this host's cores.
+seeded synthetic inputs already resident in HBM.  After W untimed forwards, K forwards
+are timed one by one with HIP events on the launch stream, each after a 1 GiB scratch
+write that flushes the caches (cold: the headline `value`); K back-to-back forwards are
+timed the same way (warm, reported beside it).  The JSON line also carries the roofline
+of the dominant kernel (timed live inside a staged forward), its matrix-core rate, the
+HBM and matrix-core peaks measured on this GPU (a streaming copy and a dense matrix-core
+loop), per-kernel times, the other workloads timed briefly, the decode step and the
+backward pass at the same shape, and the fp64 oracle timed on this host's cores.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -26,7 +30,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, published
 FP32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix cores, published
-COPY_BYTES = 512 << 20      # size of the calibration copy (bytes read = bytes written)
+COPY_BYTES = 512 << 20      # size of the counter-calibration copy (bytes read = bytes written)
+FLUSH_BYTES = 1 << 30       # scratch written before each cold step (> the 256 MB last-level cache)
+PEAK_COPY_BYTES = 1 << 30   # streaming-copy measurement: bytes read (= bytes written)
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
     current kernel sources; else None."""
@@ -60,6 +68,116 @@ def cpu_baseline(w, inp, budget_s=12.0):
                       f"in {total:.2f} s; fp64 step-by-step recurrence, OpenMP over (batch, head, headdim block)"}
 
 
+def stats(ts):
+    """mean / median / min of per-step milliseconds."""
+    return {"mean_ms": round(sum(ts) / len(ts), 5), "median_ms": round(statistics.median(ts), 5),
+            "min_ms": round(min(ts), 5), "reps": len(ts)}
+
+
+def time_each(torch, stream, fn, reps, before=None):
+    """Per-step milliseconds: an event pair on `stream` around each call of fn; `before`
+    (untimed) runs ahead of each step."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        if before is not None:
+            before()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def measure_peaks(torch, stream, dev):
+    """HBM bandwidth of a plain streaming copy and the sustained bf16 matrix-core rate of a
+    dense loop of independent 16x16x32 steps, both on this GPU (median / best of 5)."""
+    from ssd_chunked_scan_03_amd import build
+    if not os.path.exists(build.PEAK_LIB):
+        return None
+    lib = ctypes.CDLL(build.PEAK_LIB)
+    lib.peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                              ctypes.c_void_p]
+    src = torch.ones(PEAK_COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def copy():
+        assert lib.peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), PEAK_COPY_BYTES, sp) == 0
+    copy()
+    ts = time_each(torch, stream, copy, 5)
+    copy_gbs = 2 * PEAK_COPY_BYTES / (statistics.median(ts) * 1e-3) / 1e9
+    assert torch.equal(dst[:1024], src[:1024])
+    del src, dst
+    blocks, iters = 256 * 8, 4000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    fl = ctypes.c_double(0.0)
+
+    def mfma():
+        assert lib.peak_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, ctypes.byref(fl), sp) == 0
+    mfma()
+    ts = time_each(torch, stream, mfma, 5)
+    mfma_tflops = fl.value / (min(ts) * 1e-3) / 1e12
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "bf16_mfma_TFLOPs": round(mfma_tflops, 1),
+            "copy": f"{PEAK_COPY_BYTES >> 20} MiB read + written by a 16-byte streaming copy kernel, median of 5",
+            "mfma": f"{blocks} work-groups x 4 waves x {iters} rounds of 8 independent 16x16x32 bf16 steps, best of 5"}
+
+
+def upload_inputs(torch, inp, dtype, dev):
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d = {k: torch.from_numpy(inp[k]).to(dev).to(td).contiguous() for k in ("x", "B", "C")}
+    for k in ("dt", "A", "D"):
+        d[k] = torch.from_numpy(inp[k]).to(dev)
+    d["h0"] = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).to(dev)
+    return d
+
+
+def other_workloads(torch, ssd, stream, dev, headline, reps=10):
+    """The remaining workloads (every chunk size of the long one), each timed briefly: 3
+    untimed forwards, then `reps` forwards one by one (warm), on the library's default
+    schedule."""
+    from ssd_chunked_scan_03_amd import configs, metrics
+    from ssd_chunked_scan_03_amd.synth import make_inputs
+    out = {}
+    for w0 in configs.WORKLOADS:
+        if w0.name == headline.name:
+            continue
+        chunks = configs.LONG_CHUNKS if w0.name == configs.LONG.name else (w0.chunk,)
+        inp = make_inputs(w0)
+        d = upload_inputs(torch, inp, w0.dtype, dev)
+        del inp
+        for Q in chunks:
+            w = w0.with_(chunk=Q)
+            b, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+            dcode = ssd.SSD_BF16 if w.dtype == "bf16" else ssd.SSD_F32
+            prob = ssd.make_problem(b, T, H, P, N, G, Q, dcode)
+            y = torch.empty_like(d["x"])
+            hT = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(ssd.workspace_bytes(prob, w.diag), 1), dtype=torch.uint8, device=dev)
+
+            def step():
+                ssd.scan_fwd_into(prob, w.diag, d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], y, hT, ws,
+                                  stream.cuda_stream)
+            for _ in range(3):
+                step()
+            torch.cuda.synchronize()
+            st = stats(time_each(torch, stream, step, reps))
+            ms = st["median_ms"]
+            es = 2 if w.dtype == "bf16" else 4
+            mb = metrics.path_min_bytes(b, T, H, P, N, G, es, d["h0"] is not None)
+            fl = metrics.flops(b, T, H, P, N, G, Q, w.diag)["total"]
+            key = w.name if len(chunks) == 1 else f"{w.name}_Q{Q}"
+            out[key] = {"ms_per_step": ms, "min_ms": st["min_ms"], "tokens_per_s": round(b * T / (ms * 1e-3), 1),
+                        "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "path_min_bytes": mb,
+                        "path_hbm_frac": round(mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "schedule": ssd.schedule_of(prob, w.diag), "chunk": Q, "dtype": w.dtype,
+                        "decay": "diagonal" if w.diag else "scalar"}
+            print(f"[bench] {key}: {ms:.4f} ms/step", file=sys.stderr, flush=True)
+            del y, hT, ws
+        del d
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -74,6 +192,8 @@ def main():
     ap.add_argument("--schedule", choices=["auto", "split", "fused"], default="auto",
                     help="kernel schedule (auto: the library's choice for the shape)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-workloads", action="store_true", help="skip timing the other workloads")
+    ap.add_argument("--no-peaks", action="store_true", help="skip measuring the copy and matrix-core peaks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed work, stream 512 MiB through a plain elementwise kernel "
                          "(calibrates the byte counters)")
@@ -83,7 +203,6 @@ def main():
               "the multi-GPU sharding is a design note, not an implementation", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import ssd_chunked_scan_03_amd as ssd
     from ssd_chunked_scan_03_amd import configs, metrics
@@ -99,21 +218,16 @@ def main():
     dev = torch.device("cuda:0")
     t0 = time.time()
     inp = make_inputs(w)
-    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    x = torch.from_numpy(inp["x"]).to(dev).to(td).contiguous()
-    B = torch.from_numpy(inp["B"]).to(dev).to(td).contiguous()
-    C = torch.from_numpy(inp["C"]).to(dev).to(td).contiguous()
-    dt = torch.from_numpy(inp["dt"]).to(dev)
-    A = torch.from_numpy(inp["A"]).to(dev)
-    D = torch.from_numpy(inp["D"]).to(dev)
-    h0 = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).to(dev)
+    d = upload_inputs(torch, inp, w.dtype, dev)
+    x, B, C, dt, A, D, h0 = d["x"], d["B"], d["C"], d["dt"], d["A"], d["D"], d["h0"]
     b, T, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     dcode = ssd.SSD_BF16 if w.dtype == "bf16" else ssd.SSD_F32
     sched_flag = {"auto": 0, "split": ssd.SCHEDULE_SPLIT, "fused": ssd.SCHEDULE_FUSED}[args.schedule]
     prob = ssd.make_problem(b, T, H, P, N, G, Q, dcode, flags=sched_flag)
     y = torch.empty_like(x)
     hT = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
-    ws = torch.empty(ssd.workspace_bytes(prob, w.diag), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ssd.workspace_bytes(prob, w.diag), 1), dtype=torch.uint8, device=dev)
+    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     print(f"[bench] {w.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
@@ -121,20 +235,25 @@ def main():
     def step(p=prob):
         ssd.scan_fwd_into(p, w.diag, x, dt, A, B, C, D, h0, y, hT, ws, stream.cuda_stream)
 
+    flushes = [0]
+
+    def flush():
+        flushes[0] += 1
+        flush_buf.fill_(float(flushes[0] & 7))  # 1 GiB written: no input or table stays cached
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    cold = time_each(torch, stream, step, args.steps, before=flush)
     wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] {args.steps} steps: {ms:.4f} ms/step (host wall {wall * 1e3 / args.steps:.4f})",
+    warm = time_each(torch, stream, step, args.steps)
+    cs, wsm = stats(cold), stats(warm)
+    ms = cs["mean_ms"]
+    print(f"[bench] {args.steps} steps: cold {ms:.4f} ms/step (median {cs['median_ms']:.4f}), "
+          f"warm {wsm['mean_ms']:.4f} (host wall {wall * 1e3 / args.steps:.4f} with the flushes)",
           file=sys.stderr, flush=True)
+    del flush_buf
 
     # per-kernel average launch duration, HIP events on the same stream: a staged forward
     # launches the forward's kernels in the forward's order, one stage per library call,
@@ -172,12 +291,28 @@ def main():
         for _ in range(3):
             torch.neg(src, out=dst)  # one streaming kernel: reads and writes COPY_BYTES
         torch.cuda.synchronize()
+        del src, dst
+
+    peaks = None if args.no_peaks else measure_peaks(torch, stream, dev)
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     dk = kernels[dom]
     traffic = measured_traffic(dom, w.name)
     roof = {"kernel": dom, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes": dk["bytes"], "avg_launch_ms": dk["ms"]}
+    if peaks:
+        roof["peak_measured"] = peaks["hbm_copy_GBps"]
+        roof["frac_measured"] = round(dk["GBps"] / peaks["hbm_copy_GBps"], 4)
+    # matrix-core rate of the fused kernel (the diagonal-block work runs inside it): the
+    # flops of the 16x16x32 steps it issues over its measured launch duration
+    mfma = None
+    if dom == "k_fused":
+        fl_issued = metrics.fused_mfma_flops(b, T, H, N, Q)
+        rate = fl_issued / (dk["ms"] * 1e-3) / 1e12
+        mfma = {"kernel": dom, "issued_gflop": round(fl_issued / 1e9, 2), "tflops": round(rate, 1),
+                "frac_spec": round(rate / BF16_PEAK_TFLOPS, 4)}
+        if peaks:
+            mfma["frac_measured"] = round(rate / peaks["bf16_mfma_TFLOPs"], 4)
 
     # one decode step (ssd_step, seqlen 1) at the same batch, heads and state size: the
     # state is read and written once, so it is timed against HBM bandwidth
@@ -186,12 +321,16 @@ def main():
     xs, dts, Bs, Cs = x[:, :1].contiguous(), dt[:, :1].contiguous(), B[:, :1].contiguous(), C[:, :1].contiguous()
     ys = torch.empty_like(xs)
     sprob = ssd.make_problem(b, 1, H, P, N, G, Q, dcode)
-    for _ in range(3):
+
+    def dstep():
         ssd.step_into(sprob, w.diag, xs, dts, A, Bs, Cs, D, hstate, ys, stream.cuda_stream)
+    for _ in range(3):
+        dstep()
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(ksteps):
-        ssd.step_into(sprob, w.diag, xs, dts, A, Bs, Cs, D, hstate, ys, stream.cuda_stream)
+        dstep()
     e1.record(stream)
     torch.cuda.synchronize()
     sms = e0.elapsed_time(e1) / ksteps
@@ -206,6 +345,7 @@ def main():
     if not args.no_bwd:
         print("[bench] timing the backward pass", file=sys.stderr, flush=True)
         gr = make_grads(b, T, H, P, N, w.seed, dtype=w.dtype)
+        td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         dy = torch.from_numpy(gr["dy"]).to(dev).to(td).contiguous()
         dhT = torch.from_numpy(gr["dhT"]).to(dev)
         bprob = ssd.make_problem(b, T, H, P, N, G, Q, dcode)
@@ -222,21 +362,22 @@ def main():
             bstep()
         torch.cuda.synchronize()
         bsteps = max(5, ksteps // 2)
-        e0.record(stream)
-        for _ in range(bsteps):
-            bstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        bms = e0.elapsed_time(e1) / bsteps
-        es_ = 2 if w.dtype == "bf16" else 4
-        bmin = metrics.bwd_path_min_bytes(b, T, H, P, N, G, es_, h0 is not None, True)
-        backward = {"ms": round(bms, 5), "tokens_per_s": round(b * T / (bms * 1e-3), 1), "steps": bsteps,
+        bst = stats(time_each(torch, stream, bstep, bsteps))
+        bms = bst["mean_ms"]
+        bmin = metrics.bwd_path_min_bytes(b, T, H, P, N, G, es, h0 is not None, True)
+        backward = {"ms": bms, "median_ms": bst["median_ms"], "min_ms": bst["min_ms"],
+                    "tokens_per_s": round(b * T / (bms * 1e-3), 1), "steps": bsteps,
                     "inputs": "x, dt, A, B, C, D, h0, dy, dhT (y is recomputed, not stored)",
                     "path_min_bytes": bmin,
                     "path_hbm_frac": round(bmin / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "workspace_bytes": int(bws.numel())}
         del bws, g, dy, dhT
         print(f"[bench] backward: {bms:.4f} ms", file=sys.stderr, flush=True)
+
+    workloads = None
+    if not args.no_workloads and not args.workload and not args.seqlen and not args.chunk:
+        print("[bench] timing the other workloads", file=sys.stderr, flush=True)
+        workloads = other_workloads(torch, ssd, stream, dev, w)
 
     fl = metrics.flops(b, T, H, P, N, G, Q, w.diag)
     tokens = b * T
@@ -259,16 +400,24 @@ def main():
         "config": {"workload": w.name, "batch": b, "seqlen": T, "nheads": H, "headdim": P, "dstate": N,
                    "ngroups": G, "chunk": Q, "decay": "diagonal" if w.diag else "scalar",
                    "h0": h0 is not None, "schedule": schedule},
+        "timing": {"cold": cs, "warm": wsm, "value_from": "cold mean",
+                   "cold_protocol": f"{FLUSH_BYTES >> 20} MiB scratch written before each timed step"},
+        "warm_tokens_per_s": round(tokens / (wsm["mean_ms"] * 1e-3), 1),
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak, 4),
         "path_min_bytes": min_bytes,
         "path_hbm_frac": round(min_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roof,
+        "mfma": mfma,
+        "peaks_measured": peaks,
         "kernels": kernels,
         "decode_step": decode,
         "backward": backward,
+        "workloads": workloads,
         "kernel_source_hash": metrics.kernel_source_hash(),
     }
+    if peaks:
+        out["path_hbm_frac_measured"] = round(min_bytes / (ms * 1e-3) / 1e9 / peaks["hbm_copy_GBps"], 4)
     if not args.no_cpu:
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp)

@@ -101,7 +101,10 @@ typedef struct {
  * Diagnostics only (per-kernel timing and per-stage inspection): a nonzero stage mask
  * in the low byte of `flags` enqueues just those kernels; their inputs are read from the
  * workspace, which a previous full call on the same problem, inputs and workspace must
- * have filled.  Any other bit is SSD_ERR_UNSUPPORTED. */
+ * have filled.  The mask may name only kernels of the schedule that runs (the workspace
+ * holds that schedule's regions only): cumsum, cb, bt and fused for the fused schedule;
+ * cumsum, cb, state, scan and out for the split one.  Any other bit is
+ * SSD_ERR_UNSUPPORTED. */
 #define SSD_STAGE_CUMSUM 0x01 /* chunk-local cumulative sum of dt      -> ws cdt     */
 #define SSD_STAGE_CB 0x02     /* C_c B_c^T per chunk (scalar decay)    -> ws cb      */
 #define SSD_STAGE_STATE 0x04  /* chunk states S_c                      -> ws states  */
@@ -114,8 +117,10 @@ typedef struct {
 #define SSD_SCHEDULE_FUSED 0x200
 
 /* Bytes of device workspace that ssd_scan_fwd (diag = 0) or ssd_diag_scan_fwd
- * (diag = 1) needs for this problem; 0 if the problem is invalid or empty.
- * Pure host function. */
+ * (diag = 1) needs for this problem; 0 if the problem is invalid or empty.  The size
+ * follows the schedule the problem runs (the schedule flags in p->flags and the shape;
+ * see the schedule notes): the fused schedule needs the per-chunk tables only, the
+ * split schedule also the chunk states and entering states.  Pure host function. */
 size_t ssd_workspace_bytes(const ssd_problem* p, int diag);
 
 /* Where each intermediate lives inside the workspace (byte offsets, each 256-aligned;
@@ -133,8 +138,8 @@ size_t ssd_workspace_bytes(const ssd_problem* p, int diag);
  *        when the split schedule's state scan runs as a parallel scan over segments
  *        (batch * nheads * headdim * dstate too small to fill the GPU; see the schedule
  *        notes); absent otherwise
- * The split schedule fills cdt, cb, states and hin (and carry); the fused one fills
- * cdt, cb and bt.
+ * Only the regions of the schedule that runs are present (the others have size 0): the
+ * split schedule has cdt, cb, states and hin (and carry); the fused one cdt, cb and bt.
  * Returns an ssd_status.  Pure host function. */
 typedef struct {
     size_t cdt_off, cdt_bytes;

@@ -186,22 +186,46 @@ def _dtype_code(t):
     raise TypeError(f"x/B/C must be bfloat16 or float32, got {t.dtype}")
 
 
+def _check_args(shapes, floats, same_dtype):
+    """Host-side checks of a call's tensors before anything is enqueued: every expected
+    shape (name -> (tensor or None, shape)), float32 where required, one shared dtype
+    (bfloat16 or float32) for x-like tensors, and contiguous tensors on one GPU.  The C ABI
+    sees only pointers and sizes, so a short or mistyped buffer would otherwise be read or
+    written out of bounds by the kernels."""
+    import torch
+    for name, (t, shape) in shapes.items():
+        if t is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    for name in floats:
+        t = shapes[name][0]
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+    first = shapes[same_dtype[0]][0]
+    _dtype_code(first)
+    for name in same_dtype[1:]:
+        if shapes[name][0].dtype != first.dtype:
+            raise TypeError(f"{', '.join(same_dtype)} must share one dtype")
+    dev = None
+    for name, (t, _) in shapes.items():
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
 def _forward(diag, x, dt, A, B, C, D, h0, chunk, return_final_state, ws):
     import torch
-    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D), ("h0", h0)):
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
-    if not (x.dtype == B.dtype == C.dtype):
-        raise TypeError("x, B and C must share one dtype")
-    for name, t in (("dt", dt), ("A", A), ("D", D), ("h0", h0)):
-        if t is not None and t.dtype != torch.float32:
-            raise TypeError(f"{name} must be float32")
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [b, T, H, P] and B [b, T, G, N]")
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    if B.shape != (b, T, G, N) or C.shape != B.shape or dt.shape != (b, T, H):
-        raise ValueError("shape mismatch among x, dt, B, C")
-    if A.shape != ((H, N) if diag else (H,)):
-        raise ValueError(f"A must be {'[H, N]' if diag else '[H]'}")
+    _check_args({"x": (x, (b, T, H, P)), "dt": (dt, (b, T, H)), "A": (A, (H, N) if diag else (H,)),
+                 "B": (B, (b, T, G, N)), "C": (C, (b, T, G, N)), "D": (D, (H,)), "h0": (h0, (b, H, P, N))},
+                floats=("dt", "A", "D", "h0"), same_dtype=("x", "B", "C"))
     prob = make_problem(b, T, H, P, N, G, chunk, _dtype_code(x))
     y = torch.empty_like(x)
     hT = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device) if return_final_state else None
@@ -247,19 +271,17 @@ def scan_fwd_varlen(x, dt, A, B, C, cu_seqlens, D=None, h0=None, chunk=256, retu
     (cu_seqlens: int32 GPU tensor of nseq + 1 offsets).  h0 / hT are [nseq, H, P, N].
     Returns (y, hT)."""
     import torch
-    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D), ("h0", h0),
-                    ("cu_seqlens", cu_seqlens)):
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
         raise TypeError("cu_seqlens must be a 1-D int32 tensor of nseq + 1 offsets")
-    if not (x.dtype == B.dtype == C.dtype):
-        raise TypeError("x, B and C must share one dtype")
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be [T, H, P] and B [T, G, N]")
     T, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
-    if B.shape != (T, G, N) or C.shape != B.shape or dt.shape != (T, H) or A.shape != (H,):
-        raise ValueError("shape mismatch among x [T,H,P], dt [T,H], A [H], B/C [T,G,N]")
     nseq = cu_seqlens.numel() - 1
+    _check_args({"x": (x, (T, H, P)), "dt": (dt, (T, H)), "A": (A, (H,)), "B": (B, (T, G, N)),
+                 "C": (C, (T, G, N)), "D": (D, (H,)), "h0": (h0, (nseq, H, P, N)),
+                 "cu_seqlens": (cu_seqlens, (nseq + 1,))},
+                floats=("dt", "A", "D", "h0"), same_dtype=("x", "B", "C"))
     prob = make_problem(nseq, T, H, P, N, G, chunk, _dtype_code(x))
     y = torch.empty_like(x)
     hT = torch.empty((nseq, H, P, N), dtype=torch.float32, device=x.device) if return_final_state else None
@@ -289,12 +311,19 @@ def step_into(prob: Problem, diag: bool, x, dt, A, B, C, D, h, y, stream=None) -
 def step(x, dt, A, B, C, h, D=None, diag=None):
     """Decode: run the recurrence over x's tokens on state h (updated in place).
     x [b, T, H, P] (bf16 or f32), dt [b, T, H] f32, A [H] or [H, N] f32, B/C [b, T, G, N],
-    h [b, H, P, N] f32.  Returns y [b, T, H, P]."""
+    h [b, H, P, N] f32, D [H] f32 or None.  Returns y [b, T, H, P]."""
     import torch
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [b, T, H, P] and B [b, T, G, N]")
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     if diag is None:
         diag = A.dim() == 2
+    if h is None:
+        raise ValueError("h (the state, updated in place) is required")
+    _check_args({"x": (x, (b, T, H, P)), "dt": (dt, (b, T, H)), "A": (A, (H, N) if diag else (H,)),
+                 "B": (B, (b, T, G, N)), "C": (C, (b, T, G, N)), "D": (D, (H,)), "h": (h, (b, H, P, N))},
+                floats=("dt", "A", "D", "h"), same_dtype=("x", "B", "C"))
     prob = make_problem(b, T, H, P, N, G, 64, _dtype_code(x))
     y = torch.empty_like(x)
     step_into(prob, diag, x, dt, A, B, C, D, h, y)
@@ -324,20 +353,14 @@ def scan_bwd_into(prob: Problem, x, dt, A, B, C, D, h0, dy, dhT, dx, ddt, dA, dB
 
 def _backward(diag, x, dt, A, B, C, dy, D, h0, dhT, chunk, workspace):
     import torch
-    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D), ("h0", h0), ("dy", dy),
-                    ("dhT", dhT)):
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
-    if not (x.dtype == B.dtype == C.dtype == dy.dtype):
-        raise TypeError("x, B, C and dy must share one dtype")
-    for name, t in (("dt", dt), ("A", A), ("D", D), ("h0", h0), ("dhT", dhT)):
-        if t is not None and t.dtype != torch.float32:
-            raise TypeError(f"{name} must be float32")
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [b, T, H, P] and B [b, T, G, N]")
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    if (B.shape != (b, T, G, N) or C.shape != B.shape or dt.shape != (b, T, H)
-            or A.shape != ((H, N) if diag else (H,)) or dy.shape != x.shape):
-        raise ValueError("shape mismatch among x, dt, A ([H] or [H, N] for diag), B, C, dy")
+    _check_args({"x": (x, (b, T, H, P)), "dt": (dt, (b, T, H)), "A": (A, (H, N) if diag else (H,)),
+                 "B": (B, (b, T, G, N)), "C": (C, (b, T, G, N)), "dy": (dy, (b, T, H, P)), "D": (D, (H,)),
+                 "h0": (h0, (b, H, P, N)), "dhT": (dhT, (b, H, P, N))},
+                floats=("dt", "A", "D", "h0", "dhT"), same_dtype=("x", "B", "C", "dy"))
     prob = make_problem(b, T, H, P, N, G, chunk, _dtype_code(x))
     dev = x.device
     out = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dA=torch.empty_like(A), dB=torch.empty_like(B),

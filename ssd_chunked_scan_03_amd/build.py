@@ -18,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssd.so")
+PEAK_SRC = os.path.join(PKG, "peak", "peak.hip")
+PEAK_LIB = os.path.join(PKG, "libssd_peak.so")  # measurement kernels for the benchmark only
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -52,6 +54,12 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-8000:]}")
     os.replace(tmp, LIB)
+    # the benchmark's measured denominators (streaming copy, matrix-core loop)
+    tmp = PEAK_LIB + ".tmp"
+    r = subprocess.run([HIPCC, *CFLAGS, "-shared", PEAK_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PEAK_SRC}:\n{r.stderr[-8000:]}")
+    os.replace(tmp, PEAK_LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} units in {time.time() - t0:.1f}s")
     return LIB

@@ -55,9 +55,27 @@ int check_problem(const ssd_problem* p) {
     return SSD_OK;
 }
 
+// Whether a forward of this problem runs the fused schedule (the launch code takes the
+// same decision from the same fields).
+bool runs_fused(const ssd_problem* p, int diag) {
+    ssd::RunArgs a = {};
+    a.b = p->batch; a.T = p->seqlen; a.H = p->nheads; a.P = p->headdim; a.N = p->dstate;
+    a.G = p->ngroups; a.Q = p->chunk;
+    a.nc = (p->seqlen + p->chunk - 1) / p->chunk;
+    a.diag = diag;
+    a.ts = nullptr;
+    a.force_split = (p->flags & SSD_SCHEDULE_SPLIT) != 0;
+    a.force_fused = (p->flags & SSD_SCHEDULE_FUSED) != 0;
+    return ssd::fused_applies(a, p->dtype == SSD_BF16);
+}
+
+// The regions of the schedule that runs: cdt and (scalar decay) cb always; bt for the
+// fused schedule; chunk states, entering states and the segmented scan's carry for the
+// split one.  A region the schedule never touches takes no bytes.
 ssd_workspace_layout layout_of(const ssd_problem* p, int diag) {
     ssd_workspace_layout L;
     memset(&L, 0, sizeof(L));
+    const bool fused = runs_fused(p, diag);
     const int64_t nc = (p->seqlen + p->chunk - 1) / p->chunk;
     const size_t bhc = (size_t)(p->batch * p->nheads * nc);
     const size_t es = esize(p->dtype);
@@ -69,20 +87,21 @@ ssd_workspace_layout layout_of(const ssd_problem* p, int diag) {
     L.cb_bytes = diag ? 0 : (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->chunk * p->chunk) * es;
     off += align_up(L.cb_bytes);
     L.states_off = off;
-    L.states_bytes = bhc * (size_t)(p->headdim * p->dstate) * 4;
+    L.states_bytes = fused ? 0 : bhc * (size_t)(p->headdim * p->dstate) * 4;
     off += align_up(L.states_bytes);
     L.hin_off = off;
-    L.hin_bytes = bhc * (size_t)(p->headdim * p->dstate) * es;
+    L.hin_bytes = fused ? 0 : bhc * (size_t)(p->headdim * p->dstate) * es;
     off += align_up(L.hin_bytes);
     L.bt_off = off;
-    L.bt_bytes = diag ? 0 : (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->dstate * p->chunk) * es;
+    L.bt_bytes = (diag || !fused) ? 0 : (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->dstate * p->chunk) * es;
     off += align_up(L.bt_bytes);
     // the split schedule's state scan in segments (few state elements, many chunks)
     const int64_t sl = ssd::scan_segment_len(p->batch, p->nheads, p->headdim, p->dstate, nc);
     const int64_t nseg = nc > 0 ? (nc + sl - 1) / sl : 0;
     L.carry_off = off;
-    L.carry_bytes = nseg > 1 ? (size_t)nseg * (size_t)(p->batch * p->nheads) * (size_t)(p->headdim * p->dstate + 1) * 4
-                             : 0;
+    L.carry_bytes = (!fused && nseg > 1)
+                        ? (size_t)nseg * (size_t)(p->batch * p->nheads) * (size_t)(p->headdim * p->dstate + 1) * 4
+                        : 0;
     off += align_up(L.carry_bytes);
     L.total_bytes = (p->batch == 0 || p->seqlen == 0) ? 0 : off;
     return L;
@@ -151,9 +170,9 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     char* w = static_cast<char*>(ws);
     a.cdt = reinterpret_cast<float*>(w + L.cdt_off);
     a.cb = diag ? nullptr : static_cast<void*>(w + L.cb_off);
-    a.states = reinterpret_cast<float*>(w + L.states_off);
-    a.hin = static_cast<void*>(w + L.hin_off);
-    a.bt = diag ? nullptr : static_cast<void*>(w + L.bt_off);
+    a.states = L.states_bytes ? reinterpret_cast<float*>(w + L.states_off) : nullptr;
+    a.hin = L.hin_bytes ? static_cast<void*>(w + L.hin_off) : nullptr;
+    a.bt = L.bt_bytes ? static_cast<void*>(w + L.bt_off) : nullptr;
     a.carry = L.carry_bytes ? reinterpret_cast<float*>(w + L.carry_off) : nullptr;
     a.ts = nullptr; a.kb = nullptr; a.kcap = 0;
     a.stream = (hipStream_t)stream;

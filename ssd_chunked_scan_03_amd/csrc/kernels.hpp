@@ -845,8 +845,12 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
     for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // C B^T fragments of a row tile (scalar decay): the first tile's are requested before
-    // the state term, each next tile's while the current one computes
+    // C B^T fragments of a row tile (scalar decay).  bfloat16: the first tile's are
+    // requested before the state term, each next tile's while the current one computes.
+    // float32 fragments take twice the registers, so there each tile's are requested
+    // just before its own k-steps (a second set would cost occupancy and spill at
+    // headdim 128).
+    constexpr bool PF = sizeof(T) == 2;
     const T* cbb_pf = cb + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
     auto load_gf = [&](int k, v8* gf) {
         const int rt = row_tile(k);
@@ -855,8 +859,8 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbrow + (ks < nks ? ks : nks - 1) * 32 + 8 * q);
     };
-    v8 gfa[8], gfb[8];
-    if (!DIAG) load_gf(0, gfa);
+    v8 gfa[8], gfb[PF ? 8 : 1];
+    if (!DIAG && PF) load_gf(0, gfa);
 
     // 2. scalar decay: state term y^T[p][i] += sum_n H[p][n] C[i][n] from raw fragments
     if (!DIAG) {
@@ -934,8 +938,13 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                 const int rt = row_tile(k);
                 const int i = rt * 16 + l16;
                 const int nks = rt / 2 + 1;  // k-steps of 32 tokens up to this row tile
-                v8* gf = (k & 1) ? gfb : gfa;
-                if (k + 1 < rpw) load_gf(k + 1, (k & 1) ? gfa : gfb);
+                v8* gf = gfa;
+                if constexpr (PF) {
+                    gf = (k & 1) ? gfb : gfa;
+                    if (k + 1 < rpw) load_gf(k + 1, (k & 1) ? gfa : gfb);
+                } else {
+                    load_gf(k, gfa);
+                }
                 const float ci = cds[i];
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks) {

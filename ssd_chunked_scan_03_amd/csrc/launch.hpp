@@ -94,7 +94,11 @@ int run(const RunArgs& a) {
     if (a.force_fused && !fused_supported(a, kBF16)) return 3;
     const bool fused = fused_applies(a, kBF16);
     if (a.ts && (!fused || a.force_split)) return 3;  // packed rows: fused schedule only
-    int st = a.stages ? a.stages : (fused ? (1 | 2 | 32 | 64) : (1 | 2 | 4 | 8 | 16));
+    // a stage mask may name only kernels of the schedule that runs: the workspace holds
+    // that schedule's regions only
+    const int sched_bits = fused ? (1 | 2 | 32 | 64) : (1 | 2 | 4 | 8 | 16);
+    if (a.stages & ~sched_bits) return 3;
+    int st = a.stages ? a.stages : sched_bits;
     const int Q = (int)a.Q, nc = (int)a.nc, H = (int)a.H, G = (int)a.G;
     hipStream_t s = a.stream;
     const T* x = static_cast<const T*>(a.x);

@@ -102,6 +102,20 @@ def bwd_kernel_bytes(b, T, H, P, N, G, Q, es, h0=True, dhT=True) -> dict:
     }
 
 
+def fused_mfma_flops(b, T, H, N, Q) -> int:
+    """Matrix-core flops the fused kernel issues (whole 16x16x32 bf16 steps, headdim 64):
+    per chunk of one (batch, head), the output passes take sum_t (floor(t/2) + 1) C B^T
+    fragments over the Q/16 row tiles t, each times 4 column tiles of x; the state term
+    (Q/16) (N/32) 4 steps; the state update (Q/32) (N/16) 4 steps.  Ragged chunks issue
+    whole tiles too."""
+    nc = -(-T // Q)
+    rt = Q // 16
+    diag = sum(t // 2 + 1 for t in range(rt)) * 4
+    state_term = rt * (N // 32) * 4
+    state_update = (Q // 32) * (N // 16) * 4
+    return b * H * nc * (diag + state_term + state_update) * 2 * 16 * 16 * 32
+
+
 KERNEL_SOURCES = ("kernels.hpp", "device.hpp", "fused.hpp", "launch.hpp")
 
 

@@ -40,22 +40,46 @@ def prob(b=2, T=300, H=4, P=64, N=128, G=2, Q=128, dtype=ssd.SSD_BF16):
 
 
 def test_workspace_layout_arithmetic():
-    p = prob()
+    """The workspace holds the regions of the schedule that runs: cdt and C B^T always
+    (C B^T for the scalar decay only), B^T for the fused schedule, chunk states and
+    entering states for the split one."""
     nc = 3
-    for diag in (False, True):
-        lay = ssd.workspace_layout(p, diag)
-        assert lay["cdt_bytes"] == 2 * 4 * nc * 128 * 4
-        assert lay["cb_bytes"] == (0 if diag else 2 * nc * 2 * 128 * 128 * 2)
-        assert lay["states_bytes"] == 2 * 4 * nc * 64 * 128 * 4
-        assert lay["hin_bytes"] == 2 * 4 * nc * 64 * 128 * 2
-        assert lay["bt_bytes"] == (0 if diag else 2 * nc * 2 * 128 * 128 * 2)
-        assert lay["carry_bytes"] == 0  # 2 x 4 x 64 x 128 / 4 threads is not "few", and nc < 8
-        offs = [lay[k] for k in ("cdt_off", "cb_off", "states_off", "hin_off", "bt_off", "carry_off")]
-        assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
-        assert lay["total_bytes"] >= lay["bt_off"] + lay["bt_bytes"]
-        assert ssd.workspace_bytes(p, diag) == lay["total_bytes"]
+    for flags in (0, ssd.SCHEDULE_SPLIT, ssd.SCHEDULE_FUSED):
+        p = ssd.make_problem(2, 300, 4, 64, 128, 2, 128, ssd.SSD_BF16, flags)
+        for diag in (False, True):
+            fused = flags == ssd.SCHEDULE_FUSED and not diag  # 8 (batch, head) chains: split by default
+            if flags == ssd.SCHEDULE_FUSED and diag:
+                continue  # no fused diagonal-decay kernel
+            lay = ssd.workspace_layout(p, diag)
+            assert lay["cdt_bytes"] == 2 * 4 * nc * 128 * 4
+            assert lay["cb_bytes"] == (0 if diag else 2 * nc * 2 * 128 * 128 * 2)
+            assert lay["states_bytes"] == (0 if fused else 2 * 4 * nc * 64 * 128 * 4)
+            assert lay["hin_bytes"] == (0 if fused else 2 * 4 * nc * 64 * 128 * 2)
+            assert lay["bt_bytes"] == (2 * nc * 2 * 128 * 128 * 2 if fused else 0)
+            assert lay["carry_bytes"] == 0  # 2 x 4 x 64 x 128 / 4 threads is not "few", and nc < 8
+            offs = [lay[k] for k in ("cdt_off", "cb_off", "states_off", "hin_off", "bt_off", "carry_off")]
+            assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+            assert lay["total_bytes"] >= lay["bt_off"] + lay["bt_bytes"]
+            assert ssd.workspace_bytes(p, diag) == lay["total_bytes"]
     assert ssd.workspace_bytes(prob(T=0)) == 0
     assert ssd.workspace_bytes(prob(b=0)) == 0
+
+
+def test_workspace_follows_the_schedule_at_the_layer_shape():
+    """The 2.7B layer shape (b8 T4096 H80 P64 N128 G1 Q256, bf16) runs the fused schedule
+    by default: its workspace is cdt + C B^T + B^T (about 36 MB), none of the split
+    schedule's 503 MB of chunk states and entering states."""
+    b, T, H, P, N, G, Q = 8, 4096, 80, 64, 128, 1, 256
+    nc = T // Q
+    cdt, cb, bt = b * H * nc * Q * 4, b * nc * G * Q * Q * 2, b * nc * G * N * Q * 2
+    fused = ssd.workspace_layout(ssd.make_problem(b, T, H, P, N, G, Q, ssd.SSD_BF16))
+    assert (fused["cdt_bytes"], fused["cb_bytes"], fused["bt_bytes"]) == (cdt, cb, bt)
+    assert fused["states_bytes"] == fused["hin_bytes"] == fused["carry_bytes"] == 0
+    assert fused["total_bytes"] == cdt + cb + bt == 35_651_584
+    split = ssd.workspace_layout(ssd.make_problem(b, T, H, P, N, G, Q, ssd.SSD_BF16, ssd.SCHEDULE_SPLIT))
+    assert split["bt_bytes"] == 0
+    assert split["states_bytes"] == b * H * nc * P * N * 4 and split["hin_bytes"] == b * H * nc * P * N * 2
+    assert split["total_bytes"] == cdt + cb + split["states_bytes"] + split["hin_bytes"]
 
 
 def test_segmented_state_scan_workspace():
@@ -66,7 +90,7 @@ def test_segmented_state_scan_workspace():
     p = ssd.make_problem(1, 16384, 4, 64, 64, 1, 64, ssd.SSD_BF16)
     lay = ssd.workspace_layout(p)
     assert lay["carry_bytes"] == 32 * 4 * (64 * 64 + 1) * 4
-    assert lay["carry_off"] >= lay["bt_off"] + lay["bt_bytes"]
+    assert lay["bt_bytes"] == 0 and lay["carry_off"] >= lay["hin_off"] + lay["hin_bytes"]
     assert lay["total_bytes"] >= lay["carry_off"] + lay["carry_bytes"]
     # segments need at least 4 chunks each: 40 chunks allow 10
     p = ssd.make_problem(1, 40 * 64, 4, 64, 64, 1, 64, ssd.SSD_BF16)
@@ -158,6 +182,21 @@ def test_schedule_flags_validated():
     p = prob(dtype=ssd.SSD_F32)
     p.flags = ssd.SCHEDULE_FUSED
     assert call(p)[0] == ssd_status("SSD_ERR_UNSUPPORTED")
+
+
+def test_stage_mask_must_name_kernels_of_the_running_schedule():
+    """The workspace holds only the running schedule's regions, so a stage mask naming a
+    kernel of the other schedule is refused before any launch."""
+    p = prob(b=8, H=80, N=128, G=1)                   # fused by default
+    for m in (ssd.STAGE_STATE, ssd.STAGE_SCAN, ssd.STAGE_OUT, ssd.STAGE_CUMSUM | ssd.STAGE_STATE):
+        p.flags = m
+        assert call(p)[0] == ssd_status("SSD_ERR_UNSUPPORTED"), m
+    q = prob()                                       # split by default
+    for m in (ssd.STAGE_BT, ssd.STAGE_FUSED):
+        q.flags = m
+        assert call(q)[0] == ssd_status("SSD_ERR_UNSUPPORTED"), m
+        q.flags = m | ssd.SCHEDULE_SPLIT
+        assert call(q)[0] == ssd_status("SSD_ERR_UNSUPPORTED"), m
 
 
 def test_schedule_choice():

@@ -3,13 +3,13 @@
 
 Every gradient is compared slice by slice with the metric of the forward tests: per
 (batch, head) for dx, ddt and dh0, per (batch, group) for dB and dC, and over the whole
-vector for dD, ||got - ref||_inf / ||ref||_inf against 1e-4 (float32 problems) or 2e-2
-(bfloat16).  dA_h = sum_{b,t} dt dl (dl = ddt / A_h) is a sum over every token with
-strong cancellation (sum |dt dl| is up to 10^3 times |dA| here), so its tolerance is
-derived from ddt's: if every slice of dl is within tol of its largest entry, then
-|dA_gpu - dA_ref|_h <= tol * sum_b max_t |dl| * sum_t |dt|, and that bound is the gate;
-the GPU's dA must also equal the reduction of its own ddt (float32 summation order
-only).  Outputs and workspace are NaN-poisoned before each call."""
+vector for dD and dA, ||got - ref||_inf / ||ref||_inf against 1e-4 (float32 problems) or
+2e-2 (bfloat16).  dA_h = sum_{b,t} dt dl (dl = ddt / A_h) is a sum over every token with
+strong cancellation (sum |dt dl| is up to 10^3 times |dA| here); besides its direct
+relative error, two extra checks are reported and gated: the bound that ddt's gate implies,
+|dA_gpu - dA_ref|_h <= tol * sum_b max_t |dl| * sum_t |dt|, and that the GPU's dA equals
+the reduction of its own ddt (float32 summation order only).  Outputs and workspace are
+NaN-poisoned before each call."""
 import numpy as np
 import pytest
 import torch
@@ -66,12 +66,14 @@ def errors(got, ref):
     e = {}
     for k, axes in SLICES.items():
         e[k] = vec_rel(got[k], ref[k]) if not axes else max_rel_err(got[k], ref[k], axes)
+    # dA directly: max-norm relative error over the heads
+    e["dA"] = vec_rel(got["dA"], ref["dA"])
     # dA against the bound that ddt's gate implies, per head
     dt, A = ref["_dt"], ref["_A"]
     dl = ref["ddt"] / A[None, None, :]
     bound = np.sum(np.abs(dl).max(axis=1) * np.abs(dt).sum(axis=1), axis=0)     # sum_b max_t|dl| sum_t|dt|
     err = np.abs(np.asarray(got["dA"], np.float64) - ref["dA"])
-    e["dA"] = float(np.max(np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), err))) \
+    e["dA_bound"] = float(np.max(np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), err))) \
         if not np.isnan(got["dA"]).any() else float("inf")
     # the GPU's dA is the reduction of its own ddt (float32 sums on the GPU)
     terms = np.sum(np.abs(dt * dl), axis=(0, 1))
@@ -184,44 +186,14 @@ def test_bwd_python_api_matches_into():
         np.testing.assert_array_equal(out[k].float().cpu().numpy(), got[k], err_msg=k)
 
 
-def test_bwd_headline_shape_sampled():
+def test_bwd_headline_shape_full():
     """The 2.7B layer shape at full size (b8 T4096 H80 P64 N128 G1 Q256, nonzero h0), as
-    bench.py times it.  Per-head gradients (dx, ddt, dh0) of sampled (batch, head) pairs
-    against the oracle on that head alone; dB and dC of one batch row (a sum over its 80
-    heads) against the oracle on that row; dD against sum dy.x in float64; dA against the
-    reduction of the GPU's own ddt."""
+    bench.py times it: every gradient of the whole workload against the oracle's, with the
+    per-slice metric (dA and dD over the whole vector)."""
     from ssd_chunked_scan_03_amd.configs import M2P7B
     from ssd_chunked_scan_03_amd.synth import make_inputs
     w = M2P7B
     inp = make_inputs(w)
     gr = make_grads(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.seed, dtype=w.dtype)
-    d = upload(inp, "bf16")
-    dy = torch.from_numpy(gr["dy"]).to("cuda").to(torch.bfloat16)
-    dhT = torch.from_numpy(gr["dhT"]).to("cuda")
-    out = ssd.scan_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], dy, D=d["D"], h0=d["h0"], dhT=dhT, chunk=w.chunk)
-    torch.cuda.synchronize()
-    got = {k: v.float().cpu().numpy() for k, v in out.items()}
-    tol = TOL["bf16"]
-    for bi, h in ((0, 0), (3, 41), (7, 79)):
-        sl = lambda a: a[bi:bi + 1, :, h:h + 1]
-        ref = oracle.recurrence_bwd(sl(inp["x"]), sl(inp["dt"]), inp["A"][h:h + 1], inp["B"][bi:bi + 1],
-                                    inp["C"][bi:bi + 1], inp["D"][h:h + 1], inp["h0"][bi:bi + 1, h:h + 1],
-                                    dy=sl(gr["dy"]), dhT=gr["dhT"][bi:bi + 1, h:h + 1])
-        e = {"dx": max_rel_err(sl(got["dx"]), ref["dx"], (0, 2)),
-             "ddt": max_rel_err(got["ddt"][bi:bi + 1, :, h:h + 1], ref["ddt"], (0, 2)),
-             "dh0": max_rel_err(got["dh0"][bi:bi + 1, h:h + 1], ref["dh0"], (0, 1))}
-        print(f"[bwd headline b{bi} h{h}] " + " ".join(f"{k}={v:.2e}" for k, v in e.items()), flush=True)
-        assert all(v < tol for v in e.values()), (bi, h, e)
-    bi = 5
-    row = lambda a: a[bi:bi + 1]
-    ref = oracle.recurrence_bwd(row(inp["x"]), row(inp["dt"]), inp["A"], row(inp["B"]), row(inp["C"]), inp["D"],
-                                row(inp["h0"]), dy=row(gr["dy"]), dhT=row(gr["dhT"]))
-    e = {"dB": max_rel_err(row(got["dB"]), ref["dB"], (0, 2)), "dC": max_rel_err(row(got["dC"]), ref["dC"], (0, 2))}
-    print(f"[bwd headline row {bi}] " + " ".join(f"{k}={v:.2e}" for k, v in e.items()), flush=True)
-    assert all(v < tol for v in e.values()), e
-    dD = np.einsum("bthp,bthp->h", np.asarray(gr["dy"], np.float64), np.asarray(inp["x"], np.float64))
-    assert vec_rel(got["dD"], dD) < 1e-4
-    own = np.sum(np.asarray(inp["dt"], np.float64) * got["ddt"].astype(np.float64) / inp["A"][None, None, :],
-                 axis=(0, 1))
-    terms = np.sum(np.abs(np.asarray(inp["dt"], np.float64) * got["ddt"] / inp["A"][None, None, :]), axis=(0, 1))
-    assert np.max(np.abs(own - got["dA"]) / terms) < 1e-4
+    got, ref = run_bwd(inp, gr, "bf16", w.chunk)
+    check(got, ref, "bf16", w.name)

@@ -1,5 +1,6 @@
-"""Machine-code checks of the fused kernel, on the CPU: hipcc cross-compiles every fused
-instantiation for gfx950 to assembly, and the assembly is checked for
+"""Machine-code checks on the CPU: hipcc cross-compiles every fused instantiation, and
+the two forward units (every output, chunk-state and preparation kernel of both dtypes),
+for gfx950 to assembly, and the assembly is checked for
 
 - register spills: a spilled value reloaded after long-latency loads waits for all of
   them (the vector-memory counter is in order), so the kernel is kept spill-free;
@@ -87,3 +88,44 @@ def test_fused_kernels_do_not_spill(fused_asm):
 def test_fused_wide_stores_are_fenced(fused_asm):
     assert re.search(r"buffer_store_dwordx4", fused_asm), "the fused kernels store y with 16-byte stores"
     assert exposed_wide_stores(fused_asm) == []
+
+
+@pytest.fixture(scope="module")
+def forward_units_asm(tmp_path_factory):
+    """The forward instantiation units compiled to gfx950 assembly, both at once."""
+    if _hipcc() is None:
+        pytest.skip("hipcc not available")
+    d = tmp_path_factory.mktemp("isa_units")
+    procs = []
+    for unit in ("inst_bf16.hip", "inst_f32.hip"):
+        out = d / (unit + ".s")
+        cmd = [build.HIPCC, *build.CFLAGS, "--cuda-device-only", "-S", os.path.join(build.CSRC, unit), "-o", str(out)]
+        procs.append((unit, out, subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True)))
+    texts = {}
+    for unit, out, p in procs:
+        _, err = p.communicate()
+        assert p.returncode == 0, err[-4000:]
+        texts[unit] = out.read_text()
+    return texts
+
+
+def kernel_spills(asm, prefix):
+    """(mangled kernel name, vgpr spill count) of every kernel whose name holds prefix."""
+    out = []
+    for blk in re.split(r"\n\s*- \.", asm):
+        name = re.search(r"\.name:\s+(\S+)", blk)
+        spill = re.search(r"\.vgpr_spill_count:\s+(\d+)", blk)
+        if name and spill and prefix in name.group(1) and not name.group(1).endswith(".kd"):
+            out.append((name.group(1), int(spill.group(1))))
+    return out
+
+
+@pytest.mark.parametrize("kernel", ["k_out", "k_state", "k_prep", "k_scan"])
+def test_forward_kernels_do_not_spill(forward_units_asm, kernel):
+    """Every (dtype, headdim, dstate) instantiation of the split schedule's kernels is
+    spill-free (float32 output tiles at headdim 128 are the tightest)."""
+    found = []
+    for unit, asm in forward_units_asm.items():
+        found += [(unit, n, s) for n, s in kernel_spills(asm, kernel)]
+    assert len(found) >= (12 if kernel == "k_scan" else 20), found
+    assert all(s == 0 for _, _, s in found), [f for f in found if f[2]]
