@@ -6,7 +6,7 @@ One step = one full forward (every kernel of the path) over the Mamba-2 2.7B lay
 shape (b8 T4096 H80 P64 N128 G1 Q256, bf16 x/B/C, fp32 dt/A/D/h0, nonzero h0), with
 seeded synthetic inputs already resident in HBM.  After W untimed forwards, K forwards
 are timed one by one with HIP events on the launch stream, each after a 1 GiB scratch
-write that flushes the caches (cold: the headline `value`); K back-to-back forwards are
+read that flushes the caches (cold: the headline `value`); K back-to-back forwards are
 timed the same way (warm, reported beside it).  The JSON line also carries the roofline
 of the dominant kernel (timed live inside a staged forward), its matrix-core rate, the
 HBM and matrix-core peaks measured on this GPU (a streaming copy and a dense matrix-core
@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, published
 FP32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix cores, published
 COPY_BYTES = 512 << 20      # size of the counter-calibration copy (bytes read = bytes written)
-FLUSH_BYTES = 1 << 30       # scratch written before each cold step (> the 256 MB last-level cache)
+FLUSH_BYTES = 1 << 30       # scratch read before each cold step (> the 256 MB last-level cache)
 PEAK_COPY_BYTES = 1 << 30   # streaming-copy measurement: bytes read (= bytes written)
 
 
@@ -89,24 +89,30 @@ def time_each(torch, stream, fn, reps, before=None):
 
 
 def measure_peaks(torch, stream, dev):
-    """HBM bandwidth of a plain streaming copy and the sustained bf16 matrix-core rate of a
-    dense loop of independent 16x16x32 steps, both on this GPU (median / best of 5)."""
+    """HBM bandwidth of a plain streaming copy (the best of a few grid sizes and cache
+    policies, median of 5 each) and the sustained bf16 matrix-core rate of a dense loop of
+    independent 16x16x32 steps (best of 5), both on this GPU."""
     from ssd_chunked_scan_03_amd import build
     if not os.path.exists(build.PEAK_LIB):
         return None
     lib = ctypes.CDLL(build.PEAK_LIB)
-    lib.peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_void_p]
     lib.peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                               ctypes.c_void_p]
     src = torch.ones(PEAK_COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     sp = ctypes.c_void_p(stream.cuda_stream)
-
-    def copy():
-        assert lib.peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), PEAK_COPY_BYTES, sp) == 0
-    copy()
-    ts = time_each(torch, stream, copy, 5)
-    copy_gbs = 2 * PEAK_COPY_BYTES / (statistics.median(ts) * 1e-3) / 1e9
+    best, how = 0.0, ""
+    for blocks in (1024, 2048, 4096, 8192):
+        for nt in (1, 0):
+            def copy():
+                assert lib.peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                     PEAK_COPY_BYTES, blocks, nt, sp) == 0
+            copy()
+            gbs = 2 * PEAK_COPY_BYTES / (statistics.median(time_each(torch, stream, copy, 5)) * 1e-3) / 1e9
+            if gbs > best:
+                best, how = gbs, f"{blocks} work-groups, {'non-temporal' if nt else 'default'} accesses"
     assert torch.equal(dst[:1024], src[:1024])
     del src, dst
     blocks, iters = 256 * 8, 4000
@@ -118,8 +124,9 @@ def measure_peaks(torch, stream, dev):
     mfma()
     ts = time_each(torch, stream, mfma, 5)
     mfma_tflops = fl.value / (min(ts) * 1e-3) / 1e12
-    return {"hbm_copy_GBps": round(copy_gbs, 1), "bf16_mfma_TFLOPs": round(mfma_tflops, 1),
-            "copy": f"{PEAK_COPY_BYTES >> 20} MiB read + written by a 16-byte streaming copy kernel, median of 5",
+    return {"hbm_copy_GBps": round(best, 1), "bf16_mfma_TFLOPs": round(mfma_tflops, 1),
+            "copy": f"{PEAK_COPY_BYTES >> 20} MiB read + written by a streaming copy kernel (four 16-byte loads "
+                    f"in flight per thread); best setting: {how}; median of 5",
             "mfma": f"{blocks} work-groups x 4 waves x {iters} rounds of 8 independent 16x16x32 bf16 steps, best of 5"}
 
 
@@ -227,7 +234,7 @@ def main():
     y = torch.empty_like(x)
     hT = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
     ws = torch.empty(max(ssd.workspace_bytes(prob, w.diag), 1), dtype=torch.uint8, device=dev)
-    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     print(f"[bench] {w.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
@@ -235,11 +242,10 @@ def main():
     def step(p=prob):
         ssd.scan_fwd_into(p, w.diag, x, dt, A, B, C, D, h0, y, hT, ws, stream.cuda_stream)
 
-    flushes = [0]
-
     def flush():
-        flushes[0] += 1
-        flush_buf.fill_(float(flushes[0] & 7))  # 1 GiB written: no input or table stays cached
+        # 1 GiB read: no input or table of the previous step stays cached.  A read leaves
+        # clean lines; a write would leave dirty ones that the timed step then writes back.
+        flush_buf.sum()
 
     for _ in range(args.warmup):
         step()
@@ -401,7 +407,7 @@ def main():
                    "ngroups": G, "chunk": Q, "decay": "diagonal" if w.diag else "scalar",
                    "h0": h0 is not None, "schedule": schedule},
         "timing": {"cold": cs, "warm": wsm, "value_from": "cold mean",
-                   "cold_protocol": f"{FLUSH_BYTES >> 20} MiB scratch written before each timed step"},
+                   "cold_protocol": f"{FLUSH_BYTES >> 20} MiB scratch read before each timed step"},
         "warm_tokens_per_s": round(tokens / (wsm["mean_ms"] * 1e-3), 1),
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak, 4),

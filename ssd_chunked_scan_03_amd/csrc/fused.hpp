@@ -234,10 +234,18 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
     // tables of a chunk from its cdt row (in cdq) and its entering state -> Hs; runs after
     // the previous chunk's closing barrier and before the chunk's x transfer is issued
     float dch = 1.f;
+    int split_diag = 1;  // the chunk's diagonal blocks take the two-factor decay (see below)
     auto stage_tables = [&]() {
             const int ln = lane_now(), tl = w * 64 + ln, lr = ln & 15, lq = ln >> 4;
             const float cl = cdq[Q - 1];
             dch = exp2f_fast(ah2 * cl);  // decay over the whole chunk
+            // widest decay across one 32-row block of this chunk (base 2): within 2^64 the
+            // diagonal blocks split exp(A (cdt_i - cdt_j)) into u2_j * v_i like the blocks
+            // below them (v_i >= 1 there, u2_j >= 2^-64: both far inside float32 range)
+            float span = 0.f;
+#pragma unroll
+            for (int b = 0; b < Q / 32; ++b) span = fmaxf(span, cdq[32 * b + 31] - cdq[32 * b]);
+            split_diag = __builtin_amdgcn_readfirstlane((int)(-ah2 * span <= 64.f));
             if (tl < Q) {
                 const float cv = cdq[tl], cr = cdq[tl | 31];
                 cds[tl] = cv;
@@ -371,20 +379,28 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
                 const int i = tile * 16 + l16, j0 = ks * 32 + 8 * q;
                 const float ci = cds[i];
                 bf16x8 m = gf[u];
-                if (ks < kd) {
-                    // below the diagonal block: exp(A (cdt_i - cdt_j)) = u2_j * v_i, both <= 1
+                // Entries above the diagonal are exact zeros in the C B^T table, so no
+                // causal cut is needed: any finite decay factor leaves them zero.
+                if (ks < kd || split_diag) {
+                    // exp(A (cdt_i - cdt_j)) = u2_j * v_i with r the 32-row block end:
+                    // below the diagonal block both factors are <= 1; on it v_i >= 1, and
+                    // the chunk was checked to keep it within 2^64
                     const float vi = exp2f_fast(ah2 * (ci - cds[ks * 32 + 31]));
+                    if (ks < kd) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) m[e] = (bf16)((float)m[e] * (u2[j0 + e] * vi));
+                        for (int e = 0; e < 8; ++e) m[e] = (bf16)((float)m[e] * (u2[j0 + e] * vi));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            m[e] = (bf16)((float)m[e] * (u2[j0 + e] * vi) + ((j0 + e == i) ? Dh : 0.f));
+                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int j = j0 + e;
                         // exponent clamped to <= 0 so the unused (j > i) slots stay finite
-                        float v = (float)m[e] * exp2f_fast(fminf(ah2 * (ci - cds[j]), 0.f));
-                        v = (j <= i) ? v : 0.f;
-                        v += (j == i) ? Dh : 0.f;
-                        m[e] = (bf16)v;
+                        const float v = (float)m[e] * exp2f_fast(fminf(ah2 * (ci - cds[j]), 0.f));
+                        m[e] = (bf16)(v + ((j == i) ? Dh : 0.f));
                     }
                 }
 #pragma unroll

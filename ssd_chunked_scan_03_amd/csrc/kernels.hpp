@@ -211,7 +211,9 @@ __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ d
 // k_cb: cb[b,c,g][i][j] = sum_n C[b,cQ+i,g,n] B[b,cQ+j,g,n] for the 64x64 blocks on
 // and below the diagonal (block row >= block column); tokens past T read as 0.
 // This is the query-key product of the diagonal block, shared by every head of the
-// group.  Grid (chunks, nb(nb+1)/2, G) over the global chunk axis, nb = Q/64.  Each wave computes the transposed
+// group.  In the blocks on the diagonal the entries above it (j > i, outside the causal
+// form) are stored as exact zeros, so that a consumer's decay factor there needs no
+// causal cut (0 times any finite factor is 0).  Grid (chunks, nb(nb+1)/2, G) over the global chunk axis, nb = Q/64.  Each wave computes the transposed
 // tile cb^T[j][i] for 16 j x 64 i, so a lane ends up owning 4 consecutive j of one
 // row i and stores them as one vector.
 // TR = true writes the same blocks transposed, cbt[j][i] = B_j . C_i (i >= j blocks, i
@@ -290,7 +292,10 @@ __device__ __forceinline__ void cb_body(const T* __restrict__ Bm, const T* __res
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             const int i = I * 64 + 16 * ct + l16;
-            const bf16x4 v = bf16x4{(bf16)acc[ct][0], (bf16)acc[ct][1], (bf16)acc[ct][2], (bf16)acc[ct][3]};
+            bf16x4 v = bf16x4{(bf16)acc[ct][0], (bf16)acc[ct][1], (bf16)acc[ct][2], (bf16)acc[ct][3]};
+            if (!TR && I == J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = (j0 + r > i) ? (bf16)0.f : v[r];
             if (TR) st4(out + (int64_t)(J * 64 + 16 * w + l16) * Q + I * 64 + 16 * ct + 4 * q, v);
             else st4(out + (int64_t)i * Q + j0, v);
         }
@@ -320,7 +325,7 @@ __device__ __forceinline__ void cb_body(const T* __restrict__ Bm, const T* __res
         const int i = I * 64 + 16 * ct + l16;
         v4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = from_f<T>(acc[ct][r]);
+        for (int r = 0; r < 4; ++r) v[r] = from_f<T>((!TR && I == J && j0 + r > i) ? 0.f : acc[ct][r]);
         if (TR) st4(out + (int64_t)(J * 64 + 16 * w + l16) * Q + I * 64 + 16 * ct + 4 * q, v);
         else st4(out + (int64_t)i * Q + j0, v);
     }
@@ -385,7 +390,11 @@ __device__ __forceinline__ void cb_row_body(const bf16* __restrict__ Bm, const b
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             const int i = I * 64 + 16 * ct + l16;
-            st4(out + (int64_t)i * Q + j0, bf16x4{(bf16)acc[ct][0], (bf16)acc[ct][1], (bf16)acc[ct][2], (bf16)acc[ct][3]});
+            bf16x4 v = bf16x4{(bf16)acc[ct][0], (bf16)acc[ct][1], (bf16)acc[ct][2], (bf16)acc[ct][3]};
+            if (J == I)  // above the diagonal: exact zeros
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = (j0 + r > i) ? (bf16)0.f : v[r];
+            st4(out + (int64_t)i * Q + j0, v);
         }
     }
 }
@@ -959,11 +968,10 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
 #pragma unroll
                             for (int e = 0; e < 8; ++e) {
                                 const int j = j0 + e;
-                                // exponent clamped to <= 0 so the unused (j > i) slots stay finite
-                                float m = to_f(gf[ks][e]) * exp2f_fast(fminf(ah2 * (ci - cds[j]), 0.f));
-                                m = (j <= i) ? m : 0.f;
-                                m += (j == i) ? Dh : 0.f;
-                                mf[e] = from_f<T>(m);
+                                // exponent clamped to <= 0 so the (j > i) slots stay finite: the
+                                // table holds exact zeros there, so they need no causal cut
+                                const float m = to_f(gf[ks][e]) * exp2f_fast(fminf(ah2 * (ci - cds[j]), 0.f));
+                                mf[e] = from_f<T>(m + ((j == i) ? Dh : 0.f));
                             }
                         }
 #pragma unroll

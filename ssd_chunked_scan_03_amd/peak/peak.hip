@@ -11,11 +11,28 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// dst[i] = src[i] for n 16-byte elements, grid-stride, non-temporal (streamed once)
+// dst[i] = src[i] for n 16-byte elements, grid-stride; each thread has four 16-byte
+// loads in flight before its stores.  NT: non-temporal loads and stores (streamed once).
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) { return NT ? __builtin_nontemporal_load(p) : *p; }
+template <bool NT>
+__device__ __forceinline__ void st(u32x4* p, u32x4 v) {
+    if (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+template <bool NT>
 __global__ __launch_bounds__(256) void k_copy16(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const u32x4 a = ld<NT>(src + i), b = ld<NT>(src + i + stride), c = ld<NT>(src + i + 2 * stride),
+                    d = ld<NT>(src + i + 3 * stride);
+        st<NT>(dst + i, a);
+        st<NT>(dst + i + stride, b);
+        st<NT>(dst + i + 2 * stride, c);
+        st<NT>(dst + i + 3 * stride, d);
+    }
+    for (; i < n; i += stride) st<NT>(dst + i, ld<NT>(src + i));
 }
 
 // `iters` rounds of 8 independent 16x16x32 bf16 matrix-core steps per wave (8 chains hide
@@ -48,14 +65,17 @@ __global__ __launch_bounds__(256) void k_mfma(float* __restrict__ out, int iters
 
 extern "C" {
 
-// Enqueue one copy of `bytes` (a multiple of 16) from src to dst on `stream`.
-int peak_copy(const void* src, void* dst, int64_t bytes, void* stream) {
-    if (!src || !dst || bytes <= 0 || bytes % 16) return 1;
+// Enqueue one copy of `bytes` (a multiple of 16) from src to dst on `stream` with
+// `blocks` work-groups of 256 threads; nt != 0: non-temporal accesses.
+int peak_copy(const void* src, void* dst, int64_t bytes, int blocks, int nt, void* stream) {
+    if (!src || !dst || bytes <= 0 || bytes % 16 || blocks <= 0) return 1;
     const int64_t n = bytes / 16;
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 256 * 64) blocks = 256 * 64;
-    k_copy16<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>(static_cast<const u32x4*>(src),
-                                                               static_cast<u32x4*>(dst), n);
+    if (nt)
+        k_copy16<true><<<blocks, 256, 0, (hipStream_t)stream>>>(static_cast<const u32x4*>(src),
+                                                                static_cast<u32x4*>(dst), n);
+    else
+        k_copy16<false><<<blocks, 256, 0, (hipStream_t)stream>>>(static_cast<const u32x4*>(src),
+                                                                 static_cast<u32x4*>(dst), n);
     return hipGetLastError() == hipSuccess ? 0 : 7;
 }
 

@@ -84,6 +84,11 @@ def test_stage_outputs_match_oracle_dumps(dtype, diag):
             m[:, valid:] = False
             got, want = cb[:, c][..., m], ref[:, c][..., m]
             assert np.abs(got - want).max() <= tol * np.abs(want).max()
+        # above the diagonal, inside the 64 x 64 blocks on it, the table holds exact zeros
+        up = np.triu(np.ones((64, 64), dtype=bool), 1)
+        for blk in range(Q // 64):
+            sl = slice(64 * blk, 64 * blk + 64)
+            assert np.all(cb[..., sl, sl][..., up] == 0)
     check((y, hT), oracle_ref(inp, diag), dtype, "stage case end-to-end")
 
 
@@ -105,6 +110,21 @@ def test_fused_schedule_matches_oracle(case):
     print(f"[fused case] {case}", flush=True)
     inp = make_small(b, T, H, P, N, G, seed=2000 + T + N, dtype="bf16", h0=h0, D=D)
     check(run_gpu(inp, "bf16", Q, False, flags=ssd.SCHEDULE_FUSED), oracle_ref(inp, False), "bf16", str(case))
+
+
+@pytest.mark.parametrize("decay", ["one", "zero", "strong", "mixed"])
+def test_fused_schedule_decay_extremes(decay):
+    """The fused kernel splits each diagonal block's decay into two factors when every
+    32-token block of the chunk decays by at most 2^64, and takes direct exponentials
+    otherwise.  a = 1 (A = 0), a = 0 (dt A = -1e7 per token), strong decays (A = -60:
+    every chunk direct) and per-head mixtures (some chunks each way) against the oracle."""
+    b, T, H, P, N, G, Q = 2, 700, 4, 64, 128, 2, 256
+    inp = make_small(b, T, H, P, N, G, seed=61, dtype="bf16")
+    A = {"one": [0.0] * H, "zero": [-1e7] * H, "strong": [-60.0] * H, "mixed": [-0.5, -14.0, -40.0, 0.0]}[decay]
+    inp["A"] = np.asarray(A, dtype=np.float32)
+    if decay == "mixed":
+        inp["dt"][:, 300:500, :] = 0.1  # one stretch of fast decay in every head
+    check(run_gpu(inp, "bf16", Q, False, flags=ssd.SCHEDULE_FUSED), oracle_ref(inp, False), "bf16", decay)
 
 
 def test_fused_and_split_agree():
