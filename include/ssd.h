@@ -162,6 +162,24 @@ int ssd_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const flo
                  const void* B, const void* C, const float* D, const float* h0,
                  void* y, float* hT, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): ssd_scan_fwd with its workspace taken
+ * from a scratch array the library keeps in each GPU's memory, SSD_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held from the first call on that GPU (the current device) until the
+ * process ends.  The caller passes inputs and outputs only; arguments, schedule flags and
+ * errors are as for ssd_scan_fwd, and a problem whose ssd_workspace_bytes(p, 0) exceeds
+ * the scratch returns SSD_ERR_WORKSPACE before any HIP call (the 2.7B layer shape,
+ * b8 T4096 H80 P64 N128 Q256 on the fused schedule, needs 35.7 MB).  The forward fully
+ * writes every scratch region it reads, so no clearing is needed between calls.  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from threads without ordering) race on it and must be ordered
+ * on one stream.  The stream must belong to the current device.  Nothing is allocated
+ * and nothing is freed. */
+#define SSD_NOALLOC_SCRATCH_BYTES (64u << 20)
+int ssd_scan_fwd_noalloc(const ssd_problem* p, const void* x, const float* dt, const float* A,
+                         const void* B, const void* C, const float* D, const float* h0,
+                         void* y, float* hT, void* stream);
+
 /* Diagonal-decay SSD forward: A is [nheads, dstate].  Same conventions;
  * `ws` must hold ssd_workspace_bytes(p, 1) bytes.
  * The output kernel keeps a chunk's x rows and its rescaled C and B rows in LDS:

@@ -29,7 +29,8 @@ _lib = None
 SSD_F32, SSD_BF16 = 0, 1
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_ALIGN", 6: "SSD_ERR_ALIAS", 7: "SSD_ERR_HIP"}
-EXPORTS = ("ssd_workspace_bytes", "ssd_get_workspace_layout", "ssd_scan_fwd", "ssd_diag_scan_fwd",
+EXPORTS = ("ssd_workspace_bytes", "ssd_get_workspace_layout", "ssd_scan_fwd", "ssd_scan_fwd_noalloc",
+           "ssd_diag_scan_fwd",
            "ssd_varlen_workspace_bytes", "ssd_scan_fwd_varlen",
            "ssd_step", "ssd_diag_step", "ssd_bwd_workspace_bytes", "ssd_scan_bwd",
            "ssd_diag_bwd_workspace_bytes", "ssd_diag_scan_bwd",
@@ -74,6 +75,8 @@ def _load():
     for f in (lib.ssd_scan_fwd, lib.ssd_diag_scan_fwd):
         f.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp]
         f.restype = ci
+    lib.ssd_scan_fwd_noalloc.argtypes = [P, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp]
+    lib.ssd_scan_fwd_noalloc.restype = ci
     lib.ssd_varlen_workspace_bytes.argtypes = [P]
     lib.ssd_varlen_workspace_bytes.restype = sz
     lib.ssd_scan_fwd_varlen.argtypes = [P, vp, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp]
@@ -175,6 +178,22 @@ def scan_fwd_into(prob: Problem, diag: bool, x, dt, A, B, C, D, h0, y, hT, ws, s
             _ptr(y), _ptr(hT), _ptr(ws), nbytes, ctypes.c_void_p(int(stream)))
     if st:
         raise SSDError(st, "ssd_diag_scan_fwd" if diag else "ssd_scan_fwd")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def scan_fwd_noalloc_into(prob: Problem, x, dt, A, B, C, D, h0, y, hT, stream=None) -> None:
+    """Enqueue one scalar-decay forward into caller-provided outputs, with the library's
+    per-GPU scratch array as workspace (no allocation anywhere; calls on one GPU must be
+    ordered on one stream)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = _load().ssd_scan_fwd_noalloc(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(h0), _ptr(y), _ptr(hT), ctypes.c_void_p(int(stream)))
+    if st:
+        raise SSDError(st, "ssd_scan_fwd_noalloc")
 
 
 def _dtype_code(t):

@@ -1,12 +1,20 @@
 // abi.hip -- the C ABI of libssd.so (declared in include/ssd.h): host-side
-// validation, workspace layout and launch sequencing.  No allocation, no global
-// mutable state; every check happens before the first HIP call.
+// validation, workspace layout and launch sequencing.  No allocation; every check
+// happens before the first HIP call.  The only global state is the per-device address
+// of the no-allocation forward's scratch array, looked up once per device.
 #include <string.h>
 
 #include "bwd_launch.hpp"
 #include "launch.hpp"
 #include "step.hpp"
 #include "ssd.h"
+
+#include <mutex>
+
+// Workspace of ssd_scan_fwd_noalloc: one copy of this array per GPU, in the library's
+// device code, held until the process ends.  In host code its name is only a stand-in
+// for the symbol; kernels receive the per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -119,9 +127,11 @@ bool overlap(Range a, Range b) {
     return a0 < b0 + b.n && b0 < a0 + a.n;
 }
 
+// check_only: run every check except those of the workspace (which the caller supplies
+// later) and return without any HIP call.
 int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const float* A,
          const void* B, const void* C, const float* D, const float* h0, void* y, float* hT,
-         void* ws, size_t ws_bytes, void* stream) {
+         void* ws, size_t ws_bytes, void* stream, bool check_only = false) {
     int st = check_problem(p);
     if (st) return st;
     const int64_t b = p->batch, T = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate,
@@ -136,6 +146,7 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
         // empty sequence: hT = h0 (or 0); y is empty
         if (!hT) return SSD_OK;
         if (overlap({hT, state_bytes}, {h0, state_bytes})) return SSD_ERR_ALIAS;
+        if (check_only) return SSD_OK;
         const int64_t n = b * H * P * N;
         k_copy_state<<<(unsigned)((n + 255) / 256), 256, 0, (hipStream_t)stream>>>(h0, hT, n);
         return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
@@ -144,8 +155,12 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(dt, 4))
         return SSD_ERR_ALIGN;
     const ssd_workspace_layout L = layout_of(p, diag);
-    if (!ws || ws_bytes < L.total_bytes) return SSD_ERR_WORKSPACE;
-    if (!aligned(ws, kAlign)) return SSD_ERR_ALIGN;
+    if (check_only) {
+        ws = nullptr;  // the workspace is checked once it is known
+    } else {
+        if (!ws || ws_bytes < L.total_bytes) return SSD_ERR_WORKSPACE;
+        if (!aligned(ws, kAlign)) return SSD_ERR_ALIGN;
+    }
 
     const size_t xb = (size_t)(b * T * H * P) * es;
     const Range ins[] = {{x, xb},
@@ -160,6 +175,7 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     for (const Range& r : ins)
         if (overlap(ry, r) || overlap(rh, r)) return SSD_ERR_ALIAS;
     if (overlap(ry, rh)) return SSD_ERR_ALIAS;
+    if (check_only) return SSD_OK;
 
     ssd::RunArgs a;
     a.b = b; a.T = T; a.H = H; a.P = P; a.N = N; a.G = G; a.Q = Q;
@@ -180,6 +196,42 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     a.force_split = (p->flags & SSD_SCHEDULE_SPLIT) != 0;
     a.force_fused = (p->flags & SSD_SCHEDULE_FUSED) != 0;
     return p->dtype == SSD_BF16 ? ssd::run_bf16(a) : ssd::run_f32(a);
+}
+
+// ---- the forward without caller workspace (ssd_scan_fwd_noalloc) ----
+// The scratch array's device address on each GPU, looked up once per device (with that
+// device current) and kept; later calls reuse it.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SSD_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SSD_ERR_HIP;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return SSD_OK;
+}
+
+int scan_noalloc(const ssd_problem* p, const void* x, const float* dt, const float* A, const void* B,
+                 const void* C, const float* D, const float* h0, void* y, float* hT, void* stream) {
+    // every argument check first, then the size limit, before any HIP call
+    int st = scan(p, 0, x, dt, A, B, C, D, h0, y, hT, nullptr, 0, stream, true);
+    if (st) return st;
+    const ssd_workspace_layout L = layout_of(p, 0);
+    if (L.total_bytes > (size_t)SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (L.total_bytes > 0) {
+        st = scratch_of_current_device(&ws);
+        if (st) return st;
+    }
+    return scan(p, 0, x, dt, A, B, C, D, h0, y, hT, ws, SSD_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ---- packed variable-length sequences (ssd_scan_fwd_varlen) ----
@@ -531,6 +583,12 @@ int ssd_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const flo
                  const void* B, const void* C, const float* D, const float* h0, void* y,
                  float* hT, void* ws, size_t ws_bytes, void* stream) {
     return scan(p, 0, x, dt, A, B, C, D, h0, y, hT, ws, ws_bytes, stream);
+}
+
+int ssd_scan_fwd_noalloc(const ssd_problem* p, const void* x, const float* dt, const float* A,
+                         const void* B, const void* C, const float* D, const float* h0, void* y,
+                         float* hT, void* stream) {
+    return scan_noalloc(p, x, dt, A, B, C, D, h0, y, hT, stream);
 }
 
 int ssd_diag_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const float* A,

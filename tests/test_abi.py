@@ -433,3 +433,34 @@ def test_diag_bwd_error_paths_return_before_any_launch():
     # an empty problem checks dA against A over [H, N] too
     ptrs0, _ = bwd_fake_ptrs(prob(T=0), True)
     assert call_bwd(prob(T=0), True, dA=ptrs0["A"] + 4 * p.nheads)[0] == S("SSD_ERR_ALIAS")
+
+
+def call_noalloc(p, **over):
+    """ssd_scan_fwd_noalloc with fake well-formed pointers, some overridden (every use
+    below is invalid on purpose, so the host rejects it before any HIP call)."""
+    ptrs, _ = fake_ptrs(p)
+    ptrs.update(over)
+    v = lambda k: ctypes.c_void_p(ptrs[k]) if ptrs[k] else None
+    return ssd._load().ssd_scan_fwd_noalloc(ctypes.byref(p), v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"),
+                                            v("h0"), v("y"), v("hT"), None)
+
+
+def test_noalloc_forward_checks_before_any_hip_call():
+    """The forward without caller workspace checks its arguments like ssd_scan_fwd, and a
+    problem whose workspace exceeds the 64 MiB per-GPU scratch array is refused."""
+    p = prob()
+    assert call_noalloc(p, x=0) == ssd_status("SSD_ERR_NULL")
+    assert call_noalloc(p, A=0) == ssd_status("SSD_ERR_NULL")
+    assert call_noalloc(p, x=BASE + 8) == ssd_status("SSD_ERR_ALIGN")
+    ptrs, _ = fake_ptrs(p)
+    assert call_noalloc(p, y=ptrs["x"]) == ssd_status("SSD_ERR_ALIAS")
+    assert call_noalloc(prob(Q=32)) == ssd_status("SSD_ERR_UNSUPPORTED")
+    assert call_noalloc(prob(b=0)) == 0
+    # the 2.7B layer's split schedule needs 538 MB of workspace: more than the scratch holds
+    big = ssd.make_problem(8, 4096, 80, 64, 128, 1, 256, ssd.SSD_BF16, ssd.SCHEDULE_SPLIT)
+    assert ssd.workspace_bytes(big) > ssd.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(big) == ssd_status("SSD_ERR_WORKSPACE")
+    # its fused schedule fits
+    assert ssd.workspace_bytes(ssd.make_problem(8, 4096, 80, 64, 128, 1, 256, ssd.SSD_BF16)) \
+        <= ssd.NOALLOC_SCRATCH_BYTES
+    assert ssd._load().ssd_scan_fwd_noalloc(None, *([None] * 9), None) == ssd_status("SSD_ERR_NULL")
