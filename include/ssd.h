@@ -128,7 +128,10 @@ size_t ssd_workspace_bytes(const ssd_problem* p, int diag);
  *   cdt  float32 [batch, nheads, nchunks, chunk]  chunk-local cumulative sum of dt
  *        (positions past seqlen repeat the chunk total)
  *   cb   dtype   [batch, nchunks, ngroups, chunk, chunk]  C_c B_c^T, blocks on and below
- *        the diagonal (scalar decay only)
+ *        the diagonal (scalar decay); for the diagonal decay, where its output tile does
+ *        not fit LDS (see ssd_diag_scan_fwd), [batch, nheads, nchunks, chunk, chunk] each
+ *        head's decay-weighted block sum_n C_in B_jn exp(A_n (cdt_i - cdt_j)), D on the
+ *        diagonal, zero above it
  *   states float32 [batch, nheads, nchunks, headdim, dstate]  chunk states S_c
  *   hin  dtype   [batch, nheads, nchunks, headdim, dstate]  state entering chunk c
  *   bt   dtype   [batch, nchunks, ngroups, dstate, chunk]  B of each chunk, tokens contiguous
@@ -181,13 +184,13 @@ int ssd_scan_fwd_noalloc(const ssd_problem* p, const void* x, const float* dt, c
                          void* y, float* hT, void* stream);
 
 /* Diagonal-decay SSD forward: A is [nheads, dstate].  Same conventions;
- * `ws` must hold ssd_workspace_bytes(p, 1) bytes.
- * The output kernel keeps a chunk's x rows and its rescaled C and B rows in LDS:
- * (chunk * (headdim + 8) + 2 * chunk * (dstate + 8)) elements plus (2 * chunk + dstate)
- * floats must fit the 160 KiB of one CU (for bfloat16 at chunk 256 that allows dstate up
- * to 64 at headdim 64, for example); larger problems return SSD_ERR_UNSUPPORTED before
- * any launch.  (The scalar decay's tile, chunk * (headdim + 8) elements plus 2 * chunk
- * floats, always fits.) */
+ * `ws` must hold ssd_workspace_bytes(p, 1) bytes.  Every supported (chunk, headdim,
+ * dstate, dtype) runs.  The output kernel keeps a chunk's x rows and its rescaled C and B
+ * rows in LDS where (chunk * (headdim + 8) + 2 * chunk * (dstate + 8)) elements plus
+ * (2 * chunk + dstate) floats fit the 160 KiB of one CU; otherwise (bfloat16 at chunk 256
+ * with dstate 128 or more, for example) a table kernel first forms each (batch, head,
+ * chunk)'s decay-weighted query-key block in the workspace's cb region,
+ * batch * nheads * nchunks * chunk^2 elements, and the output kernel reads it. */
 int ssd_diag_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const float* A,
                       const void* B, const void* C, const float* D, const float* h0,
                       void* y, float* hT, void* ws, size_t ws_bytes, void* stream);

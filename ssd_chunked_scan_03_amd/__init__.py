@@ -115,13 +115,25 @@ SPLIT_KERNELS = ("k_cumsum", "k_cb", "k_state", "k_scan", "k_out")
 FUSED_KERNELS = ("k_cumsum", "k_cb", "k_bt", "k_fused")
 
 
-def schedule_kernels(schedule: str, diag: bool):
+def diag_uses_table(chunk, headdim, dstate, dtype_code) -> bool:
+    """Whether the diagonal decay's output kernel reads a per-(batch, head, chunk) table of
+    decay-weighted query-key products (its LDS tile of x rows and rescaled C / B rows
+    would not fit one CU's 160 KiB)."""
+    es = 2 if dtype_code == SSD_BF16 else 4
+    return (chunk * (headdim + 8) + 2 * chunk * (dstate + 8)) * es + (2 * chunk + dstate) * 4 > 160 * 1024
+
+
+def schedule_kernels(schedule: str, diag: bool, prob: "Problem" = None):
     """(kernel name, stage mask) in the order a whole forward launches them.  A whole
     forward runs its preparation (cumsum, C B^T, and B^T on the fused schedule) as one
-    launch, k_prep; a stage mask that holds all of those bits runs that same launch."""
+    launch, k_prep; a stage mask that holds all of those bits runs that same launch.
+    The diagonal decay's table kernel, where it runs (see diag_uses_table), is the C B^T
+    stage."""
     if schedule == "fused":
         return [("k_prep", STAGE_CUMSUM | STAGE_CB | STAGE_BT), ("k_fused", STAGE_FUSED)]
     first = [("k_cumsum", STAGE_CUMSUM)] if diag else [("k_prep", STAGE_CUMSUM | STAGE_CB)]
+    if diag and prob is not None and diag_uses_table(prob.chunk, prob.headdim, prob.dstate, prob.dtype):
+        first.append(("k_gtab", STAGE_CB))
     return first + [("k_state", STAGE_STATE), ("k_scan", STAGE_SCAN), ("k_out", STAGE_OUT)]
 
 

@@ -92,7 +92,12 @@ ssd_workspace_layout layout_of(const ssd_problem* p, int diag) {
     L.cdt_bytes = bhc * (size_t)p->chunk * 4;
     off += align_up(L.cdt_bytes);
     L.cb_off = off;
-    L.cb_bytes = diag ? 0 : (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->chunk * p->chunk) * es;
+    // scalar decay: the group's C B^T per chunk; diagonal decay: each head's table of
+    // decay-weighted products, only where the output kernel's LDS tile does not fit
+    const bool tab = diag && ssd::diag_uses_table(p->chunk, p->headdim, p->dstate, es);
+    L.cb_bytes = tab    ? bhc * (size_t)(p->chunk * p->chunk) * es
+                 : diag ? 0
+                        : (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->chunk * p->chunk) * es;
     off += align_up(L.cb_bytes);
     L.states_off = off;
     L.states_bytes = fused ? 0 : bhc * (size_t)(p->headdim * p->dstate) * 4;
@@ -185,7 +190,7 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     a.y = y; a.hT = hT;
     char* w = static_cast<char*>(ws);
     a.cdt = reinterpret_cast<float*>(w + L.cdt_off);
-    a.cb = diag ? nullptr : static_cast<void*>(w + L.cb_off);
+    a.cb = L.cb_bytes ? static_cast<void*>(w + L.cb_off) : nullptr;
     a.states = L.states_bytes ? reinterpret_cast<float*>(w + L.states_off) : nullptr;
     a.hin = L.hin_bytes ? static_cast<void*>(w + L.hin_off) : nullptr;
     a.bt = L.bt_bytes ? static_cast<void*>(w + L.bt_off) : nullptr;

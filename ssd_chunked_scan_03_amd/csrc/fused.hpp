@@ -54,35 +54,6 @@ __device__ __forceinline__ int fused_tile(int pass, int t, int w) {
     return w;
 }
 
-// element offset of x(j, p) in the swizzled x tile (64 bf16 = 128 B per row, 16-byte
-// chunks).  A transpose read touches 4 consecutive rows x 32 B per 16-lane group, and two
-// groups 8 (or 16) rows apart are serviced together: the 32-byte slot of a row is XORed
-// with (j & 3) and with bit 3 ^ bit 4 of j, so all 8 rows of a serviced pair land in
-// distinct bank ranges.  Rows j and j + 32 k share a swizzle.
-__device__ __forceinline__ int xs_swz(int j) { return (j & 3) ^ (((j >> 3) ^ (j >> 4)) & 1); }
-__device__ __forceinline__ int xs_off(int j, int p) {
-    const int ch = p >> 3;
-    return j * 64 + (((((ch >> 1) ^ xs_swz(j)) << 1) | (ch & 1)) << 3) + (p & 7);
-}
-
-// MFMA fragment of the swizzled x tile: lane l holds x(k0 + 8 (l/16) + e, c0 + l % 16)
-__device__ __forceinline__ bf16x8 frag_xs(const bf16* Xs, int k0, int c0, int lane) {
-    const int s = lane & 15;
-    const int r = k0 + 8 * (lane >> 4) + (s >> 2);
-    const int col = c0 + 4 * (s & 3);
-    const s16x4 a = ds_tr16(Xs + xs_off(r, col));
-    const s16x4 b = ds_tr16(Xs + xs_off(r + 4, col));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Same fragment from a lane-constant base: xo = xs_off(8 (l/16) + (l%16)/4, c0 + 4 (l%4)).
-// k0 is a multiple of 32, so the row swizzle (j & 3) is unchanged and k0 adds k0 * 64.
-__device__ __forceinline__ bf16x8 frag_xs_o(const bf16* Xs, int xo, int k0) {
-    const s16x4 a = ds_tr16(Xs + xo + k0 * 64);
-    const s16x4 b = ds_tr16(Xs + xo + k0 * 64 + 256);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 template <int N>
 __device__ __forceinline__ int hs_off(int p, int n) {
     constexpr int HSW = (N / 8) < 16 ? (N / 8) : 16;

@@ -507,6 +507,71 @@ __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ dt,
 }
 
 // ---------------------------------------------------------------------------
+// The bfloat16 x tile of 64-element rows (headdim 64) in LDS, shared by the chunk kernels.
+// element offset of x(j, p) in the swizzled x tile (64 bf16 = 128 B per row, 16-byte
+// chunks).  A transpose read touches 4 consecutive rows x 32 B per 16-lane group, and two
+// groups 8 (or 16) rows apart are serviced together: the 32-byte slot of a row is XORed
+// with (j & 3) and with bit 3 ^ bit 4 of j, so all 8 rows of a serviced pair land in
+// distinct bank ranges.  Rows j and j + 32 k share a swizzle.
+__device__ __forceinline__ int xs_swz(int j) { return (j & 3) ^ (((j >> 3) ^ (j >> 4)) & 1); }
+__device__ __forceinline__ int xs_off(int j, int p) {
+    const int ch = p >> 3;
+    return j * 64 + (((((ch >> 1) ^ xs_swz(j)) << 1) | (ch & 1)) << 3) + (p & 7);
+}
+
+// MFMA fragment of the swizzled x tile: lane l holds x(k0 + 8 (l/16) + e, c0 + l % 16)
+__device__ __forceinline__ bf16x8 frag_xs(const bf16* Xs, int k0, int c0, int lane) {
+    const int s = lane & 15;
+    const int r = k0 + 8 * (lane >> 4) + (s >> 2);
+    const int col = c0 + 4 * (s & 3);
+    const s16x4 a = ds_tr16(Xs + xs_off(r, col));
+    const s16x4 b = ds_tr16(Xs + xs_off(r + 4, col));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Same fragment from a lane-constant base: xo = xs_off(8 (l/16) + (l%16)/4, c0 + 4 (l%4)).
+// k0 is a multiple of 32, so the row swizzle (j & 3) is unchanged and k0 adds k0 * 64.
+__device__ __forceinline__ bf16x8 frag_xs_o(const bf16* Xs, int xo, int k0) {
+    const s16x4 a = ds_tr16(Xs + xo + k0 * 64);
+    const s16x4 b = ds_tr16(Xs + xo + k0 * 64 + 256);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Fragment with rows ra + e (e < 4) and rb + e - 4 (e >= 4) of column c0 + l % 16, as
+// frag_rows_split, from the swizzled tile.
+__device__ __forceinline__ bf16x8 frag_xs_split(const bf16* Xs, int ra, int rb, int c0, int lane) {
+    const int s = lane & 15;
+    const int col = c0 + 4 * (s & 3);
+    const s16x4 a = ds_tr16(Xs + xs_off(ra + (s >> 2), col));
+    const s16x4 b = ds_tr16(Xs + xs_off(rb + (s >> 2), col));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Element offsets of a chunk's x rows in LDS: the swizzled 64-element rows for bfloat16
+// at headdim 64 (no bank conflicts in the transpose reads), else rows padded by 8.
+// (The diagonal-decay output kernel keeps the padded rows: its split-row fragments would
+// need more address registers than its occupancy allows.)
+template <typename T, int P, bool ALLOW = true>
+struct XRows {
+    static constexpr bool SWZ = ALLOW && sizeof(T) == 2 && P == 64;
+    static constexpr int LD = SWZ ? 64 : P + 8;
+    __device__ static int off(int j, int p) {
+        if constexpr (SWZ) return xs_off(j, p);
+        else return j * LD + p;
+    }
+};
+template <typename T, int P, bool ALLOW = true>
+__device__ __forceinline__ typename V8<T>::type frag_x(const T* Xs, int k0, int c0, int lane) {
+    if constexpr (XRows<T, P, ALLOW>::SWZ) return frag_xs(Xs, k0, c0, lane);
+    else return frag_rows(Xs, XRows<T, P, ALLOW>::LD, k0, c0, lane);
+}
+template <typename T, int P, bool ALLOW = true>
+__device__ __forceinline__ typename V8<T>::type frag_x_split(const T* Xs, int ra, int rb, int c0, int lane) {
+    if constexpr (XRows<T, P, ALLOW>::SWZ) return frag_xs_split(Xs, ra, rb, c0, lane);
+    else return frag_rows_split(Xs, XRows<T, P, ALLOW>::LD, ra, rb, c0, lane);
+}
+
+// ---------------------------------------------------------------------------
 // Wave tiling of a [N/16] x [P/16] grid of 16x16 output tiles over 4 waves: each
 // wave owns WN x WP tiles starting at (n-tile n0, p-tile p0) (or none).
 // ---------------------------------------------------------------------------
@@ -544,7 +609,8 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
                                                     int Q, int nc) {
     typedef typename V8<T>::type v8;
     typedef StateTiling<P, N> TL;
-    constexpr int JB = 64, LDX = P + 8, LDB = N + 8;
+    typedef XRows<T, P> XL;
+    constexpr int JB = 64, LDX = XL::LD, LDB = N + 8;
     constexpr int XV = JB * P / 8, BV = JB * N / 8;                       // 8-element vectors per slab
     constexpr int XR = (XV + kThreads - 1) / kThreads, BR = (BV + kThreads - 1) / kThreads;
     __shared__ __attribute__((aligned(16))) T Xs[JB * LDX];
@@ -610,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
 #pragma unroll
                     for (int e = 0; e < 8; ++e) o[e] = from_f<T>(to_f(o[e]) * wj);
                 }
-                st8(&Xs[jj * LDX + p0], o);
+                st8(Xs + XL::off(jj, p0), o);
             }
         }
 #pragma unroll
@@ -634,7 +700,7 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
             for (int kk = 0; kk < JB; kk += 32) {
                 v8 bf[TL::WP];
 #pragma unroll
-                for (int b = 0; b < TL::WP; ++b) bf[b] = frag_rows(Xs, LDX, kk, (wp0 + b) * 16, lane);
+                for (int b = 0; b < TL::WP; ++b) bf[b] = frag_x<T, P>(Xs, kk, (wp0 + b) * 16, lane);
 #pragma unroll
                 for (int a = 0; a < TL::WN; ++a) {
                     const v8 af = frag_rows(Bs, LDB, kk, (wn0 + a) * 16, lane);
@@ -782,19 +848,20 @@ __global__ __launch_bounds__(kThreads) void k_scan_carry(const float* __restrict
 // Each wave owns Q/64 row tiles of 16 rows, paired (k, 7-k) within every 128 rows so
 // the causal work is balanced.  y is staged through LDS (aliasing x) for row stores.
 // ---------------------------------------------------------------------------
-template <typename T, int P, int N, bool DIAG>
+template <typename T, int P, int N, bool DIAG, bool TAB = false>
 struct OutSmem {
-    static constexpr int LDX = P + 8;  // x (then y) rows
+    static constexpr bool RESCALED = DIAG && !TAB;  // rescaled C / B rows in LDS
+    static constexpr int LDX = XRows<T, P, !RESCALED>::LD;  // x (then y) rows
     static constexpr int LDN = N + 8;  // rescaled C / B rows (diagonal decay)
     __host__ __device__ static int xs(int Q) { return Q * LDX; }
-    __host__ __device__ static int diag_elems(int Q) { return DIAG ? 2 * Q * LDN : 0; }
-    __host__ __device__ static int floats(int Q) { return 2 * Q + (DIAG ? N : 0); }
+    __host__ __device__ static int diag_elems(int Q) { return RESCALED ? 2 * Q * LDN : 0; }
+    __host__ __device__ static int floats(int Q) { return 2 * Q + (RESCALED ? N : 0); }
     __host__ __device__ static size_t bytes(int Q) {
         return (size_t)(xs(Q) + diag_elems(Q)) * sizeof(T) + (size_t)floats(Q) * sizeof(float);
     }
 };
 
-template <typename T, int P, int N, bool DIAG>
+template <typename T, int P, int N, bool DIAG, bool TAB = false>
 __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const T* __restrict__ Bm,
                                                   const T* __restrict__ Cm, const T* __restrict__ cb,
                                                   const T* __restrict__ hin, const float* __restrict__ A,
@@ -803,8 +870,10 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                                                   int64_t Tn, int H, int G, int Q, int nc) {
     typedef typename V8<T>::type v8;
     typedef typename V4<T>::type v4;
-    typedef OutSmem<T, P, N, DIAG> SM;
-    constexpr int LDX = SM::LDX, LDN = SM::LDN;
+    typedef OutSmem<T, P, N, DIAG, TAB> SM;
+    typedef XRows<T, P, !SM::RESCALED> XL;
+    constexpr bool SCAL = !DIAG || TAB;  // diagonal block from a table of query-key products
+    constexpr int LDN = SM::LDN;
     constexpr int PT = P / 16;
     constexpr float LOG2E = 1.4426950408889634f;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -860,7 +929,9 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
     // just before its own k-steps (a second set would cost occupancy and spill at
     // headdim 128).
     constexpr bool PF = sizeof(T) == 2;
-    const T* cbb_pf = cb + ((bi * nc + c) * G + g) * (int64_t)Q * Q;
+    // scalar decay: the group's C B^T table; diagonal decay (TAB): this head's table of
+    // decay-weighted products, D on its diagonal
+    const T* cbb_pf = cb + (TAB ? bh * nc + c : (bi * nc + c) * G + g) * (int64_t)Q * Q;
     auto load_gf = [&](int k, v8* gf) {
         const int rt = row_tile(k);
         const int nks = rt / 2 + 1;
@@ -869,10 +940,19 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
         for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbrow + (ks < nks ? ks : nks - 1) * 32 + 8 * q);
     };
     v8 gfa[8], gfb[PF ? 8 : 1];
-    if (!DIAG && PF) load_gf(0, gfa);
+    if (SCAL && PF) load_gf(0, gfa);
 
-    // 2. scalar decay: state term y^T[p][i] += sum_n H[p][n] C[i][n] from raw fragments
-    if (!DIAG) {
+    // 2. state term y^T[p][i] += sum_n H[p][n] C[i][n] from raw fragments (scalar decay:
+    //    the row factor exp(A cdt_i) follows in step 4); diagonal decay with a table:
+    //    each C element scaled by its own exp(A_n cdt_i) <= 1
+    if (SCAL) {
+        float crow[4];
+        if (TAB)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = row_tile(k) * 16 + l16;
+                crow[k] = cd[k < rpw && i < len ? i : 0];
+            }
 #pragma unroll
         for (int n0 = 0; n0 < N; n0 += 32) {
             const int nn = n0 + 8 * q;
@@ -885,6 +965,14 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                 const int i = row_tile(k) * 16 + l16;
                 const int ir = i < len ? i : len - 1;
                 cf[k] = sel8(k < rpw && nv && i < len, ld8(cbase_rows + (int64_t)ir * G * N + (nv ? nn : 0)));
+            }
+            if (TAB) {
+                const f32x8 an = ld8(A + (int64_t)h * N + (nv ? nn : 0));
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        cf[k][e] = from_f<T>(to_f(cf[k][e]) * exp2f_fast(an[e] * LOG2E * crow[k]));
             }
 #pragma unroll
             for (int k = 0; k < 4; ++k)
@@ -900,15 +988,15 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
         const int v = tid + r * kThreads;
         if (v < XV) {
             const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
-            st8(&Xs[jj * LDX + p0], xv[r]);
+            st8(Xs + XL::off(jj, p0), xv[r]);
         }
     }
     if (tid < Q) cds[tid] = cdv;
-    if (DIAG)
+    if (SM::RESCALED)
         for (int n = tid; n < N; n += kThreads) an2[n] = A[h * N + n] * LOG2E;
     __syncthreads();
     if (!DIAG && tid < Q) u2[tid] = exp2f_fast(ah2 * (cds[tid | 31] - cds[tid]));
-    if (DIAG) {
+    if (SM::RESCALED) {
         // rescaled rows: Ct[i][n] = C_i[n] e^{A_n (cdt_i - cdt_sI)}, Bt[j][n] = B_j[n] e^{A_n (cdt_eJ - cdt_j)}
         const T* bbase_rows = Bm + ((bi * Tn + tok0) * G + g) * N;
         for (int v = tid; v < Q * N / 8; v += kThreads) {
@@ -931,11 +1019,11 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
     }
     __syncthreads();
 
-    if (!DIAG) {
+    if (SCAL) {
         // 4. per-row factor of the state term: this lane's column is row i
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            if (k < rpw) {
+            if (!TAB && k < rpw) {
                 const float sc = exp2f_fast(ah2 * cds[row_tile(k) * 16 + l16]);
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) acc[k][pt] *= sc;
@@ -960,7 +1048,9 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                     if (ks < nks) {
                         const int j0 = ks * 32 + 8 * q;
                         v8 mf;
-                        if (ks < nks - 1) {
+                        if (TAB) {
+                            mf = gf[ks];  // decay, causal zeros and D are in the table
+                        } else if (ks < nks - 1) {
                             const float vi = exp2f_fast(ah2 * (ci - cds[ks * 32 + 31]));
 #pragma unroll
                             for (int e = 0; e < 8; ++e) mf[e] = from_f<T>(to_f(gf[ks][e]) * (u2[j0 + e] * vi));
@@ -976,7 +1066,7 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                         }
 #pragma unroll
                         for (int pt = 0; pt < PT; ++pt) {
-                            const v8 xf = frag_rows(Xs, LDX, ks * 32, pt * 16, lane);
+                            const v8 xf = frag_x<T, P, !SM::RESCALED>(Xs, ks * 32, pt * 16, lane);
                             acc[k][pt] = mma(acc[k][pt], xf, mf);
                         }
                     }
@@ -1051,7 +1141,7 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                     }
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) {
-                        const v8 xf = frag_rows_split(Xs, LDX, 32 * u + 4 * q, 32 * u + 16 + 4 * q, pt * 16, lane);
+                        const v8 xf = frag_x_split<T, P, !SM::RESCALED>(Xs, 32 * u + 4 * q, 32 * u + 16 + 4 * q, pt * 16, lane);
                         acc[k][pt] = mma(acc[k][pt], xf, mf);
                     }
                 }
@@ -1089,14 +1179,144 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                 v4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = from_f<T>(acc[k][pt][r]);
-                st4(&Ys[i * LDX + pt * 16 + 4 * q], o);
+                st4(Ys + XL::off(i, pt * 16 + 4 * q), o);
             }
         }
     }
     __syncthreads();
     for (int v = tid; v < len * (P / 8); v += kThreads) {
         const int ii = v / (P / 8), p0 = (v - ii * (P / 8)) * 8;
-        st8(y + ((bi * Tn + tok0 + ii) * H + h) * P + p0, ld8(&Ys[ii * LDX + p0]));
+        st8(y + ((bi * Tn + tok0 + ii) * H + h) * P + p0, ld8(Ys + XL::off(ii, p0)));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_gtab: the diagonal decay's query-key block of one (b, h, c), as a table for k_out
+// when a chunk's rescaled C and B rows do not fit LDS next to its x rows:
+//   tab[i][j] = sum_n C_i[n] B_j[n] exp(A_n (cdt_i - cdt_j)) for j < i,
+//   tab[i][i] = the same + D_h,  tab[i][j] = 0 for j > i within the 64 x 64 blocks on the
+//   diagonal (every entry of those blocks is written: the output kernel reads them)
+// ("Structured State Space Duality" concept page, "What the duality gives up": each state
+// dimension decays at its own rate, so the block is a sum of N scalar-decay masked
+// products).  One work-group per (b, h, c) and 64 x 64 block pair (I >= J): the block
+// pair's C rows and B rows are staged in LDS rescaled within their 16-row sub-blocks,
+// C~_i = C_i exp(A (cdt_i - cdt_sI)), B~_j = B_j exp(A (cdt_eJ - cdt_j)) (sI first row of
+// i's sub-block, eJ last row of j's), and each 16 x 16 sub-block pair is
+// B~_J diag(exp(A (cdt_sI - cdt_eJ))) C~_I^T on the matrix cores (all three factors <= 1
+// off the diagonal sub-blocks).  A diagonal sub-block whose decay span exceeds 2^115 is
+// summed directly with per-term exponentials.  Wave w owns sub-block row w of the pair.
+// Grid (b H nc, nb (nb + 1) / 2), nb = Q / 64; dynamic LDS gtab_smem<T, N>().
+// ---------------------------------------------------------------------------
+template <typename T, int N>
+constexpr size_t gtab_smem() { return (size_t)2 * 64 * (N + 8) * sizeof(T) + (size_t)(128 + N) * sizeof(float); }
+
+template <typename T, int N>
+__global__ __launch_bounds__(kThreads) void k_gtab(const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                                   const float* __restrict__ A, const float* __restrict__ D,
+                                                   const float* __restrict__ cdt, T* __restrict__ tab,
+                                                   int64_t Tn, int H, int G, int Q, int nc) {
+    typedef typename V8<T>::type v8;
+    typedef typename V4<T>::type v4;
+    constexpr int LDN = N + 8;
+    constexpr float LOG2E = 1.4426950408889634f;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    T* Cs = reinterpret_cast<T*>(smem_raw);          // 64 rescaled C rows of block I
+    T* Bs = Cs + 64 * LDN;                           // 64 rescaled B rows of block J
+    float* ci = reinterpret_cast<float*>(Bs + 64 * LDN);  // cdt of block I's rows
+    float* cj = ci + 64;                             // cdt of block J's rows
+    float* an2 = cj + 64;                            // A_n log2(e)
+
+    const int64_t blk = blockIdx.x;
+    const int c = (int)(blk % nc);
+    const int64_t bh = blk / nc;
+    const int h = (int)(bh % H);
+    const int64_t bi = bh / H;
+    const int g = h / (H / G);
+    int I = 0;
+    while ((I + 1) * (I + 2) / 2 <= (int)blockIdx.y) ++I;
+    const int J = (int)blockIdx.y - I * (I + 1) / 2;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, q = lane >> 4;
+    const int64_t tok0 = (int64_t)c * Q;
+    const int len = (int)((Tn - tok0) < Q ? (Tn - tok0) : Q);
+    const float* cd = cdt + (bh * nc + c) * (int64_t)Q;
+    const T* crows = Cm + ((bi * Tn + tok0) * G + g) * N;  // chunk row r at + r * G * N
+    const T* brows = Bm + ((bi * Tn + tok0) * G + g) * N;
+    for (int n = tid; n < N; n += kThreads) an2[n] = A[(int64_t)h * N + n] * LOG2E;
+    if (tid < 64) ci[tid] = cd[I * 64 + tid];
+    else if (tid < 128) cj[tid - 64] = cd[J * 64 + tid - 64];
+    __syncthreads();
+    for (int v = tid; v < 64 * N / 8; v += kThreads) {
+        const int r = v / (N / 8), n0 = (v - r * (N / 8)) * 8;
+        v8 cv = zero8<T>(), bv = zero8<T>();
+        if (I * 64 + r < len) {
+            const v8 cr = ld8(crows + (int64_t)(I * 64 + r) * G * N + n0);
+            const float dc = ci[r] - ci[r & ~15];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cv[e] = from_f<T>(to_f(cr[e]) * exp2f_fast(an2[n0 + e] * dc));
+        }
+        if (J * 64 + r < len) {
+            const v8 br = ld8(brows + (int64_t)(J * 64 + r) * G * N + n0);
+            const float db = cj[r | 15] - cj[r];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[e] = from_f<T>(to_f(br[e]) * exp2f_fast(an2[n0 + e] * db));
+        }
+        st8(&Cs[r * LDN + n0], cv);
+        st8(&Bs[r * LDN + n0], bv);
+    }
+    __syncthreads();
+    float amax = 0.f;  // widest per-n decay rate, for the diagonal sub-block split
+    for (int n = 0; n < N; ++n) amax = fmaxf(amax, -an2[n]);
+    const float Dh = D ? D[h] : 0.f;
+    T* out = tab + (bh * nc + c) * (int64_t)Q * Q;
+    const int sI = 16 * w;  // this wave's sub-block row (local rows sI .. sI + 15 of block I)
+    const int i = I * 64 + sI + l16;
+    for (int J16 = 0; J16 < 4; ++J16) {
+        const bool on_diag = I == J && J16 == w;
+        if (I == J && J16 > w) {  // above the diagonal: zeros (the output kernel reads them)
+            st4(out + (int64_t)i * Q + J * 64 + 16 * J16 + 4 * q, v4{});
+            continue;
+        }
+        const int eJ = 16 * J16 + 15;
+        f32x4 gt = f32x4{0.f, 0.f, 0.f, 0.f};  // lane: G^T[j = 16 J16 + 4q + r][i = sI + l16]
+        if (!on_diag || amax * (cj[eJ] - ci[sI]) <= 80.f * LOG2E) {
+            const float dm = ci[sI] - cj[eJ];
+#pragma unroll
+            for (int n0 = 0; n0 < N; n0 += 32) {
+                const int nn = n0 + 8 * q;
+                const bool nv = (N % 32 == 0) || (nn < N);
+                v8 a = zero8<T>(), b = zero8<T>();
+                if (nv) {
+                    a = ld8(&Bs[(16 * J16 + l16) * LDN + nn]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a[e] = from_f<T>(to_f(a[e]) * exp2f_fast(an2[nn + e] * dm));
+                    b = ld8(&Cs[(sI + l16) * LDN + nn]);
+                }
+                gt = mma(gt, a, b);
+            }
+        } else {
+            // direct sums for this lane's 4 entries (i, j = J 64 + 16 J16 + 4q + r)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int jl = 16 * J16 + 4 * q + r, j = J * 64 + jl;
+                float sum = 0.f;
+                if (j <= i && i < len) {
+                    const T* cr = crows + (int64_t)i * G * N;
+                    const T* br = brows + (int64_t)j * G * N;
+                    const float dd = ci[sI + l16] - cj[jl];
+                    for (int n = 0; n < N; ++n) sum += to_f(cr[n]) * to_f(br[n]) * exp2f_fast(an2[n] * dd);
+                }
+                gt[r] = sum;
+            }
+        }
+        v4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = J * 64 + 16 * J16 + 4 * q + r;
+            float m = gt[r];
+            if (on_diag) m = (j > i) ? 0.f : (j == i ? m + Dh : m);
+            v[r] = from_f<T>(m);
+        }
+        st4(out + (int64_t)i * Q + J * 64 + 16 * J16 + 4 * q, v);
     }
 }
 

@@ -19,7 +19,7 @@ struct RunArgs {
     void* y;
     float* hT;
     float* cdt;     // [b,H,nc,Q]
-    void* cb;       // [b,nc,G,Q,Q]  (scalar decay only)
+    void* cb;       // [b,nc,G,Q,Q] (scalar decay); [b,H,nc,Q,Q] (diagonal decay, table path)
     float* states;  // [b,H,nc,P,N]
     void* hin;      // [b,H,nc,P,N]
     void* bt;       // [b,nc,G,N,Q]  (scalar decay only)
@@ -80,6 +80,15 @@ inline Rows rows_of(const RunArgs& a) {
     return r;
 }
 
+// The diagonal decay's output kernel keeps a chunk's x rows and its rescaled C and B rows
+// in LDS (OutSmem<T, P, N, true>).  Where they do not fit one CU's 160 KiB, k_gtab forms
+// each (b, h, c)'s decay-weighted query-key block as a table in the workspace (the cb
+// region) and the output kernel reads it instead.
+inline bool diag_uses_table(int64_t Q, int64_t P, int64_t N, size_t es) {
+    const size_t bytes = (size_t)(Q * (P + 8) + 2 * Q * (N + 8)) * es + (size_t)(2 * Q + N) * 4;
+    return bytes > 160 * 1024;
+}
+
 template <int Q, int N>
 void launch_fused(const RunArgs& a) {
     const int BH = (int)(a.b * a.H);
@@ -109,7 +118,10 @@ int run(const RunArgs& a) {
     T* y = static_cast<T*>(a.y);
 
     // the output kernel's LDS must fit one CU (160 KiB); checked before any launch
-    const size_t smem = a.diag ? OutSmem<T, P, N, true>::bytes(Q) : OutSmem<T, P, N, false>::bytes(Q);
+    const bool tab = a.diag && diag_uses_table(Q, P, N, sizeof(T));
+    const size_t smem = !a.diag ? OutSmem<T, P, N, false>::bytes(Q)
+                        : tab   ? OutSmem<T, P, N, true, true>::bytes(Q)
+                                : OutSmem<T, P, N, true>::bytes(Q);
     if (smem > 160 * 1024) return 3;
 
     // the prep kernels run over the global chunk axis (blocks past the last chunk exit)
@@ -141,6 +153,12 @@ int run(const RunArgs& a) {
         const int nb = Q / 64;
         const dim3 g2(kc, nb * (nb + 1) / 2, (unsigned)G);
         k_cb<T, N><<<g2, kThreads, 0, s>>>(Bm, Cm, cb, rows, G, Q);
+    } else if (tab && (st & 2)) {
+        const int nb = Q / 64;
+        const size_t gsm = gtab_smem<T, N>();
+        hipFuncSetAttribute((const void*)k_gtab<T, N>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)gsm);
+        k_gtab<T, N><<<dim3((unsigned)(a.b * H * nc), (unsigned)(nb * (nb + 1) / 2)), kThreads, gsm, s>>>(
+            Bm, Cm, a.A, a.D, a.cdt, cb, a.T, H, G, Q, nc);
     }
     const dim3 g3((unsigned)(a.b * H * nc));
     if (!(st & 4)) {
@@ -178,6 +196,10 @@ int run(const RunArgs& a) {
     }
 
     if (!(st & 16)) {
+    } else if (tab) {
+        hipFuncSetAttribute((const void*)k_out<T, P, N, true, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem);
+        k_out<T, P, N, true, true><<<g3, kThreads, smem, s>>>(x, Bm, Cm, cb, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);
     } else if (a.diag) {
         hipFuncSetAttribute((const void*)k_out<T, P, N, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         k_out<T, P, N, true><<<g3, kThreads, smem, s>>>(x, Bm, Cm, nullptr, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);

@@ -61,6 +61,13 @@ def kernel_bytes(b, T, H, P, N, G, Q, es, diag=False, h0=True) -> dict:
     }
 
 
+def gtab_bytes(b, T, H, G, N, Q, es) -> int:
+    """The diagonal decay's table kernel: B and C rows of each (batch, head, chunk) block
+    pair read once per head, the lower 64 x 64 blocks of the table written."""
+    nc = -(-T // Q)
+    nb = Q // 64
+    return 2 * b * H * T * N * es + b * H * nc * (nb * (nb + 1) // 2) * 64 * 64 * es
+
 def path_min_bytes(b, T, H, P, N, G, es, h0=True) -> int:
     return 2 * b * T * H * P * es + 2 * b * T * G * N * es + b * T * H * 4 + \
         (2 if h0 else 1) * b * H * P * N * 4

@@ -164,10 +164,21 @@ def test_error_paths_return_before_any_launch(diag):
     assert ssd._load().ssd_scan_fwd(None, *([None] * 10), 0, None) == ssd_status("SSD_ERR_NULL")
 
 
-def test_diag_output_kernel_lds_limit_is_unsupported():
-    """The diagonal-decay output kernel keeps rescaled C and B rows of a chunk in LDS;
-    a (chunk, dstate) pair that does not fit 160 KiB is reported, not launched."""
-    assert call(prob(P=64, N=256, Q=256), True)[0] == ssd_status("SSD_ERR_UNSUPPORTED")
+def test_diag_table_path_workspace():
+    """The diagonal-decay output kernel keeps a chunk's x rows and rescaled C and B rows in
+    LDS where they fit 160 KiB; otherwise a table kernel writes each (batch, head, chunk)'s
+    decay-weighted query-key block into the cb region, batch * nheads * nchunks * chunk^2
+    elements, which the output kernel reads (host arithmetic only)."""
+    for (P, N, Q, dt, es) in ((64, 128, 256, ssd.SSD_BF16, 2), (64, 256, 256, ssd.SSD_BF16, 2),
+                              (128, 256, 128, ssd.SSD_F32, 4), (64, 64, 128, ssd.SSD_BF16, 2)):
+        p = prob(b=2, T=600, H=4, P=P, N=N, G=2, Q=Q, dtype=dt)
+        nc = -(-600 // Q)
+        lay = ssd.workspace_layout(p, True)
+        tab = ssd.diag_uses_table(Q, P, N, dt)
+        assert tab == ((Q * (P + 8) + 2 * Q * (N + 8)) * es + (2 * Q + N) * 4 > 160 * 1024)
+        assert lay["cb_bytes"] == (2 * 4 * nc * Q * Q * es if tab else 0), (P, N, Q)
+        assert lay["states_bytes"] == 2 * 4 * nc * P * N * 4
+    assert ssd.diag_uses_table(256, 64, 128, ssd.SSD_BF16) and not ssd.diag_uses_table(128, 64, 64, ssd.SSD_BF16)
 
 
 def test_schedule_flags_validated():

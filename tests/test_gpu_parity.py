@@ -38,6 +38,11 @@ SMALL = [  # b, T, H, P, N, G, Q, dtype, diag, h0, D
     (1, 517, 2, 64, 64, 1, 128, "bf16", True, True, True),
     (1, 200, 2, 32, 128, 1, 64, "bf16", True, False, True),
     (1, 150, 2, 64, 32, 1, 256, "bf16", True, True, False),
+    # diagonal decay through the table of decay-weighted products (LDS tile over 160 KiB)
+    (1, 700, 3, 64, 128, 1, 256, "bf16", True, True, True),
+    (2, 300, 4, 64, 256, 2, 256, "bf16", True, True, True),
+    (1, 333, 2, 128, 256, 1, 128, "f32", True, True, False),
+    (2, 129, 2, 16, 256, 2, 256, "f32", True, False, True),
 ]
 
 
@@ -157,7 +162,7 @@ def full_reference(w, **kw):
     """Inputs and the oracle's (y, hT) for a whole workload, computed once per process (the
     oracle does not depend on the chunk size or the schedule, so every run of the
     workload is compared with the same reference)."""
-    key = (w.name, w.seqlen, tuple(sorted(kw.items())))
+    key = (w.name, w.seqlen, w.diag, tuple(sorted(kw.items())))
     if key not in _FULL:
         _FULL.clear()  # one whole workload's reference held at a time
         inp = make_inputs(w, **kw)
@@ -211,6 +216,18 @@ def test_diag_equal_decays_match_scalar_kernel():
     ref = oracle_ref(s, False)
     check((yd, hd), ref, "bf16", "diag-equal vs oracle scalar")
     check((ys, hs), ref, "bf16", "scalar kernel vs oracle scalar")
+
+
+def test_diag_decay_at_the_layer_shape_full_parity():
+    """The diagonal decay at the 2.7B layer shape (b8 T4096 H80 P64 N128 Q256, bf16,
+    A[h, n] drawn per head and state dimension, nonzero h0): its output tile does not fit
+    LDS, so it runs through the table of decay-weighted products; every (batch, head)
+    slice of y and hT against the oracle."""
+    w = M2P7B.with_(diag=True)
+    print(f"[workload] {w.name} diagonal decay", flush=True)
+    prob = ssd.make_problem(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, ssd.SSD_BF16)
+    assert ssd.workspace_layout(prob, True)["cb_bytes"] > 0  # the table path
+    full_parity(w, w.chunk)
 
 
 @pytest.mark.parametrize("diag", [False, True])
