@@ -334,9 +334,9 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             // accumulators move in.
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                __builtin_amdgcn_sched_barrier(0);
+                // (no scheduling fences here or in the state update's k-step loop: letting
+                // the compiler interleave neighbouring k-steps measured 2% faster)
                 if (u + GW < NU) gf[u + GW] = bload8(rcb, vq, gf_off(c, u + GW, tA, tB));
-                __builtin_amdgcn_sched_barrier(0);
                 const bool inA = TPP == 1 || u < KA;
                 if (TPP == 1 && u >= KA) break;
                 if (TPP == 2 && u == KA) {
@@ -394,12 +394,10 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             for (int a = 0; a < SN; ++a) bt[ks][a] = bload8(rbt, a == 0 ? vq : vq1, sbt + ks * 64);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            __builtin_amdgcn_sched_barrier(0);
             if (ks + 2 < KS) {
 #pragma unroll
                 for (int a = 0; a < SN; ++a) bt[(ks + 2) % 3][a] = bload8(rbt, a == 0 ? vq : vq1, sbt + (ks + 2) * 64);
             }
-            __builtin_amdgcn_sched_barrier(0);
             const int j0 = ks * 32 + 8 * q;
             bf16x8 bw[SN];
 #pragma unroll

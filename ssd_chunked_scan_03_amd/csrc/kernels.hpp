@@ -861,8 +861,14 @@ struct OutSmem {
     }
 };
 
+// Work-groups per CU the output kernel is compiled for: three for bfloat16 up to headdim 64
+// (its registers then fit 168 per lane without spills; two per CU left latency exposed:
+// 371 -> 327 us at the 2.7B layer's split schedule), else what its tile needs.
+template <typename T, int P>
+constexpr int out_min_blocks() { return (sizeof(T) == 2 && P <= 64) ? 3 : 1; }
+
 template <typename T, int P, int N, bool DIAG, bool TAB = false>
-__global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const T* __restrict__ Bm,
+__global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(const T* __restrict__ x, const T* __restrict__ Bm,
                                                   const T* __restrict__ Cm, const T* __restrict__ cb,
                                                   const T* __restrict__ hin, const float* __restrict__ A,
                                                   const float* __restrict__ D,
@@ -904,7 +910,7 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
 
     auto row_tile = [&](int k) { return (rpw == 1) ? w : ((k & 1) ? 8 * (k >> 1) + 7 - w : 8 * (k >> 1) + w); };
 
-    // 1. x rows of the chunk: issue the loads now, store them to LDS after the state term
+    // 1. x rows of the chunk, loaded and stored to LDS before the state term
     constexpr int XR = (256 * P / 8 + kThreads - 1) / kThreads;  // enough for Q = 256
     const int XV = Q * P / 8;
     v8 xv[XR];
@@ -917,18 +923,23 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
     }
     float cdv = 0.f;
     if (tid < Q) cdv = cd[tid];
+    // x rows to LDS now, so their registers are free during the state term
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+        const int v = tid + r * kThreads;
+        if (v < XV) {
+            const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
+            st8(Xs + XL::off(jj, p0), xv[r]);
+        }
+    }
 
     f32x4 acc[4][PT];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // C B^T fragments of a row tile (scalar decay).  bfloat16: the first tile's are
-    // requested before the state term, each next tile's while the current one computes.
-    // float32 fragments take twice the registers, so there each tile's are requested
-    // just before its own k-steps (a second set would cost occupancy and spill at
-    // headdim 128).
-    constexpr bool PF = sizeof(T) == 2;
+    // C B^T fragments of a row tile, requested just before its own k-steps (a second set
+    // in flight ahead of use costs the registers of a third work-group per CU)
     // scalar decay: the group's C B^T table; diagonal decay (TAB): this head's table of
     // decay-weighted products, D on its diagonal
     const T* cbb_pf = cb + (TAB ? bh * nc + c : (bi * nc + c) * G + g) * (int64_t)Q * Q;
@@ -939,8 +950,7 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbrow + (ks < nks ? ks : nks - 1) * 32 + 8 * q);
     };
-    v8 gfa[8], gfb[PF ? 8 : 1];
-    if (SCAL && PF) load_gf(0, gfa);
+    v8 gfa[8];
 
     // 2. state term y^T[p][i] += sum_n H[p][n] C[i][n] from raw fragments (scalar decay:
     //    the row factor exp(A cdt_i) follows in step 4); diagonal decay with a table:
@@ -982,15 +992,7 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
         }
     }
 
-    // 3. x -> LDS (row-major), chunk decay tables
-#pragma unroll
-    for (int r = 0; r < XR; ++r) {
-        const int v = tid + r * kThreads;
-        if (v < XV) {
-            const int jj = v / (P / 8), p0 = (v - jj * (P / 8)) * 8;
-            st8(Xs + XL::off(jj, p0), xv[r]);
-        }
-    }
+    // 3. chunk decay tables
     if (tid < Q) cds[tid] = cdv;
     if (SM::RESCALED)
         for (int n = tid; n < N; n += kThreads) an2[n] = A[h * N + n] * LOG2E;
@@ -1036,12 +1038,7 @@ __global__ __launch_bounds__(kThreads) void k_out(const T* __restrict__ x, const
                 const int i = rt * 16 + l16;
                 const int nks = rt / 2 + 1;  // k-steps of 32 tokens up to this row tile
                 v8* gf = gfa;
-                if constexpr (PF) {
-                    gf = (k & 1) ? gfb : gfa;
-                    if (k + 1 < rpw) load_gf(k + 1, (k & 1) ? gfa : gfb);
-                } else {
-                    load_gf(k, gfa);
-                }
+                load_gf(k, gfa);
                 const float ci = cds[i];
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks) {
