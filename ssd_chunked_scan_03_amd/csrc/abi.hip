@@ -396,12 +396,13 @@ int step(const ssd_problem* p, int diag, const void* x, const float* dt, const f
 // ---- backward pass (ssd_scan_bwd) ----
 struct BwdLayout {
     size_t cdt, cb, cbt, bt, ct, states, hin, rin, hTf, ds, dDp, dAp, kpart, zh, yh, dxp, ddtp, total;
+    bool has_states;  // (the chunk walks need no chunk-state region)
 };
 
-// Scalar decay: C B^T tables, per-token decay terms and boundary partials.  Diagonal decay:
-// per-token Zh / Yh of every head and, when dstate is split over several waves, per-slice
-// partials of dx and ddt.  Both: cumulative dt, chunk states, H_c, R_c, hT and the
-// per-chunk partial sums of dA and dD.
+// Scalar decay: C B^T tables, per-token decay terms and boundary partials, and the chunk
+// states unless the chunk walks run.  Diagonal decay: per-token Zh / Yh of every head and,
+// when dstate is split over several waves, per-slice partials of dx and ddt, and the chunk
+// states.  Both: cumulative dt, H_c, R_c, hT and the per-chunk partial sums of dA and dD.
 BwdLayout bwd_layout_of(const ssd_problem* p, int diag) {
     BwdLayout L;
     memset(&L, 0, sizeof(L));
@@ -418,6 +419,7 @@ BwdLayout bwd_layout_of(const ssd_problem* p, int diag) {
         const int nsl = ssd::diag_bwd_slices(P, N);
         take(L.cdt, bhc * (size_t)Q * 4);
         take(L.states, bhc * (size_t)(P * N) * 4);
+        L.has_states = true;
         take(L.hin, bhc * (size_t)(P * N) * es);
         take(L.rin, bhc * (size_t)(P * N) * es);
         take(L.hTf, (size_t)(b * H * P * N) * 4);
@@ -437,7 +439,9 @@ BwdLayout bwd_layout_of(const ssd_problem* p, int diag) {
     take(L.cbt, bgc * (size_t)(Q * Q) * es);
     take(L.bt, bgc * (size_t)(N * Q) * es);
     take(L.ct, bgc * (size_t)(N * Q) * es);
-    take(L.states, bhc * (size_t)(P * N) * 4);
+    // chunk states (and the adjoint's chunk inputs) only where the chunk walks do not run
+    L.has_states = !ssd::walks_apply(p->dtype == SSD_BF16, b, T, H, P, N, G, Q);
+    if (L.has_states) take(L.states, bhc * (size_t)(P * N) * 4);
     take(L.hin, bhc * (size_t)(P * N) * es);
     take(L.rin, bhc * (size_t)(P * N) * es);
     take(L.hTf, (size_t)(b * H * P * N) * 4);
@@ -540,7 +544,7 @@ int scan_bwd(const ssd_problem* p, int diag, const void* x, const float* dt, con
     a.cbt = w + L.cbt;
     a.bt = w + L.bt;
     a.ct = w + L.ct;
-    a.states = reinterpret_cast<float*>(w + L.states);
+    a.states = L.has_states ? reinterpret_cast<float*>(w + L.states) : nullptr;
     a.hin = w + L.hin;
     a.rin = w + L.rin;
     a.hTf = reinterpret_cast<float*>(w + L.hTf);

@@ -678,7 +678,11 @@ __global__ __launch_bounds__(kBcThreads) void k_bwd_bc(const T* __restrict__ x, 
     float* scj = sci + Q;  // exp(A (cdt_last - cdt_j))
 
     const int nslab = Q / 64;
+    // blocks k, k+8, k+16, ... run on one XCD: give each XCD a contiguous range of the
+    // (b, c, g, slab, n range) grid, so that the slabs of one chunk, which stage the same
+    // heads' H, R, dy and x tiles, share an L2
     int64_t blk = blockIdx.x;
+    if (gridDim.x % 8 == 0) blk = (blk % 8) * (gridDim.x / 8) + blk / 8;
     const int nr = (int)(blk % NR);
     blk /= NR;
     const int s = (int)(blk % nslab);

@@ -3,6 +3,9 @@
 
 #include "bwd.hpp"
 #include "bwd_diag.hpp"
+#include "walk.hpp"
+
+#include <type_traits>
 
 namespace ssd {
 
@@ -46,6 +49,32 @@ struct BwdArgs {
     float* ddtp;    // [nsl,b,T,H]   per-slice partials of ddt
     hipStream_t stream;
 };
+
+// The chunk-pipelined walks (walk.hpp) take both state recurrences when there are enough
+// (batch, head) chains to occupy every CU and the shape is theirs: bfloat16, headdim 64,
+// dstate 64 or 128, and buffer offsets of a batch row within 32 bits.  (The workspace
+// layout takes the same decision: the walks need no chunk-state region.)
+inline bool walks_apply(bool bf16_dtype, int64_t b, int64_t T, int64_t H, int64_t P, int64_t N, int64_t G,
+                        int64_t Q) {
+    const int64_t lim = (int64_t)1 << 31, nc = (T + Q - 1) / Q;
+    return bf16_dtype && P == 64 && (N == 64 || N == 128) && b * H >= 512 && T * H * P * 2 < lim &&
+           nc * G * N * Q * 2 < lim;
+}
+template <typename T, int P, int N>
+bool walk_applies(const BwdArgs& a) {
+    return walks_apply(std::is_same<T, bf16>::value, a.b, a.T, a.H, P, N, a.G, a.Q);
+}
+
+template <int Q, int N>
+void launch_walks(const BwdArgs& a, const bf16* x, const bf16* dy, const bf16* bt, const bf16* ct, bf16* hin,
+                  bf16* rin, int nslot) {
+    const unsigned nb = (unsigned)(a.b * a.H);
+    const int H = (int)a.H, G = (int)a.G, nc = (int)a.nc, nrows = (int)a.b;
+    k_walk<Q, N, false><<<nb, kThreads, 0, a.stream>>>(x, bt, a.A, a.cdt, a.h0, hin, a.dhT ? a.hTf : nullptr,
+                                                       nullptr, nullptr, nullptr, 0, a.T, nrows, H, G, nc);
+    k_walk<Q, N, true><<<nb, kThreads, 0, a.stream>>>(dy, ct, a.A, a.cdt, a.dhT, rin, a.dh0, hin,
+                                                      a.dhT ? a.hTf : nullptr, a.kpart, nslot, a.T, nrows, H, G, nc);
+}
 
 template <typename T, int P, int N>
 int run_bwd(const BwdArgs& a) {
@@ -92,12 +121,27 @@ int run_bwd(const BwdArgs& a) {
     k_bt<T, N><<<g6, kThreads, 0, s>>>(Cm, ct, rows, G, Q);
     const dim3 g3((unsigned)(a.b * H * nc));
     const int per_head = (int)((a.P * a.N / 4 + kThreads - 1) / kThreads);
-    // the forward states: with many (b, h) chains, each chain's chunks walked with the state
-    // in registers; else chunk states, then the scan
-    if (a.b * H >= 512) {
+    int nvalid = (int)(a.P * a.N / 4 / 64);  // partials of <R_c, H_{c+1}> per chunk
+    bool walked = false;
+    if constexpr (std::is_same<T, bf16>::value && P == 64 && (N == 64 || N == 128)) {
+        if (walk_applies<T, P, N>(a)) {
+            // both recurrences walked chunk by chunk, the states on chip
+            switch (Q) {
+                case 64: launch_walks<64, N>(a, x, dy, bt, ct, hin, rin, per_head * 4); break;
+                case 128: launch_walks<128, N>(a, x, dy, bt, ct, hin, rin, per_head * 4); break;
+                case 256: launch_walks<256, N>(a, x, dy, bt, ct, hin, rin, per_head * 4); break;
+                default: return 3;
+            }
+            nvalid = 4;  // one partial per wave
+            walked = true;
+        }
+    }
+    // otherwise the forward states: with many (b, h) chains, each chain's chunks walked with
+    // the state in registers; else chunk states, then the scan
+    if (!walked && a.b * H >= 512) {
         k_states<T, P, N><<<(unsigned)(a.b * H), kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.h0, hin,
                                                                    a.dhT ? a.hTf : nullptr, a.T, H, G, Q, nc);
-    } else {
+    } else if (!walked) {
         k_state<T, P, N, false, false><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
         const int64_t BHPN = a.b * H * a.P * a.N;
         const dim3 g4((unsigned)(a.b * H * per_head));
@@ -106,11 +150,13 @@ int run_bwd(const BwdArgs& a) {
                                                     per_head, nc, BHPN);
     }
     // the adjoint: chunk inputs (into the chunk-state buffer), reverse scan
-    const dim3 g4((unsigned)(a.b * H * per_head));
-    k_state<T, P, N, false, true><<<g3, kThreads, 0, s>>>(dy, Cm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
-    k_scan_rev<T><<<g4, kThreads, 0, s>>>(a.states, rin, a.dh0, a.dhT, a.A, a.cdt, hin, a.hTf, a.kpart, H,
-                                          (int)(a.P * a.N), (int)a.N, Q, nc, per_head);
-    const int nslot = per_head * 4, nvalid = (int)(a.P * a.N / 4 / 64);  // partials per chunk; waves with elements
+    if (!walked) {
+        const dim3 g4((unsigned)(a.b * H * per_head));
+        k_state<T, P, N, false, true><<<g3, kThreads, 0, s>>>(dy, Cm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
+        k_scan_rev<T><<<g4, kThreads, 0, s>>>(a.states, rin, a.dh0, a.dhT, a.A, a.cdt, hin, a.hTf, a.kpart, H,
+                                              (int)(a.P * a.N), (int)a.N, Q, nc, per_head);
+    }
+    const int nslot = per_head * 4;  // partials' stride per chunk
     // gradients
     (void)hipFuncSetAttribute((const void*)k_bwd_x<T, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sx);
     k_bwd_x<T, P, N><<<g3, kThreads, sx, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,

@@ -93,6 +93,15 @@ __device__ __forceinline__ brsrc make_rsrc(const void* base, uint32_t bytes) {
     void* p = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
+// Lane index recomputed from the execution mask (two VALU ops) instead of kept live:
+// values needed only at chunk boundaries are rebuilt there rather than spilled.
+__device__ __forceinline__ int lane_now() {
+    int l;
+    // volatile: recomputed where it is used, never hoisted and kept live
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // wave index within the work-group, known uniform to the compiler
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 __device__ __forceinline__ bf16x8 bload8(brsrc r, int voff, int soff) {

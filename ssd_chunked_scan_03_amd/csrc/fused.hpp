@@ -72,15 +72,6 @@ __device__ __forceinline__ int xs_dma_lane(int lane, int bit, int XS, int hcol) 
 }
 __device__ __forceinline__ int xs_dma_bit(int m) { return (m ^ (m >> 1)) & 1; }
 
-// Lane index recomputed from the execution mask (two VALU ops) instead of kept live:
-// values needed only at chunk boundaries are rebuilt there rather than spilled.
-__device__ __forceinline__ int lane_now() {
-    int l;
-    // volatile: recomputed where it is used, never hoisted and kept live
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-    return l;
-}
-
 template <int Q, int N>
 __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ x, const bf16* __restrict__ Cm,
                                                     const bf16* __restrict__ cb, const bf16* __restrict__ Bt,
@@ -245,13 +236,16 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) acc_h[a][pt] *= dch;
 
+        // B^T fragments of the state update (the first two are requested during the last pass)
+        const int sbt = __builtin_amdgcn_readfirstlane(((c * G + g) * N * Q + w * SN * 16 * Q) * 2);
+        bf16x8 bt[3][SN];
+
         // ---- output passes ----
 #pragma unroll
         for (int pass = 0; pass < NPASS; ++pass) {
             int tA, tB;
             pass_tiles(pass, tA, tB);
             const int KA = tA / 2 + 1, KB = tB / 2 + 1;  // k-steps of each tile (last = diagonal)
-            if (pass > 0) issue_front(fr, c, pass);
             __builtin_amdgcn_sched_barrier(0);
 
             // the second tile's C rows, requested now and consumed after the first tile's
@@ -377,21 +371,27 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) acc[0][pt] = mma(acc[0][pt], frag_xs_o(Xs, xo[pt], ks * 32), m);
             }
+            // What the next phase reads first is requested before the pass's last y store:
+            // the memory counter retires accesses in order, so a load issued after a store
+            // cannot be waited for without waiting for the store too.
+            __builtin_amdgcn_sched_barrier(0);
+            if (pass + 1 < NPASS) {
+                issue_front(fr, c, pass + 1);
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 2 && ks < KS; ++ks)
+#pragma unroll
+                    for (int a = 0; a < SN; ++a) bt[ks][a] = bload8(rbt, a == 0 ? vq : vq1, sbt + ks * 64);
+                // the next chunk's cdt row: every wave read this chunk's at the chunk top
+                if (c + 1 < nc) dma_cdt(c + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             store_y(acc[0], TPP == 2 ? tB : tA);
         }
 
-        // the next chunk's cdt row: every wave read this chunk's at the chunk top
-        __builtin_amdgcn_sched_barrier(0);
-        if (c + 1 < nc) dma_cdt(c + 1);
         // ---- state update H_{c+1} = exp(A cdt_last) H_c + B^T diag(w) X_c, B^T fragments
         //      requested two k-steps ahead ----
         __builtin_amdgcn_sched_barrier(0);
-        const int sbt = __builtin_amdgcn_readfirstlane(((c * G + g) * N * Q + w * SN * 16 * Q) * 2);
-        bf16x8 bt[3][SN];
-#pragma unroll
-        for (int ks = 0; ks < 2 && ks < KS; ++ks)
-#pragma unroll
-            for (int a = 0; a < SN; ++a) bt[ks][a] = bload8(rbt, a == 0 ? vq : vq1, sbt + ks * 64);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 2 < KS) {
@@ -416,8 +416,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
         if (c + 1 < nc) issue_front(fr, c + 1, 0);
         __syncthreads();  // every wave is done with Xs, Hs and the tables of this chunk
         if (c + 1 < nc) {
-            stage_tables();
             dma_x(c + 1);
+            stage_tables();
         }
     }
     if (hT) {

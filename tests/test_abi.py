@@ -376,6 +376,28 @@ def test_bwd_workspace_arithmetic():
     assert ssd.bwd_workspace_bytes(p) == 0
 
 
+def test_bwd_workspace_without_chunk_states_when_the_walks_run():
+    """With 512 or more (batch, head) chains at bfloat16, headdim 64 and dstate 64 / 128 the
+    chunk walks carry both recurrences on chip: no float32 chunk-state region (335 MB at the
+    2.7B layer shape); float32, other headdims and fewer chains keep it."""
+    a = lambda n: (n + 255) // 256 * 256
+
+    def want(b, T, H, P, N, G, Q, es, states):
+        nc = -(-T // Q)
+        return (a(b * H * nc * Q * 4) + 2 * a(b * nc * G * Q * Q * es) + 2 * a(b * nc * G * N * Q * es)
+                + (a(b * H * nc * P * N * 4) if states else 0) + 2 * a(b * H * nc * P * N * es)
+                + a(b * H * P * N * 4) + a(b * H * nc * Q * 4) + 2 * a(b * H * nc * 4)
+                + a(b * H * nc * 4 * ((P * N // 4 + 255) // 256) * 4))
+
+    layer = (8, 4096, 80, 64, 128, 1, 256)
+    assert ssd.bwd_workspace_bytes(ssd.make_problem(*layer, ssd.SSD_BF16)) == want(*layer, 2, False)
+    assert ssd.bwd_workspace_bytes(ssd.make_problem(*layer, ssd.SSD_F32)) == want(*layer, 4, True)
+    for shape, walks in (((8, 300, 64, 64, 64, 4, 128), True), ((1, 100, 515, 64, 64, 5, 64), True),
+                         ((8, 300, 63, 64, 64, 3, 128), False), ((8, 300, 64, 32, 64, 4, 128), False),
+                         ((8, 300, 64, 64, 256, 4, 128), False)):
+        assert ssd.bwd_workspace_bytes(ssd.make_problem(*shape, ssd.SSD_BF16)) == want(*shape, 2, not walks), shape
+
+
 def test_bwd_error_paths_return_before_any_launch():
     p = prob()
     S = ssd_status

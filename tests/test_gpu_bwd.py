@@ -109,6 +109,17 @@ CASES = [  # b, T, H, P, N, G, Q, dtype
     # 512 (batch, head) chains: the forward states walk each chain's chunks (k_states)
     (8, 300, 64, 32, 64, 4, 128, "bf16"),
     (8, 200, 64, 16, 32, 2, 64, "f32"),
+    # 512 or more chains, bfloat16, headdim 64, dstate 64 / 128: both recurrences walked
+    # chunk by chunk with the state on chip (k_walk), every chunk size, ragged T down to a
+    # one-token last chunk, a chain count that is not a multiple of 8 (no XCD remapping of
+    # blocks).  (Not T = 1 with hundreds of slices: a one-token slice of ddt is a single
+    # value, often a near-cancellation of the boundary value against the token's own term,
+    # so its relative error measures the cancellation, not the kernels.)
+    (8, 300, 64, 64, 64, 4, 128, "bf16"),
+    (8, 260, 64, 64, 128, 2, 256, "bf16"),
+    (4, 130, 128, 64, 128, 1, 64, "bf16"),
+    (8, 257, 64, 64, 128, 1, 256, "bf16"),
+    (1, 100, 515, 64, 64, 5, 64, "bf16"),
 ]
 
 
@@ -128,6 +139,17 @@ def test_bwd_optional_inputs(use_D, use_h0, use_dhT):
     gr = make_grads(2, 333, 4, 64, 64, seed=32, dtype="bf16")
     got, ref = run_bwd(inp, gr, "bf16", 128, use_D, use_h0, use_dhT)
     check(got, ref, "bf16", f"D={use_D} h0={use_h0} dhT={use_dhT}")
+
+
+@pytest.mark.parametrize("use_D,use_h0,use_dhT", [(False, False, False), (True, False, True), (False, True, False)])
+def test_bwd_walk_optional_inputs(use_D, use_h0, use_dhT):
+    """The chunk walks (512 chains, bfloat16, headdim 64) with D, h0 and dhT absent in turn:
+    no h0 starts the forward walk from zero, no dhT the adjoint walk (and every boundary value
+    of the last chunk is zero)."""
+    inp = make_small(8, 333, 64, 64, 64, 2, seed=33, dtype="bf16")
+    gr = make_grads(8, 333, 64, 64, 64, seed=33, dtype="bf16")
+    got, ref = run_bwd(inp, gr, "bf16", 128, use_D, use_h0, use_dhT)
+    check(got, ref, "bf16", f"walk D={use_D} h0={use_h0} dhT={use_dhT}")
 
 
 def test_bwd_layer_shapes():
