@@ -598,6 +598,247 @@ __global__ __launch_bounds__(kThreads) void k_bwd_x(const T* __restrict__ x, con
 }
 
 // ---------------------------------------------------------------------------
+// k_bwd_xs: what k_bwd_x computes, for bfloat16 at headdim 64 and dstate 64 or 128, laid
+// out like the fused forward kernel: the chunk's x (then dy) rows and its entering state
+// H_c (then the adjoint R_c) go straight into swizzled LDS tiles by direct transfers, so no
+// register holds them in flight; each wave then takes its row tiles one at a time (one
+// tile's accumulators live, not four), its state term from the LDS state tile and its
+// diagonal block from the C B^T (or transposed) table in L2, and dx leaves in whole rows.
+// That fits three work-groups per CU.  Per row tile, phase 1 keeps only dy_i . yhat_i (a
+// scalar per row) for phase 2's decay term.
+// ---------------------------------------------------------------------------
+template <int Q, int N>
+struct BxsCfg {
+    static constexpr int P = 64;
+    static constexpr int RPW = Q / 64;          // row tiles per wave
+    static constexpr int KS = Q / 32;           // 32-token k-steps per chunk
+    static constexpr int XR = Q / 32;           // 1 KB transfers per wave of a Q x 64 row tile
+    static constexpr int HR = N / 32;           // 1 KB transfers per wave of the 64 x N state tile
+    static constexpr int SRW = 512 / N;         // state rows per 1 KB transfer
+    static constexpr int NF = N / 32;           // 32-wide n-steps of the state term
+};
+
+template <int Q, int N>
+__global__ __launch_bounds__(kThreads, 3) void k_bwd_xs(const bf16* __restrict__ x, const bf16* __restrict__ dy,
+                                                     const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
+                                                     const bf16* __restrict__ cb, const bf16* __restrict__ cbt,
+                                                     const bf16* __restrict__ hin, const bf16* __restrict__ rin,
+                                                     const float* __restrict__ A, const float* __restrict__ D,
+                                                     const float* __restrict__ cdt, bf16* __restrict__ dx,
+                                                     float* __restrict__ ds, float* __restrict__ dDp, int64_t Tn,
+                                                     int H, int G, int nc) {
+    typedef BxsCfg<Q, N> CF;
+    constexpr int P = 64, RPW = CF::RPW, KS = CF::KS, XR = CF::XR, HR = CF::HR, SRW = CF::SRW, NF = CF::NF;
+    constexpr int PN = P * N, HSW = (N / 8) < 16 ? (N / 8) : 16;
+    constexpr float LOG2E = 1.4426950408889634f;
+    __shared__ __attribute__((aligned(16))) bf16 Ts[Q * P];   // x rows, then dy rows (swizzled)
+    __shared__ __attribute__((aligned(16))) bf16 Hs[P * N];   // H_c, then R_c (chunks swizzled by row)
+    __shared__ float cds[Q], u2[Q], v2[Q], red[4];
+
+    const int64_t blk = blockIdx.x;
+    const int c = (int)(blk % nc);
+    const int64_t bh = blk / nc;
+    const int h = (int)(bh % H);
+    const int64_t bi = bh / H;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), l16 = lane & 15, q = lane >> 4;
+    const float ah2 = A[h] * LOG2E;
+    const float Dh = D ? D[h] : 0.f;
+
+    // buffer resources based at this batch row (rows past T read as zero, stores dropped),
+    // the group's tables and this chain's states
+    const int XS = H * P * 2, CS = G * N * 2;  // row strides in bytes
+    const uint32_t xbytes = (uint32_t)(Tn * H * P * 2);
+    const brsrc rx = make_rsrc(x + bi * Tn * H * P, xbytes);
+    const brsrc rdy = make_rsrc(dy + bi * Tn * H * P, xbytes);
+    const brsrc rdx = make_rsrc(dx + bi * Tn * H * P, xbytes);
+    const brsrc rc = make_rsrc(Cm + bi * Tn * G * N, (uint32_t)(Tn * G * N * 2));
+    const brsrc rb = make_rsrc(Bm + bi * Tn * G * N, (uint32_t)(Tn * G * N * 2));
+    const uint32_t tbytes = (uint32_t)((int64_t)nc * G * Q * Q * 2);
+    const brsrc rcb = make_rsrc(cb + bi * nc * G * Q * Q, tbytes);
+    const brsrc rcbt = make_rsrc(cbt + bi * nc * G * Q * Q, tbytes);
+    const uint32_t sbytes = (uint32_t)((int64_t)nc * PN * 2);
+    const brsrc rh = make_rsrc(hin + bh * nc * PN, sbytes);
+    const brsrc rr = make_rsrc(rin + bh * nc * PN, sbytes);
+    const int hcol = h * P * 2;
+    const int tab0 = (c * G + g) * Q * Q * 2;                    // this chunk's table, bytes
+    const int vq = (l16 * Q + 8 * q) * 2;                        // table row l16 of a tile, k-group q
+    const int vc = l16 * CS + 8 * q * 2;                         // C / B row l16 of a tile, n-group q
+
+    // the chunk's rows (x or dy) and a state tile (H_c or R_c) into LDS, this wave's share
+    auto stage = [&](brsrc rrows, brsrc rstate) {
+        int ln = lane;  // opaque: the lane offsets are rebuilt per call, not kept live
+        asm volatile("" : "+v"(ln));
+        const int vd0 = xs_dma_lane(ln, 0, XS, hcol), vd1 = xs_dma_lane(ln, 1, XS, hcol);
+#pragma unroll
+        for (int r = 0; r < XR; ++r) {
+            const int m = w * XR + r;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rrows, (__attribute__((address_space(3))) void*)(Ts + m * 512), 16,
+                                                     xs_dma_bit(m) ? vd1 : vd0,
+                                                     __builtin_amdgcn_readfirstlane((c * Q + 8 * m) * XS), 0, 0);
+        }
+        // state transfer m: rows p = m SRW + l / (N / 8), LDS slot l % (N / 8) holding n-chunk
+        // slot ^ (p % HSW)
+#pragma unroll
+        for (int r = 0; r < HR; ++r) {
+            const int m = w * HR + r;
+            const int pr = ln / (N / 8), slot = ln % (N / 8), p = m * SRW + pr;
+            const int ch = slot ^ (p % HSW);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rstate, (__attribute__((address_space(3))) void*)(Hs + m * 512), 16,
+                                                     (pr * N + ch * 8) * 2,
+                                                     __builtin_amdgcn_readfirstlane((c * PN + m * SRW * N) * 2), 0, 0);
+        }
+    };
+    auto row_tile = [&](int k) { return (RPW == 1) ? w : ((k & 1) ? 8 * (k >> 1) + 7 - w : 8 * (k >> 1) + w); };
+    // state term of one row tile: acc^T[p][t] = sum_n S[p][n] V_t[n] (S in Hs, V = C or B rows)
+    auto state_term = [&](f32x4* acc, brsrc rv, int rt) {
+        bf16x8 vf[NF];
+        const int sv = __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * CS + g * N * 2);
+#pragma unroll
+        for (int n = 0; n < NF; ++n) vf[n] = bload8(rv, vc, sv + n * 64);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n = 0; n < NF; ++n)
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+                acc[pt] = mma(acc[pt], ld8(Hs + hs_off<N>(pt * 16 + l16, n * 32 + 8 * q)), vf[n]);
+    };
+
+    // ---- phase 1: yhat ----
+    stage(rx, rh);
+    if (tid < Q) {
+        const float* cd = cdt + (bh * nc + c) * (int64_t)Q;
+        const float cv = cd[tid], cr = cd[tid | 31], cs = cd[tid & ~31];
+        cds[tid] = cv;
+        u2[tid] = exp2f_fast(ah2 * (cr - cv));  // exp(A (cdt_{j|31} - cdt_j))
+        v2[tid] = exp2f_fast(ah2 * (cv - cs));  // exp(A (cdt_i - cdt_{i&~31}))
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's transfers have landed
+    __syncthreads();                    // ... every wave's, and the tables are in place
+    float p1[RPW];
+    float dd = 0.f;
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        const int rt = row_tile(k), i = rt * 16 + l16, nks = rt / 2 + 1;
+        bf16x8 gf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            if (ks < nks) gf[ks] = bload8(rcb, vq, __builtin_amdgcn_readfirstlane(tab0 + rt * 16 * Q * 2 + ks * 64));
+        f32x4 acc[4];
+        state_term(acc, rc, rt);
+        const float ci = cds[i];
+        const float sc = exp2f_fast(ah2 * ci);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] *= sc;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks < nks) {
+                const int j0 = ks * 32 + 8 * q;
+                bf16x8 mf;
+                if (ks < nks - 1) {
+                    const float vi = exp2f_fast(ah2 * (ci - cds[ks * 32 + 31]));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) mf[e] = (bf16)((float)gf[ks][e] * (u2[j0 + e] * vi));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = j0 + e;
+                        const float m = (float)gf[ks][e] * exp2f_fast(fminf(ah2 * (ci - cds[j]), 0.f));
+                        mf[e] = (bf16)(j <= i ? m : 0.f);
+                    }
+                }
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) acc[pt] = mma(acc[pt], frag_xs(Ts, ks * 32, pt * 16, lane), mf);
+                __builtin_amdgcn_sched_barrier(0);  // (hoisting every k-step's reads spills)
+            }
+        }
+        // dy_i . yhat_i (lane (i, q) holds p = 16 pt + 4 q + r), and dy . x for dD
+        const int sy = __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * XS);
+        float s = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            const bf16x4 dv = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                             rdy, l16 * XS + hcol + (pt * 16 + 4 * q) * 2, sy, 0));
+            const bf16x4 xv = ld4(Ts + xs_off(i, pt * 16 + 4 * q));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s += (float)dv[r] * acc[pt][r];
+                dd += (float)dv[r] * (float)xv[r];
+            }
+        }
+        p1[k] = sum_q(s);
+        __builtin_amdgcn_sched_barrier(0);  // one row tile's operands in flight at a time
+    }
+    // dD's partial now (left for the end, its operands would stay live through phase 2)
+    dd = sum_wave(dd);
+    if (lane == 0) red[w] = dd;
+    __syncthreads();  // every wave is done with the x rows and H_c
+
+    // ---- phase 2: dxhat, the decay term, dx ----
+    stage(rdy, rr);
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    __syncthreads();
+    const float clast = cds[Q - 1];
+    float* dsb = ds + (bh * nc + c) * (int64_t)Q;
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        const int rt = row_tile(k), j = rt * 16 + l16, kd = rt / 2;  // kd: the k-step holding the tile
+        bf16x8 gf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            if (ks >= kd) gf[ks] = bload8(rcbt, vq, __builtin_amdgcn_readfirstlane(tab0 + rt * 16 * Q * 2 + ks * 64));
+        f32x4 acc[4];
+        state_term(acc, rb, rt);
+        const float cj = cds[j];
+        const float sc = exp2f_fast(ah2 * (clast - cj));
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] *= sc;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks >= kd) {
+                const int i0 = ks * 32 + 8 * q;
+                bf16x8 mf;
+                if (ks > kd) {
+                    const float wj = exp2f_fast(ah2 * (cds[ks * 32] - cj));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) mf[e] = (bf16)((float)gf[ks][e] * (v2[i0 + e] * wj));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int i = i0 + e;
+                        const float m = (float)gf[ks][e] * exp2f_fast(fminf(ah2 * (cds[i] - cj), 0.f));
+                        mf[e] = (bf16)(i >= j ? m : 0.f);
+                    }
+                }
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) acc[pt] = mma(acc[pt], frag_xs(Ts, ks * 32, pt * 16, lane), mf);
+                __builtin_amdgcn_sched_barrier(0);  // (hoisting every k-step's reads spills)
+            }
+        }
+        // ds_j = dy_j . yhat_j - x_j . dxhat_j; dx = dxhat + D dy
+        const int sx = __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * XS);
+        float s = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            const bf16x4 xv = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                             rx, l16 * XS + hcol + (pt * 16 + 4 * q) * 2, sx, 0));
+            const bf16x4 dv = ld4(Ts + xs_off(j, pt * 16 + 4 * q));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s += (float)xv[r] * acc[pt][r];
+                acc[pt][r] += Dh * (float)dv[r];
+            }
+        }
+        s = sum_q(s);
+        if (q == 0) dsb[j] = p1[k] - s;
+        store_tile16(acc, rdx, sx, XS, hcol);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (tid == 0) dDp[bh * nc + c] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ---------------------------------------------------------------------------
 // k_bwd_bc: dB and dC of one (b, c, group) chunk, for the 64-row slab s of tokens and
 // the n range [n0, n0 + NB).  Loop over the group's heads:
 //   W   += L^h o (dy^h x^h^T)  on the tiles a slab needs: rows i in the slab with

@@ -157,10 +157,29 @@ int run_bwd(const BwdArgs& a) {
                                               (int)(a.P * a.N), (int)a.N, Q, nc, per_head);
     }
     const int nslot = per_head * 4;  // partials' stride per chunk
-    // gradients
-    (void)hipFuncSetAttribute((const void*)k_bwd_x<T, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sx);
-    k_bwd_x<T, P, N><<<g3, kThreads, sx, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
-                                              static_cast<T*>(a.dx), a.ds, a.dDp, a.T, H, G, Q, nc);
+    // gradients: dx and the per-token decay term (LDS-staged kernel where it applies)
+    bool xs_done = false;
+    if constexpr (std::is_same<T, bf16>::value && P == 64 && (N == 64 || N == 128)) {
+        const int64_t lim = (int64_t)1 << 31;
+        if (a.T * H * P * 2 < lim && a.T * G * N * 2 < lim && a.nc * G * Q * Q * 2 < lim && a.nc * P * N * 2 < lim) {
+            bf16* dxp = static_cast<bf16*>(a.dx);
+            switch (Q) {
+                case 64: k_bwd_xs<64, N><<<g3, kThreads, 0, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
+                                                                 dxp, a.ds, a.dDp, a.T, H, G, nc); break;
+                case 128: k_bwd_xs<128, N><<<g3, kThreads, 0, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
+                                                                   dxp, a.ds, a.dDp, a.T, H, G, nc); break;
+                case 256: k_bwd_xs<256, N><<<g3, kThreads, 0, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
+                                                                   dxp, a.ds, a.dDp, a.T, H, G, nc); break;
+                default: return 3;
+            }
+            xs_done = true;
+        }
+    }
+    if (!xs_done) {
+        (void)hipFuncSetAttribute((const void*)k_bwd_x<T, P, N>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sx);
+        k_bwd_x<T, P, N><<<g3, kThreads, sx, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
+                                                  static_cast<T*>(a.dx), a.ds, a.dDp, a.T, H, G, Q, nc);
+    }
     (void)hipFuncSetAttribute((const void*)k_bwd_bc<T, P, N, NB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sbc);
     const dim3 g7((unsigned)(a.b * nc * G * (Q / 64) * (N / NB)));
     k_bwd_bc<T, P, N, NB><<<g7, kBcThreads, sbc, s>>>(x, dy, bt, ct, hin, rin, a.A, a.cdt, static_cast<T*>(a.dB),

@@ -54,24 +54,6 @@ __device__ __forceinline__ int fused_tile(int pass, int t, int w) {
     return w;
 }
 
-template <int N>
-__device__ __forceinline__ int hs_off(int p, int n) {
-    constexpr int HSW = (N / 8) < 16 ? (N / 8) : 16;
-    return p * N + ((((n >> 3) ^ (p % HSW))) << 3) + (n & 7);
-}
-
-// Direct-to-LDS transfer m (1 KB) of a chunk's x tile fills LDS bytes [1024 m, 1024 m + 1024)
-// lane by lane: x-tile rows 8 m .. 8 m + 7, eight 16-byte slots each.  Lane l takes row
-// 8 m + l/8 and slot l % 8; the row swizzle decides which column chunk that slot holds.
-// Within the row the swizzle depends on (l/8) & 3 and on one bit of m (bit 0 ^ bit 1), so
-// a lane needs two source offsets, one per value of that bit; the row offset is uniform.
-__device__ __forceinline__ int xs_dma_lane(int lane, int bit, int XS, int hcol) {
-    const int r = lane >> 3, slot = lane & 7;
-    const int ch = ((((slot >> 1) ^ (r & 3) ^ bit)) << 1) | (slot & 1);
-    return r * XS + hcol + ch * 16;
-}
-__device__ __forceinline__ int xs_dma_bit(int m) { return (m ^ (m >> 1)) & 1; }
-
 template <int Q, int N>
 __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ x, const bf16* __restrict__ Cm,
                                                     const bf16* __restrict__ cb, const bf16* __restrict__ Bt,
@@ -282,45 +264,9 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             for (int u = 0; u < GW; ++u) gf[u] = fr.gf[u];
             __builtin_amdgcn_sched_barrier(0);
 
-            // y leaves in whole 128-byte rows.  The accumulators hold y^T: lane (i, q) has
-            // p = 16 pt + 4 q + r of row i.  v_permlane16_swap trades p-tiles between lanes
-            // q and q ^ 1, so every lane holds two 16-byte runs of consecutive p (its row's
-            // bytes [0, 64) and [64, 128) between the 4 lanes of the row).  A lane ^ 8
-            // swizzle then hands the second run to the lane of row i ^ 8, and each 16-byte
-            // store writes 8 complete rows: whole lines, sent non-temporal.  (Four 32-byte
-            // pieces per row, even merged in L2, made every write a partial-line miss.)
+            // y leaves in whole 128-byte rows (store_tile16)
             auto store_y = [&](const f32x4* a, int tile) {
-                const int sy = __builtin_amdgcn_readfirstlane((int)((t0 + tile * 16) * XS));
-                u32x2 yv[4];
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-                    yv[pt] = __builtin_bit_cast(u32x2, bf16x4{(bf16)a[pt][0], (bf16)a[pt][1], (bf16)a[pt][2], (bf16)a[pt][3]});
-                u32x4v lo, hi;  // 16-byte runs from p-tiles 0, 1 (row bytes 0..63) and 2, 3 (64..127)
-#pragma unroll
-                for (int d = 0; d < 2; ++d) {
-                    const auto r01 = __builtin_amdgcn_permlane16_swap(yv[0][d], yv[1][d], false, false);
-                    const auto r23 = __builtin_amdgcn_permlane16_swap(yv[2][d], yv[3][d], false, false);
-                    lo[d] = r01[0]; lo[2 + d] = r01[1];
-                    hi[d] = r23[0]; hi[2 + d] = r23[1];
-                }
-                u32x4v hx;  // the other half-row of this lane's partner i ^ 8
-#pragma unroll
-                for (int d = 0; d < 4; ++d) hx[d] = (unsigned)__builtin_amdgcn_ds_swizzle((int)hi[d], 0x201F);
-                const int ln = lane_now(), qq = ln >> 4, ii = ln & 15;
-                const bool up = ii >= 8;
-                // byte of the lane's run in its row: q = 0, 2 hold p 0..7, 8..15; q = 1, 3 hold 16..23, 24..31
-                const int vrow = (ii & 7) * XS + h * P * 2 + (qq & 1) * 32 + (qq & 2) * 8;
-                // The data registers of a 16-byte buffer store must not be rewritten by the next
-                // instructions: the store then sends the new values (seen on gfx950 with an SGPR
-                // offset, where no wait is inserted).  Each store is fenced off with s_nop.
-                __builtin_amdgcn_raw_buffer_store_b128(up ? hx : lo, ry, vrow + (up ? 64 : 0), sy, 2);
-                __builtin_amdgcn_sched_barrier(0);
-                asm volatile("s_nop 4");
-                __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_raw_buffer_store_b128(up ? lo : hx, ry, vrow + (up ? 0 : 64), sy + 8 * XS, 2);
-                __builtin_amdgcn_sched_barrier(0);
-                asm volatile("s_nop 4");
-                __builtin_amdgcn_sched_barrier(0);
+                store_tile16(a, ry, __builtin_amdgcn_readfirstlane((int)((t0 + tile * 16) * XS)), XS, h * P * 2);
             };
 
             // C B^T fragments in order: tile A's k-steps, then tile B's.  The running tile's
