@@ -612,9 +612,6 @@ struct BxsCfg {
     static constexpr int P = 64;
     static constexpr int RPW = Q / 64;          // row tiles per wave
     static constexpr int KS = Q / 32;           // 32-token k-steps per chunk
-    static constexpr int XR = Q / 32;           // 1 KB transfers per wave of a Q x 64 row tile
-    static constexpr int HR = N / 32;           // 1 KB transfers per wave of the 64 x N state tile
-    static constexpr int SRW = 512 / N;         // state rows per 1 KB transfer
     static constexpr int NF = N / 32;           // 32-wide n-steps of the state term
 };
 
@@ -628,8 +625,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_xs(const bf16* __restrict__
                                                      float* __restrict__ ds, float* __restrict__ dDp, int64_t Tn,
                                                      int H, int G, int nc) {
     typedef BxsCfg<Q, N> CF;
-    constexpr int P = 64, RPW = CF::RPW, KS = CF::KS, XR = CF::XR, HR = CF::HR, SRW = CF::SRW, NF = CF::NF;
-    constexpr int PN = P * N, HSW = (N / 8) < 16 ? (N / 8) : 16;
+    constexpr int P = 64, RPW = CF::RPW, KS = CF::KS, NF = CF::NF;
+    constexpr int PN = P * N;
     constexpr float LOG2E = 1.4426950408889634f;
     __shared__ __attribute__((aligned(16))) bf16 Ts[Q * P];   // x rows, then dy rows (swizzled)
     __shared__ __attribute__((aligned(16))) bf16 Hs[P * N];   // H_c, then R_c (chunks swizzled by row)
@@ -667,27 +664,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_xs(const bf16* __restrict__
 
     // the chunk's rows (x or dy) and a state tile (H_c or R_c) into LDS, this wave's share
     auto stage = [&](brsrc rrows, brsrc rstate) {
-        int ln = lane;  // opaque: the lane offsets are rebuilt per call, not kept live
-        asm volatile("" : "+v"(ln));
-        const int vd0 = xs_dma_lane(ln, 0, XS, hcol), vd1 = xs_dma_lane(ln, 1, XS, hcol);
-#pragma unroll
-        for (int r = 0; r < XR; ++r) {
-            const int m = w * XR + r;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rrows, (__attribute__((address_space(3))) void*)(Ts + m * 512), 16,
-                                                     xs_dma_bit(m) ? vd1 : vd0,
-                                                     __builtin_amdgcn_readfirstlane((c * Q + 8 * m) * XS), 0, 0);
-        }
-        // state transfer m: rows p = m SRW + l / (N / 8), LDS slot l % (N / 8) holding n-chunk
-        // slot ^ (p % HSW)
-#pragma unroll
-        for (int r = 0; r < HR; ++r) {
-            const int m = w * HR + r;
-            const int pr = ln / (N / 8), slot = ln % (N / 8), p = m * SRW + pr;
-            const int ch = slot ^ (p % HSW);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rstate, (__attribute__((address_space(3))) void*)(Hs + m * 512), 16,
-                                                     (pr * N + ch * 8) * 2,
-                                                     __builtin_amdgcn_readfirstlane((c * PN + m * SRW * N) * 2), 0, 0);
-        }
+        dma_rows_state<Q, N>(Ts, Hs, rrows, c * Q * XS, XS, hcol, rstate, c * PN * 2, w);
     };
     auto row_tile = [&](int k) { return (RPW == 1) ? w : ((k & 1) ? 8 * (k >> 1) + 7 - w : 8 * (k >> 1) + w); };
     // state term of one row tile: acc^T[p][t] = sum_n S[p][n] V_t[n] (S in Hs, V = C or B rows)

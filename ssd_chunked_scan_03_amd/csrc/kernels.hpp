@@ -609,6 +609,36 @@ __device__ __forceinline__ int hs_off(int p, int n) {
     return p * N + ((((n >> 3) ^ (p % HSW))) << 3) + (n & 7);
 }
 
+// A chunk's Q rows of a headdim-64 bfloat16 tensor (x, dy) and a [64][N] bfloat16 state tile
+// (H_c, R_c) straight into LDS by direct transfers, wave w taking its quarter of each: the
+// rows into Ts in xs_off's layout, the state into Hs in hs_off's.  srow0: byte offset of
+// the chunk's first row in rrows (row stride XS, the head at byte hcol); sstate0: byte
+// offset of the state tile in rstate.  The caller waits (vmcnt) and synchronises.
+template <int Q, int N>
+__device__ __forceinline__ void dma_rows_state(bf16* Ts, bf16* Hs, brsrc rrows, int srow0, int XS, int hcol,
+                                               brsrc rstate, int sstate0, int w) {
+    constexpr int XR = Q / 32, HR = N / 32, SRW = 512 / N, HSW = (N / 8) < 16 ? (N / 8) : 16;
+    int ln = lane_now();  // rebuilt per call, not kept live
+    const int vd0 = xs_dma_lane(ln, 0, XS, hcol), vd1 = xs_dma_lane(ln, 1, XS, hcol);
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+        const int m = w * XR + r;  // 1 KB transfer m: rows 8 m .. 8 m + 7
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rrows, (__attribute__((address_space(3))) void*)(Ts + m * 512), 16,
+                                                 xs_dma_bit(m) ? vd1 : vd0,
+                                                 __builtin_amdgcn_readfirstlane(srow0 + 8 * m * XS), 0, 0);
+    }
+    // state transfer m: rows p = m SRW + l / (N / 8); LDS slot l % (N / 8) holds n-chunk slot ^ (p % HSW)
+#pragma unroll
+    for (int r = 0; r < HR; ++r) {
+        const int m = w * HR + r;
+        const int pr = ln / (N / 8), slot = ln % (N / 8), p = m * SRW + pr;
+        const int ch = slot ^ (p % HSW);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rstate, (__attribute__((address_space(3))) void*)(Hs + m * 512), 16,
+                                                 (pr * N + ch * 8) * 2,
+                                                 __builtin_amdgcn_readfirstlane(sstate0 + m * SRW * N * 2), 0, 0);
+    }
+}
+
 // Element offsets of a chunk's x rows in LDS: the swizzled 64-element rows for bfloat16
 // at headdim 64 (no bank conflicts in the transpose reads), else rows padded by 8.
 // (The diagonal-decay output kernel keeps the padded rows: its split-row fragments would
@@ -1246,6 +1276,118 @@ __global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(cons
     for (int v = tid; v < len * (P / 8); v += kThreads) {
         const int ii = v / (P / 8), p0 = (v - ii * (P / 8)) * 8;
         st8(y + ((bi * Tn + tok0 + ii) * H + h) * P + p0, ld8(Ys + XL::off(ii, p0)));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_outs: k_out for the scalar decay at bfloat16 and headdim 64 (dstate 64, 128 or 256),
+// laid out like the fused kernel's output passes: the chunk's x rows and its entering state
+// H_c go straight into swizzled LDS tiles by direct transfers (no register holds them in
+// flight), each wave takes its row tiles one at a time -- state term from the LDS state
+// tile and the tile's C rows, decay-masked C B^T fragments from the group's table times x
+// fragments, D x_i riding in the diagonal k-step -- and y leaves in whole rows.  Three
+// work-groups per CU up to dstate 128 (two at 256, whose state tile is 32 KB).
+// ---------------------------------------------------------------------------
+template <int Q, int N>
+__global__ __launch_bounds__(kThreads, N <= 128 ? 3 : 2) void k_outs(const bf16* __restrict__ x,
+                                                                 const bf16* __restrict__ Cm,
+                                                                 const bf16* __restrict__ cb,
+                                                                 const bf16* __restrict__ hin,
+                                                                 const float* __restrict__ A,
+                                                                 const float* __restrict__ D,
+                                                                 const float* __restrict__ cdt,
+                                                                 bf16* __restrict__ y, int64_t Tn, int H, int G,
+                                                                 int nc) {
+    constexpr int P = 64, RPW = Q / 64, KS = Q / 32, NF = N / 32, PN = P * N;
+    constexpr float LOG2E = 1.4426950408889634f;
+    __shared__ __attribute__((aligned(16))) bf16 Ts[Q * P];  // x rows (swizzled)
+    __shared__ __attribute__((aligned(16))) bf16 Hs[P * N];  // H_c (chunks swizzled by row)
+    __shared__ float cds[Q], u2[Q];
+
+    const int64_t blk = blockIdx.x;
+    const int c = (int)(blk % nc);
+    const int64_t bh = blk / nc;
+    const int h = (int)(bh % H);
+    const int64_t bi = bh / H;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), l16 = lane & 15, q = lane >> 4;
+    const float ah2 = A[h] * LOG2E;
+    const float Dh = D ? D[h] : 0.f;
+
+    // buffer resources based at this batch row (rows past T read as zero, stores dropped),
+    // the group's table and this chain's entering states
+    const int XS = H * P * 2, CS = G * N * 2;
+    const uint32_t xbytes = (uint32_t)(Tn * H * P * 2);
+    const brsrc rx = make_rsrc(x + bi * Tn * H * P, xbytes);
+    const brsrc ry = make_rsrc(y + bi * Tn * H * P, xbytes);
+    const brsrc rc = make_rsrc(Cm + bi * Tn * G * N, (uint32_t)(Tn * G * N * 2));
+    const brsrc rcb = make_rsrc(cb + bi * nc * G * Q * Q, (uint32_t)((int64_t)nc * G * Q * Q * 2));
+    const brsrc rh = make_rsrc(hin + bh * nc * PN, (uint32_t)((int64_t)nc * PN * 2));
+    const int hcol = h * P * 2;
+    const int tab0 = (c * G + g) * Q * Q * 2;
+    const int vq = (l16 * Q + 8 * q) * 2, vc = l16 * CS + 8 * q * 2;
+
+    dma_rows_state<Q, N>(Ts, Hs, rx, c * Q * XS, XS, hcol, rh, c * PN * 2, w);
+    if (tid < Q) {
+        const float* cd = cdt + (bh * nc + c) * (int64_t)Q;
+        const float cv = cd[tid], cr = cd[tid | 31];
+        cds[tid] = cv;
+        u2[tid] = exp2f_fast(ah2 * (cr - cv));  // exp(A (cdt_{j|31} - cdt_j))
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's transfers have landed
+    __syncthreads();                    // ... every wave's, and the tables are in place
+
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        const int rt = (RPW == 1) ? w : ((k & 1) ? 8 * (k >> 1) + 7 - w : 8 * (k >> 1) + w);
+        const int i = rt * 16 + l16, nks = rt / 2 + 1;
+        bf16x8 gf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            if (ks < nks) gf[ks] = bload8(rcb, vq, __builtin_amdgcn_readfirstlane(tab0 + rt * 16 * Q * 2 + ks * 64));
+        // state term y^T[p][i] = exp(A cdt_i) sum_n H_c[p][n] C_i[n]
+        bf16x8 cf[NF];
+        const int sc0 = __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * CS + g * N * 2);
+#pragma unroll
+        for (int n = 0; n < NF; ++n) cf[n] = bload8(rc, vc, sc0 + n * 64);
+        f32x4 acc[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n = 0; n < NF; ++n)
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+                acc[pt] = mma(acc[pt], ld8(Hs + hs_off<N>(pt * 16 + l16, n * 32 + 8 * q)), cf[n]);
+        const float ci = cds[i];
+        const float sc = exp2f_fast(ah2 * ci);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] *= sc;
+        // diagonal block: below the row tile's k-step the decay factors as u2_j v_i (both
+        // <= 1); on it, direct exps with D on the diagonal (the table is zero above it)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks < nks) {
+                const int j0 = ks * 32 + 8 * q;
+                bf16x8 mf;
+                if (ks < nks - 1) {
+                    const float vi = exp2f_fast(ah2 * (ci - cds[ks * 32 + 31]));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) mf[e] = (bf16)((float)gf[ks][e] * (u2[j0 + e] * vi));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = j0 + e;
+                        const float m = (float)gf[ks][e] * exp2f_fast(fminf(ah2 * (ci - cds[j]), 0.f));
+                        mf[e] = (bf16)(m + ((j == i) ? Dh : 0.f));
+                    }
+                }
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) acc[pt] = mma(acc[pt], frag_xs(Ts, ks * 32, pt * 16, lane), mf);
+                __builtin_amdgcn_sched_barrier(0);  // (hoisting every k-step's reads spills)
+            }
+        }
+        store_tile16(acc, ry, __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * XS), XS, hcol);
+        __builtin_amdgcn_sched_barrier(0);  // one row tile's operands in flight at a time
     }
 }
 

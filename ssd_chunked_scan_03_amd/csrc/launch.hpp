@@ -3,6 +3,8 @@
 
 #include "fused.hpp"
 
+#include <type_traits>
+
 namespace ssd {
 
 // Everything one launch sequence needs; validated by the C ABI beforehand.
@@ -66,6 +68,28 @@ inline bool fused_supported(const RunArgs& a, bool bf16_dtype) {
 }
 inline bool fused_applies(const RunArgs& a, bool bf16_dtype) {
     return fused_supported(a, bf16_dtype) && !a.force_split && (a.ts || a.force_fused || a.b * a.H >= 512);
+}
+
+// The split schedule's scalar-decay output kernel in the fused layout (k_outs): bfloat16,
+// headdim 64, dstate 64 to 256, dense rows, buffer offsets of a batch row within 32 bits.
+// Enqueues it and returns true where it applies; false leaves the output to k_out.
+template <typename T, int P, int N>
+bool launch_outs(const RunArgs& a, dim3 g3, hipStream_t s, const T* x, const T* Cm, const T* cb, const T* hin,
+                 T* y) {
+    if constexpr (std::is_same<T, bf16>::value && P == 64 && (N == 64 || N == 128 || N == 256)) {
+        const int64_t lim = (int64_t)1 << 31;
+        if (a.ts || !(a.T * a.H * a.P * 2 < lim && a.T * a.G * a.N * 2 < lim && a.nc * a.G * a.Q * a.Q * 2 < lim &&
+                      a.nc * a.P * a.N * 2 < lim))
+            return false;
+        const int H = (int)a.H, G = (int)a.G, nc = (int)a.nc;
+        switch (a.Q) {
+            case 64: k_outs<64, N><<<g3, kThreads, 0, s>>>(x, Cm, cb, hin, a.A, a.D, a.cdt, y, a.T, H, G, nc); return true;
+            case 128: k_outs<128, N><<<g3, kThreads, 0, s>>>(x, Cm, cb, hin, a.A, a.D, a.cdt, y, a.T, H, G, nc); return true;
+            case 256: k_outs<256, N><<<g3, kThreads, 0, s>>>(x, Cm, cb, hin, a.A, a.D, a.cdt, y, a.T, H, G, nc); return true;
+            default: return false;
+        }
+    }
+    return false;
 }
 
 inline Rows rows_of(const RunArgs& a) {
@@ -203,6 +227,7 @@ int run(const RunArgs& a) {
     } else if (a.diag) {
         hipFuncSetAttribute((const void*)k_out<T, P, N, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         k_out<T, P, N, true><<<g3, kThreads, smem, s>>>(x, Bm, Cm, nullptr, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);
+    } else if (launch_outs<T, P, N>(a, g3, s, x, Cm, cb, hin, y)) {
     } else {
         hipFuncSetAttribute((const void*)k_out<T, P, N, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         k_out<T, P, N, false><<<g3, kThreads, smem, s>>>(x, Bm, Cm, cb, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);
