@@ -134,8 +134,13 @@ size_t ssd_workspace_bytes(const ssd_problem* p, int diag);
  *        diagonal, zero above it
  *   states float32 [batch, nheads, nchunks, headdim, dstate]  chunk states S_c
  *   hin  dtype   [batch, nheads, nchunks, headdim, dstate]  state entering chunk c
- *   bt   dtype   [batch, nchunks, ngroups, dstate, chunk]  B of each chunk, tokens contiguous
+ *   bt   dtype   [batch, nchunks, ngroups, dstate, chunk]  B of each chunk by token
  *        (scalar decay)
+ * The per-chunk tables (cb and bt: a chunk's rows of `chunk` columns) are stored in
+ * matrix-core fragment order: entry (r, col) of a chunk's table sits at element
+ *   ((r / 16) * (chunk / 32) + col / 32) * 512 + ((col % 32) / 8) * 128 + (r % 16) * 8 + col % 8
+ * of that chunk's block, so that the 16 x 32 fragment a kernel loads is one contiguous
+ * run.
  *   carry float32 [nseg, batch, nheads, headdim, dstate] then [batch, nheads, nseg]: the
  *        state entering each segment of chunks and each segment's summed cdt totals,
  *        when the split schedule's state scan runs as a parallel scan over segments

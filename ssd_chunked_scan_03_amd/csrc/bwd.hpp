@@ -438,11 +438,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_x(const T* __restrict__ x, con
         if (k < rpw) {
             const int rt = row_tile(k);
             const int i = rt * 16 + l16;
-            const T* cbrow = cbb + (int64_t)i * Q;
             const int nks = rt / 2 + 1;  // k-steps of 32 tokens up to this row tile
             v8 gf[8];
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbrow + (ks < nks ? ks : nks - 1) * 32 + 8 * q);
+            for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbb + tfrag(i, (ks < nks ? ks : nks - 1) * 32 + 8 * q, Q));
             const float ci = cds[i];
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
@@ -517,11 +516,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_x(const T* __restrict__ x, con
         if (k < rpw) {
             const int rt = row_tile(k);
             const int j = rt * 16 + l16;
-            const T* trow = cbtb + (int64_t)j * Q;
             const int kd = rt / 2;  // the k-step holding row tile rt
             v8 gf[8];
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(trow + ((ks >= kd && ks < KS) ? ks : kd) * 32 + 8 * q);
+            for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbtb + tfrag(j, ((ks >= kd && ks < KS) ? ks : kd) * 32 + 8 * q, Q));
             const float cj = cds[j];
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
@@ -659,7 +657,6 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_xs(const bf16* __restrict__
     const brsrc rr = make_rsrc(rin + bh * nc * PN, sbytes);
     const int hcol = h * P * 2;
     const int tab0 = (c * G + g) * Q * Q * 2;                    // this chunk's table, bytes
-    const int vq = (l16 * Q + 8 * q) * 2;                        // table row l16 of a tile, k-group q
     const int vc = l16 * CS + 8 * q * 2;                         // C / B row l16 of a tile, n-group q
 
     // the chunk's rows (x or dy) and a state tile (H_c or R_c) into LDS, this wave's share
@@ -701,7 +698,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_xs(const bf16* __restrict__
         bf16x8 gf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            if (ks < nks) gf[ks] = bload8(rcb, vq, __builtin_amdgcn_readfirstlane(tab0 + rt * 16 * Q * 2 + ks * 64));
+            if (ks < nks) gf[ks] = bload8(rcb, lane * 16, __builtin_amdgcn_readfirstlane(tab0 + (rt * (Q / 32) + ks) * 1024));
         f32x4 acc[4];
         state_term(acc, rc, rt);
         const float ci = cds[i];
@@ -764,7 +761,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_bwd_xs(const bf16* __restrict__
         bf16x8 gf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            if (ks >= kd) gf[ks] = bload8(rcbt, vq, __builtin_amdgcn_readfirstlane(tab0 + rt * 16 * Q * 2 + ks * 64));
+            if (ks >= kd) gf[ks] = bload8(rcbt, lane * 16, __builtin_amdgcn_readfirstlane(tab0 + (rt * (Q / 32) + ks) * 1024));
         f32x4 acc[4];
         state_term(acc, rb, rt);
         const float cj = cds[j];
@@ -1107,20 +1104,20 @@ __global__ __launch_bounds__(kBcThreads) void k_bwd_bc(const T* __restrict__ x, 
         }
     }
     __syncthreads();
-    const T* btb = bt + ((bi * nc + c) * G + g) * (int64_t)N * Q + (int64_t)n0 * Q;  // [n][j]
-    const T* ctb = ct + ((bi * nc + c) * G + g) * (int64_t)N * Q + (int64_t)n0 * Q;
+    const T* btb = bt + ((bi * nc + c) * G + g) * (int64_t)N * Q;  // [n][j], fragment order
+    const T* ctb = ct + ((bi * nc + c) * G + g) * (int64_t)N * Q;
     if (!sact) return;
     for (int j0 = 0; j0 < s64 + 64; j0 += 32) {
         const v8 wf = ld8(&Wc[(iw - s64) * ldc + j0 + 8 * q]);
 #pragma unroll
         for (int nt = 0; nt < NBH; ++nt)
-            accC[nt] = mma(accC[nt], ld8(btb + (int64_t)((nb0 + nt) * 16 + l16) * Q + j0 + 8 * q), wf);
+            accC[nt] = mma(accC[nt], ld8(btb + tfrag(n0 + (nb0 + nt) * 16 + l16, j0 + 8 * q, Q)), wf);
     }
     for (int i0 = s64; i0 < Q; i0 += 32) {
         const v8 wf = frag_rows(Wb, LDW, i0 - s64, rt * 16, lane);
 #pragma unroll
         for (int nt = 0; nt < NBH; ++nt)
-            accB[nt] = mma(accB[nt], ld8(ctb + (int64_t)((nb0 + nt) * 16 + l16) * Q + i0 + 8 * q), wf);
+            accB[nt] = mma(accB[nt], ld8(ctb + tfrag(n0 + (nb0 + nt) * 16 + l16, i0 + 8 * q, Q)), wf);
     }
     if (iw < len) {
         T* dCr = dC + ((bi * Tn + tok0 + iw) * G + g) * N + n0;

@@ -93,6 +93,16 @@ __device__ __forceinline__ brsrc make_rsrc(const void* base, uint32_t bytes) {
     void* p = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
+// Element offset of entry (r, col) of a per-chunk table whose rows hold Q columns (C B^T
+// and its transpose, B^T and C^T per chunk), stored in matrix-core fragment order: the
+// 16-row x 32-column fragment (r / 16, col / 32) is 512 consecutive elements, in which lane
+// l = 16 ((col % 32) / 8) + r % 16 of a fragment load finds its 8 consecutive columns.  A
+// wave's fragment load is then one contiguous 1 KB run (bfloat16) rather than a piece of
+// each of 16 rows.
+__host__ __device__ __forceinline__ int64_t tfrag(int64_t r, int col, int Q) {
+    return ((r >> 4) * (Q >> 5) + (col >> 5)) * 512 + (((col & 31) >> 3) << 7) + ((r & 15) << 3) + (col & 7);
+}
+
 // Lane index recomputed from the execution mask (two VALU ops) instead of kept live:
 // values needed only at chunk boundaries are rebuilt there rather than spilled.
 __device__ __forceinline__ int lane_now() {

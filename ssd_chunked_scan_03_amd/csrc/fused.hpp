@@ -96,8 +96,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
     const int XS = H * P * 2, CS = G * N * 2;                     // row strides in bytes
     // per-lane byte offsets
     const int vc = l16 * CS + g * N * 2 + q * 16;                  // C row l16 of a row tile
-    const int vq = (l16 * Q + 8 * q) * 2;                          // C B^T / B^T row l16, k-group q
-    const int vq1 = vq + 16 * Q * 2;                               // B^T rows of the next n-tile
+    const int vf = lane * 16;                                      // a lane's 16 bytes of a table fragment
 
     // lane-constant LDS offsets: x fragments per p-tile, H rows per 32-wide n-step
     int xo[4], ho[NF];
@@ -134,7 +133,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
         const bool inA = TPP == 1 || u < KA;
         const int tile = inA ? tA : tB;
         const int ks = TPP == 1 ? min(u, KA - 1) : (inA ? u : u - KA);
-        return __builtin_amdgcn_readfirstlane(((c * G + g) * Q * Q + tile * 16 * Q + ks * 32) * 2);
+        return __builtin_amdgcn_readfirstlane(((c * G + g) * Q * Q + (tile * (Q / 32) + ks) * 512) * 2);
     };
     auto issue_front = [&](Front& f, int c, int pass) {
         int tA, tB;
@@ -143,7 +142,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
 #pragma unroll
         for (int n = 0; n < NF; ++n) f.cf[n] = bload8(rc, vc, sb + n * 64);
 #pragma unroll
-        for (int u = 0; u < GW; ++u) f.gf[u] = bload8(rcb, vq, gf_off(c, u, tA, tB));
+        for (int u = 0; u < GW; ++u) f.gf[u] = bload8(rcb, vf, gf_off(c, u, tA, tB));
     };
     // the chunk's cdt row straight into LDS (wave 0, one 16-byte slot per lane), so no
     // loaded value has to stay in registers across the chunk loop
@@ -219,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             for (int pt = 0; pt < 4; ++pt) acc_h[a][pt] *= dch;
 
         // B^T fragments of the state update (the first two are requested during the last pass)
-        const int sbt = __builtin_amdgcn_readfirstlane(((c * G + g) * N * Q + w * SN * 16 * Q) * 2);
+        const int sbt = __builtin_amdgcn_readfirstlane(((c * G + g) * N * Q + w * SN * (Q / 32) * 512) * 2);
         bf16x8 bt[3][SN];
 
         // ---- output passes ----
@@ -276,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             for (int u = 0; u < NU; ++u) {
                 // (no scheduling fences here or in the state update's k-step loop: letting
                 // the compiler interleave neighbouring k-steps measured 2% faster)
-                if (u + GW < NU) gf[u + GW] = bload8(rcb, vq, gf_off(c, u + GW, tA, tB));
+                if (u + GW < NU) gf[u + GW] = bload8(rcb, vf, gf_off(c, u + GW, tA, tB));
                 const bool inA = TPP == 1 || u < KA;
                 if (TPP == 1 && u >= KA) break;
                 if (TPP == 2 && u == KA) {
@@ -327,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
 #pragma unroll
                 for (int ks = 0; ks < 2 && ks < KS; ++ks)
 #pragma unroll
-                    for (int a = 0; a < SN; ++a) bt[ks][a] = bload8(rbt, a == 0 ? vq : vq1, sbt + ks * 64);
+                    for (int a = 0; a < SN; ++a) bt[ks][a] = bload8(rbt, vf, sbt + (a * (Q / 32) + ks) * 1024);
                 // the next chunk's cdt row: every wave read this chunk's at the chunk top
                 if (c + 1 < nc) dma_cdt(c + 1);
             }
@@ -342,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 2 < KS) {
 #pragma unroll
-                for (int a = 0; a < SN; ++a) bt[(ks + 2) % 3][a] = bload8(rbt, a == 0 ? vq : vq1, sbt + (ks + 2) * 64);
+                for (int a = 0; a < SN; ++a) bt[(ks + 2) % 3][a] = bload8(rbt, vf, sbt + (a * (Q / 32) + ks + 2) * 1024);
             }
             const int j0 = ks * 32 + 8 * q;
             bf16x8 bw[SN];

@@ -296,8 +296,8 @@ __device__ __forceinline__ void cb_body(const T* __restrict__ Bm, const T* __res
             if (!TR && I == J)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v[r] = (j0 + r > i) ? (bf16)0.f : v[r];
-            if (TR) st4(out + (int64_t)(J * 64 + 16 * w + l16) * Q + I * 64 + 16 * ct + 4 * q, v);
-            else st4(out + (int64_t)i * Q + j0, v);
+            if (TR) st4(out + tfrag(J * 64 + 16 * w + l16, I * 64 + 16 * ct + 4 * q, Q), v);
+            else st4(out + tfrag(i, j0, Q), v);
         }
         return;
     }
@@ -326,8 +326,8 @@ __device__ __forceinline__ void cb_body(const T* __restrict__ Bm, const T* __res
         v4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = from_f<T>((!TR && I == J && j0 + r > i) ? 0.f : acc[ct][r]);
-        if (TR) st4(out + (int64_t)(J * 64 + 16 * w + l16) * Q + I * 64 + 16 * ct + 4 * q, v);
-        else st4(out + (int64_t)i * Q + j0, v);
+        if (TR) st4(out + tfrag(J * 64 + 16 * w + l16, I * 64 + 16 * ct + 4 * q, Q), v);
+        else st4(out + tfrag(i, j0, Q), v);
     }
 }
 
@@ -394,7 +394,7 @@ __device__ __forceinline__ void cb_row_body(const bf16* __restrict__ Bm, const b
             if (J == I)  // above the diagonal: exact zeros
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v[r] = (j0 + r > i) ? (bf16)0.f : v[r];
-            st4(out + (int64_t)i * Q + j0, v);
+            st4(out + tfrag(i, j0, Q), v);
         }
     }
 }
@@ -441,10 +441,10 @@ __device__ __forceinline__ void bt_body(const T* __restrict__ Bm, T* __restrict_
         for (int e = 0; e < 8; ++e) s[(n0 + e) * LD + jj] = val[e];
     }
     __syncthreads();
-    T* out = Bt + ((int64_t)kg * G + g) * (int64_t)N * Q + j0;
+    T* out = Bt + ((int64_t)kg * G + g) * (int64_t)N * Q;
     for (int v = threadIdx.x; v < N * JB / 8; v += kThreads) {
         const int n = v / (JB / 8), jv = (v - n * (JB / 8)) * 8;
-        st8(out + (int64_t)n * Q + jv, ld8(&s[n * LD + jv]));
+        st8(out + tfrag(n, j0 + jv, Q), ld8(&s[n * LD + jv]));
     }
 }
 
@@ -1038,9 +1038,8 @@ __global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(cons
     auto load_gf = [&](int k, v8* gf) {
         const int rt = row_tile(k);
         const int nks = rt / 2 + 1;
-        const T* cbrow = cbb_pf + (int64_t)(rt * 16 + l16) * Q;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbrow + (ks < nks ? ks : nks - 1) * 32 + 8 * q);
+        for (int ks = 0; ks < 8; ++ks) gf[ks] = ld8(cbb_pf + tfrag(rt * 16 + l16, (ks < nks ? ks : nks - 1) * 32 + 8 * q, Q));
     };
     v8 gfa[8];
 
@@ -1325,7 +1324,7 @@ __global__ __launch_bounds__(kThreads, N <= 128 ? 3 : 2) void k_outs(const bf16*
     const brsrc rh = make_rsrc(hin + bh * nc * PN, (uint32_t)((int64_t)nc * PN * 2));
     const int hcol = h * P * 2;
     const int tab0 = (c * G + g) * Q * Q * 2;
-    const int vq = (l16 * Q + 8 * q) * 2, vc = l16 * CS + 8 * q * 2;
+    const int vc = l16 * CS + 8 * q * 2;
 
     dma_rows_state<Q, N>(Ts, Hs, rx, c * Q * XS, XS, hcol, rh, c * PN * 2, w);
     if (tid < Q) {
@@ -1344,7 +1343,7 @@ __global__ __launch_bounds__(kThreads, N <= 128 ? 3 : 2) void k_outs(const bf16*
         bf16x8 gf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            if (ks < nks) gf[ks] = bload8(rcb, vq, __builtin_amdgcn_readfirstlane(tab0 + rt * 16 * Q * 2 + ks * 64));
+            if (ks < nks) gf[ks] = bload8(rcb, lane * 16, __builtin_amdgcn_readfirstlane(tab0 + (rt * (Q / 32) + ks) * 1024));
         // state term y^T[p][i] = exp(A cdt_i) sum_n H_c[p][n] C_i[n]
         bf16x8 cf[NF];
         const int sc0 = __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * CS + g * N * 2);
@@ -1474,7 +1473,7 @@ __global__ __launch_bounds__(kThreads) void k_gtab(const T* __restrict__ Bm, con
     for (int J16 = 0; J16 < 4; ++J16) {
         const bool on_diag = I == J && J16 == w;
         if (I == J && J16 > w) {  // above the diagonal: zeros (the output kernel reads them)
-            st4(out + (int64_t)i * Q + J * 64 + 16 * J16 + 4 * q, v4{});
+            st4(out + tfrag(i, J * 64 + 16 * J16 + 4 * q, Q), v4{});
             continue;
         }
         const int eJ = 16 * J16 + 15;
@@ -1517,7 +1516,7 @@ __global__ __launch_bounds__(kThreads) void k_gtab(const T* __restrict__ Bm, con
             if (on_diag) m = (j > i) ? 0.f : (j == i ? m + Dh : m);
             v[r] = from_f<T>(m);
         }
-        st4(out + (int64_t)i * Q + J * 64 + 16 * J16 + 4 * q, v);
+        st4(out + tfrag(i, J * 64 + 16 * J16 + 4 * q, Q), v);
     }
 }
 

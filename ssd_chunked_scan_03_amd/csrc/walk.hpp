@@ -74,7 +74,6 @@ __global__ __launch_bounds__(kThreads, 3) void k_walk(const bf16* __restrict__ x
     const brsrc rt = make_rsrc(tab + bi * nc * G * N * Q, (uint32_t)((int64_t)nc * G * N * Q * 2));
     const brsrc rcd = make_rsrc(cdt + bh * (int64_t)nc * Q, (uint32_t)((int64_t)nc * Q * 4));
     const brsrc rh = make_rsrc(ADJ ? hin + bh * (int64_t)nc * PN : hin, ADJ ? (uint32_t)((int64_t)nc * PN * 2) : 0u);
-    const int vq = (l16 * Q + 8 * q) * 2;  // table row l16 of an n-tile, k-group q
     // thread's row vectors: v = tid + 256 r -> row v / 8, columns 8 (v % 8) .. + 8
     const int vrow = tid >> 3, vcol = (tid & 7) * 8;
 
@@ -119,11 +118,11 @@ __global__ __launch_bounds__(kThreads, 3) void k_walk(const bf16* __restrict__ x
     // table fragments of half e of chunk c: k-steps [e KH, e KH + KH)
     bf16x8 bt[2][KH][SN];
     auto load_half = [&](int c, int e) {
-        const int sbt = __builtin_amdgcn_readfirstlane(((c * G + g) * N * Q + w * SN * 16 * Q) * 2);
+        const int sbt = __builtin_amdgcn_readfirstlane(((c * G + g) * N * Q + w * SN * (Q / 32) * 512) * 2);
 #pragma unroll
         for (int kk = 0; kk < KH; ++kk)
 #pragma unroll
-            for (int a = 0; a < SN; ++a) bt[e][kk][a] = bload8(rt, vq + a * 16 * Q * 2, sbt + (e * KH + kk) * 64);
+            for (int a = 0; a < SN; ++a) bt[e][kk][a] = bload8(rt, lane * 16, sbt + (a * (Q / 32) + e * KH + kk) * 1024);
     };
 
     // adjoint: the last chunk's boundary value <R_{nc-1}, H_nc> = <dhT, hT> (zero without dhT)

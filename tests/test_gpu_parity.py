@@ -55,6 +55,16 @@ def test_small_shapes_match_oracle(case):
     check(run_gpu(inp, dtype, Q, diag), oracle_ref(inp, diag), dtype, str(case))
 
 
+def frag_to_rows(t, R, Q):
+    """A workspace table stored in matrix-core fragment order (include/ssd.h: the 16-row x
+    32-column fragment (r / 16, col / 32) is 512 consecutive elements, lane 16 ((col % 32) / 8)
+    + r % 16 holding 8 consecutive columns) back to rows of Q columns: [..., R * Q] -> [..., R, Q]."""
+    r = np.arange(R)[:, None]
+    col = np.arange(Q)[None, :]
+    idx = ((r // 16) * (Q // 32) + col // 32) * 512 + ((col % 32) // 8) * 128 + (r % 16) * 8 + col % 8
+    return t[..., idx]
+
+
 @pytest.mark.parametrize("diag", [False, True])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_stage_outputs_match_oracle_dumps(dtype, diag):
@@ -79,7 +89,7 @@ def test_stage_outputs_match_oracle_dumps(dtype, diag):
     assert max_rel_err(S, st["S"], (0, 1, 2)) < tol
     assert max_rel_err(Hc, st["Hc"], (0, 1, 2)) < tol
     if not diag:
-        cb = view(lay["cb_off"], lay["cb_bytes"], td, (b, nc, G, Q, Q))
+        cb = frag_to_rows(view(lay["cb_off"], lay["cb_bytes"], td, (b, nc, G, Q * Q)), Q, Q)
         ref = st["G"]
         low = np.tril(np.ones((Q, Q), dtype=bool))
         for c in range(nc):
