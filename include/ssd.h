@@ -134,8 +134,8 @@ size_t ssd_workspace_bytes(const ssd_problem* p, int diag);
  *        diagonal, zero above it
  *   states float32 [batch, nheads, nchunks, headdim, dstate]  chunk states S_c
  *   hin  dtype   [batch, nheads, nchunks, headdim, dstate]  state entering chunk c
- *   bt   dtype   [batch, nchunks, ngroups, dstate, chunk]  B of each chunk by token
- *        (scalar decay)
+ *   bt   dtype   [batch, nchunks, ngroups, dstate, chunk]  B of each chunk by token, then
+ *        [batch, nchunks, ngroups, chunk, dstate] C of each chunk (fused schedule)
  * The per-chunk tables (cb and bt: a chunk's rows of `chunk` columns) are stored in
  * matrix-core fragment order: entry (r, col) of a chunk's table sits at element
  *   ((r / 16) * (chunk / 32) + col / 32) * 512 + ((col % 32) / 8) * 128 + (r % 16) * 8 + col % 8
@@ -177,7 +177,7 @@ int ssd_scan_fwd(const ssd_problem* p, const void* x, const float* dt, const flo
  * process ends.  The caller passes inputs and outputs only; arguments, schedule flags and
  * errors are as for ssd_scan_fwd, and a problem whose ssd_workspace_bytes(p, 0) exceeds
  * the scratch returns SSD_ERR_WORKSPACE before any HIP call (the 2.7B layer shape,
- * b8 T4096 H80 P64 N128 Q256 on the fused schedule, needs 35.7 MB).  The forward fully
+ * b8 T4096 H80 P64 N128 Q256 on the fused schedule, needs 44.0 MB).  The forward fully
  * writes every scratch region it reads, so no clearing is needed between calls.  Every
  * call on one GPU shares that GPU's array: calls that overlap in time on one GPU (on
  * different streams, or from threads without ordering) race on it and must be ordered

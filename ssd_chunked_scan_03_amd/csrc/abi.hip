@@ -106,7 +106,8 @@ ssd_workspace_layout layout_of(const ssd_problem* p, int diag) {
     L.hin_bytes = fused ? 0 : bhc * (size_t)(p->headdim * p->dstate) * es;
     off += align_up(L.hin_bytes);
     L.bt_off = off;
-    L.bt_bytes = (diag || !fused) ? 0 : (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->dstate * p->chunk) * es;
+    // B^T of every chunk, then C of every chunk (both in fragment order)
+    L.bt_bytes = (diag || !fused) ? 0 : 2 * (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->dstate * p->chunk) * es;
     off += align_up(L.bt_bytes);
     // the split schedule's state scan in segments (few state elements, many chunks)
     const int64_t sl = ssd::scan_segment_len(p->batch, p->nheads, p->headdim, p->dstate, nc);
@@ -241,7 +242,8 @@ int scan_noalloc(const ssd_problem* p, const void* x, const float* dt, const flo
 
 // ---- packed variable-length sequences (ssd_scan_fwd_varlen) ----
 // batch = number of sequences, seqlen = tokens of the packed axis.  Workspace: cdt
-// [H][kcap][Q] f32, C B^T [kcap][G][Q][Q] and B^T [kcap][G][N][Q] in the problem dtype,
+// [H][kcap][Q] f32, C B^T [kcap][G][Q][Q], B^T [kcap][G][N][Q] and C [kcap][G][Q][N] in the
+// problem dtype,
 // then the row maps ts and kb (batch + 1 int32 each).  kcap = ceil(T/Q) + batch bounds
 // the chunks of all sequences together (each adds at most one partial chunk).
 struct VarlenLayout {
@@ -261,7 +263,7 @@ VarlenLayout varlen_layout_of(const ssd_problem* p) {
     L.cb_off = off;
     off += align_up(kc * (size_t)p->ngroups * (size_t)(Q * Q) * es);
     L.bt_off = off;
-    off += align_up(kc * (size_t)p->ngroups * (size_t)(p->dstate * Q) * es);
+    off += align_up(2 * kc * (size_t)p->ngroups * (size_t)(p->dstate * Q) * es);  // B^T, then C
     L.ts_off = off;
     off += align_up((size_t)(nseq + 1) * 4);
     L.kb_off = off;

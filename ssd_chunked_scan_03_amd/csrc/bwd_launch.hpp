@@ -117,8 +117,8 @@ int run_bwd(const BwdArgs& a) {
     k_cb<T, N, false><<<g2, kThreads, 0, s>>>(Bm, Cm, cb, rows, G, Q);
     k_cb<T, N, true><<<g2, kThreads, 0, s>>>(Bm, Cm, cbt, rows, G, Q);
     const dim3 g6(kc * (unsigned)(Q / 64), (unsigned)G);
-    k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, bt, rows, G, Q);
-    k_bt<T, N><<<g6, kThreads, 0, s>>>(Cm, ct, rows, G, Q);
+    k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, bt, nullptr, nullptr, rows, G, Q);
+    k_bt<T, N><<<g6, kThreads, 0, s>>>(Cm, ct, nullptr, nullptr, rows, G, Q);
     const dim3 g3((unsigned)(a.b * H * nc));
     const int per_head = (int)((a.P * a.N / 4 + kThreads - 1) / kThreads);
     int nvalid = (int)(a.P * a.N / 4 / 64);  // partials of <R_c, H_{c+1}> per chunk

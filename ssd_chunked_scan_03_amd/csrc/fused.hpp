@@ -55,7 +55,7 @@ __device__ __forceinline__ int fused_tile(int pass, int t, int w) {
 }
 
 template <int Q, int N>
-__global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ x, const bf16* __restrict__ Cm,
+__global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ x, const bf16* __restrict__ Cf,
                                                     const bf16* __restrict__ cb, const bf16* __restrict__ Bt,
                                                     const float* __restrict__ A, const float* __restrict__ D,
                                                     const float* __restrict__ cdt, const float* __restrict__ h0,
@@ -90,12 +90,11 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
     const uint32_t xbytes = (uint32_t)(Tn * H * P * 2);
     const brsrc rx = make_rsrc(x + rt0 * H * P, xbytes);
     const brsrc ry = make_rsrc(y + rt0 * H * P, xbytes);
-    const brsrc rc = make_rsrc(Cm + rt0 * G * N, (uint32_t)(Tn * G * N * 2));
+    const brsrc rc = make_rsrc(Cf + kb0 * G * Q * N, (uint32_t)((int64_t)nc * G * Q * N * 2));
     const brsrc rcb = make_rsrc(cb + kb0 * G * Q * Q, (uint32_t)((int64_t)nc * G * Q * Q * 2));
     const brsrc rbt = make_rsrc(Bt + kb0 * G * N * Q, (uint32_t)((int64_t)nc * G * N * Q * 2));
-    const int XS = H * P * 2, CS = G * N * 2;                     // row strides in bytes
+    const int XS = H * P * 2;                                      // x / y row stride in bytes
     // per-lane byte offsets
-    const int vc = l16 * CS + g * N * 2 + q * 16;                  // C row l16 of a row tile
     const int vf = lane * 16;                                      // a lane's 16 bytes of a table fragment
 
     // lane-constant LDS offsets: x fragments per p-tile, H rows per 32-wide n-step
@@ -138,9 +137,9 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
     auto issue_front = [&](Front& f, int c, int pass) {
         int tA, tB;
         pass_tiles(pass, tA, tB);
-        const int sb = __builtin_amdgcn_readfirstlane((c * Q + tA * 16) * CS);
+        const int sb = __builtin_amdgcn_readfirstlane(((c * G + g) * Q * N + tA * (N / 32) * 512) * 2);
 #pragma unroll
-        for (int n = 0; n < NF; ++n) f.cf[n] = bload8(rc, vc, sb + n * 64);
+        for (int n = 0; n < NF; ++n) f.cf[n] = bload8(rc, vf, sb + n * 1024);
 #pragma unroll
         for (int u = 0; u < GW; ++u) f.gf[u] = bload8(rcb, vf, gf_off(c, u, tA, tB));
     };
@@ -232,9 +231,9 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
             // the second tile's C rows, requested now and consumed after the first tile's
             bf16x8 cfB[TPP == 2 ? NF : 1];
             if (TPP == 2) {
-                const int sb = __builtin_amdgcn_readfirstlane((c * Q + tB * 16) * CS);
+                const int sb = __builtin_amdgcn_readfirstlane(((c * G + g) * Q * N + tB * (N / 32) * 512) * 2);
 #pragma unroll
-                for (int n = 0; n < NF; ++n) cfB[n] = bload8(rc, vc, sb + n * 64);
+                for (int n = 0; n < NF; ++n) cfB[n] = bload8(rc, vf, sb + n * 1024);
             }
             __builtin_amdgcn_sched_barrier(0);
             // state term, one tile at a time: y^T[p][i] = exp(A cdt_i) sum_n H_c[p][n] C_i[n]

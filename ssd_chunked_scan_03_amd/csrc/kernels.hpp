@@ -414,17 +414,19 @@ __global__ __launch_bounds__(kThreads) void k_cb(const T* __restrict__ Bm, const
 }
 
 // ---------------------------------------------------------------------------
-// k_bt: Bt[b,c,g][n][j] = B[b, cQ+j, g, n] (0 past T): each chunk's B with tokens
-// contiguous, the layout the fused kernel reads its chunk-state A operand from.
-// Grid (chunks * Q/64, G) over the global chunk axis: one 64-token slab per
-// work-group, transposed through LDS.
+// k_bt: Bt[b,c,g][n][j] = B[b, cQ+j, g, n] (0 past T): each chunk's B by token, the
+// operand the fused kernel's state update (and the backward's walks) read; with Cf, also
+// Cf[b,c,g][i][n] = C[b, cQ+i, g, n] (0 past T), the operand of the fused kernel's state
+// term.  Both in fragment order (tfrag).  Grid (chunks * Q/64, G) over the global chunk
+// axis: one 64-token slab per work-group, B transposed through LDS.
 // ---------------------------------------------------------------------------
 template <typename T, int N>
 constexpr size_t bt_smem() { return (size_t)N * (64 + 8) * sizeof(T); }
 
 template <typename T, int N>
-__device__ __forceinline__ void bt_body(const T* __restrict__ Bm, T* __restrict__ Bt, Rows rows, int G, int Q,
-                                        int kg, int j0, int g, T* __restrict__ s) {
+__device__ __forceinline__ void bt_body(const T* __restrict__ Bm, T* __restrict__ Bt, const T* __restrict__ Cm,
+                                        T* __restrict__ Cf, Rows rows, int G, int Q, int kg, int j0, int g,
+                                        T* __restrict__ s) {
     typedef typename V8<T>::type v8;
     constexpr int JB = 64, LD = JB + 8;
     if (kg >= rows.total_chunks()) return;
@@ -434,6 +436,17 @@ __device__ __forceinline__ void bt_body(const T* __restrict__ Bm, T* __restrict_
     Bm += rows.tok0(rr) * G * N;
     const int64_t bi = 0;
     const int64_t tok0 = (int64_t)c * Q + j0;
+    if constexpr (N % 32 == 0) {
+        if (Cf) {
+            Cm += rows.tok0(rr) * G * N;
+            T* cout = Cf + ((int64_t)kg * G + g) * (int64_t)Q * N;
+            for (int v = threadIdx.x; v < JB * N / 8; v += kThreads) {
+                const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
+                const v8 val = (tok0 + jj < Tn) ? ld8(Cm + ((bi * Tn + tok0 + jj) * G + g) * N + n0) : zero8<T>();
+                st8(cout + tfrag(j0 + jj, n0, N), val);
+            }
+        }
+    }
     for (int v = threadIdx.x; v < JB * N / 8; v += kThreads) {
         const int jj = v / (N / 8), n0 = (v - jj * (N / 8)) * 8;
         const v8 val = (tok0 + jj < Tn) ? ld8(Bm + ((bi * Tn + tok0 + jj) * G + g) * N + n0) : zero8<T>();
@@ -449,12 +462,13 @@ __device__ __forceinline__ void bt_body(const T* __restrict__ Bm, T* __restrict_
 }
 
 template <typename T, int N>
-__global__ __launch_bounds__(kThreads) void k_bt(const T* __restrict__ Bm, T* __restrict__ Bt, Rows rows,
-                                                 int G, int Q) {
+__global__ __launch_bounds__(kThreads) void k_bt(const T* __restrict__ Bm, T* __restrict__ Bt,
+                                                 const T* __restrict__ Cm, T* __restrict__ Cf, Rows rows, int G,
+                                                 int Q) {
     __shared__ __attribute__((aligned(16))) T s[N * (64 + 8)];
     const int slabs = Q / 64;
     const int kg = blockIdx.x / slabs;
-    bt_body<T, N>(Bm, Bt, rows, G, Q, kg, (blockIdx.x - kg * slabs) * 64, blockIdx.y, s);
+    bt_body<T, N>(Bm, Bt, Cm, Cf, rows, G, Q, kg, (blockIdx.x - kg * slabs) * 64, blockIdx.y, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -503,7 +517,9 @@ __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ dt,
         return;
     }
     y -= ncb * G;
-    if (BT) bt_body<T, N>(Bm, Bt, rows, G, Q, k, (y % nslab) * 64, y / nslab, reinterpret_cast<T*>(smem));
+    // (the C copy follows the B^T tables of every chunk in the same region)
+    if (BT) bt_body<T, N>(Bm, Bt, Cm, Bt + (int64_t)rows.kcap * G * N * Q, rows, G, Q, k, (y % nslab) * 64,
+                          y / nslab, reinterpret_cast<T*>(smem));
 }
 
 // ---------------------------------------------------------------------------

@@ -116,9 +116,11 @@ inline bool diag_uses_table(int64_t Q, int64_t P, int64_t N, size_t es) {
 template <int Q, int N>
 void launch_fused(const RunArgs& a) {
     const int BH = (int)(a.b * a.H);
+    const Rows rows = rows_of(a);
+    const bf16* bt = static_cast<const bf16*>(a.bt);  // B^T per chunk, then C per chunk
     k_fused<Q, N><<<BH, kThreads, 0, a.stream>>>(
-        static_cast<const bf16*>(a.x), static_cast<const bf16*>(a.C), static_cast<const bf16*>(a.cb),
-        static_cast<const bf16*>(a.bt), a.A, a.D, a.cdt, a.h0, static_cast<bf16*>(a.y), a.hT, rows_of(a), (int)a.G);
+        static_cast<const bf16*>(a.x), bt + (int64_t)rows.kcap * a.G * N * Q, static_cast<const bf16*>(a.cb), bt,
+        a.A, a.D, a.cdt, a.h0, static_cast<bf16*>(a.y), a.hT, rows, (int)a.G);
 }
 
 template <typename T, int P, int N>
@@ -234,7 +236,8 @@ int run(const RunArgs& a) {
     }
     if (!a.diag && (st & 32)) {
         const dim3 g6(kc * (unsigned)(Q / 64), (unsigned)G);
-        k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, static_cast<T*>(a.bt), rows, G, Q);
+        T* btp = static_cast<T*>(a.bt);
+        k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, btp, Cm, btp + (int64_t)rows.kcap * G * N * Q, rows, G, Q);
     }
     if (st & 64) {
         if constexpr (kBF16 && P == 64 && (N == 64 || N == 128)) {

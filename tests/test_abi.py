@@ -41,8 +41,8 @@ def prob(b=2, T=300, H=4, P=64, N=128, G=2, Q=128, dtype=ssd.SSD_BF16):
 
 def test_workspace_layout_arithmetic():
     """The workspace holds the regions of the schedule that runs: cdt and C B^T always
-    (C B^T for the scalar decay only), B^T for the fused schedule, chunk states and
-    entering states for the split one."""
+    (C B^T for the scalar decay only), B^T and C per chunk for the fused schedule, chunk
+    states and entering states for the split one."""
     nc = 3
     for flags in (0, ssd.SCHEDULE_SPLIT, ssd.SCHEDULE_FUSED):
         p = ssd.make_problem(2, 300, 4, 64, 128, 2, 128, ssd.SSD_BF16, flags)
@@ -55,7 +55,7 @@ def test_workspace_layout_arithmetic():
             assert lay["cb_bytes"] == (0 if diag else 2 * nc * 2 * 128 * 128 * 2)
             assert lay["states_bytes"] == (0 if fused else 2 * 4 * nc * 64 * 128 * 4)
             assert lay["hin_bytes"] == (0 if fused else 2 * 4 * nc * 64 * 128 * 2)
-            assert lay["bt_bytes"] == (2 * nc * 2 * 128 * 128 * 2 if fused else 0)
+            assert lay["bt_bytes"] == (2 * (2 * nc * 2 * 128 * 128 * 2) if fused else 0)  # B^T, then C
             assert lay["carry_bytes"] == 0  # 2 x 4 x 64 x 128 / 4 threads is not "few", and nc < 8
             offs = [lay[k] for k in ("cdt_off", "cb_off", "states_off", "hin_off", "bt_off", "carry_off")]
             assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
@@ -67,15 +67,15 @@ def test_workspace_layout_arithmetic():
 
 def test_workspace_follows_the_schedule_at_the_layer_shape():
     """The 2.7B layer shape (b8 T4096 H80 P64 N128 G1 Q256, bf16) runs the fused schedule
-    by default: its workspace is cdt + C B^T + B^T (about 36 MB), none of the split
-    schedule's 503 MB of chunk states and entering states."""
+    by default: its workspace is cdt + C B^T + B^T and C per chunk (about 44 MB), none of
+    the split schedule's 503 MB of chunk states and entering states."""
     b, T, H, P, N, G, Q = 8, 4096, 80, 64, 128, 1, 256
     nc = T // Q
-    cdt, cb, bt = b * H * nc * Q * 4, b * nc * G * Q * Q * 2, b * nc * G * N * Q * 2
+    cdt, cb, bt = b * H * nc * Q * 4, b * nc * G * Q * Q * 2, 2 * b * nc * G * N * Q * 2
     fused = ssd.workspace_layout(ssd.make_problem(b, T, H, P, N, G, Q, ssd.SSD_BF16))
     assert (fused["cdt_bytes"], fused["cb_bytes"], fused["bt_bytes"]) == (cdt, cb, bt)
     assert fused["states_bytes"] == fused["hin_bytes"] == fused["carry_bytes"] == 0
-    assert fused["total_bytes"] == cdt + cb + bt == 35_651_584
+    assert fused["total_bytes"] == cdt + cb + bt == 44_040_192
     split = ssd.workspace_layout(ssd.make_problem(b, T, H, P, N, G, Q, ssd.SSD_BF16, ssd.SCHEDULE_SPLIT))
     assert split["bt_bytes"] == 0
     assert split["states_bytes"] == b * H * nc * P * N * 4 and split["hin_bytes"] == b * H * nc * P * N * 2
@@ -272,12 +272,12 @@ def _align(v, a=256):
 
 def test_varlen_workspace_bytes_and_support():
     """Packed sequences run on the fused schedule: bf16, headdim 64, dstate 64/128.
-    Workspace = cdt [H][kcap][Q] f32 + C B^T [kcap][G][Q][Q] + B^T [kcap][G][N][Q] (bf16)
-    + two int32 row maps of nseq + 1 entries, kcap = ceil(T/Q) + nseq."""
+    Workspace = cdt [H][kcap][Q] f32 + C B^T [kcap][G][Q][Q] + B^T [kcap][G][N][Q] and C
+    [kcap][G][Q][N] (bf16) + two int32 row maps of nseq + 1 entries, kcap = ceil(T/Q) + nseq."""
     for nseq, T, H, N, G, Q in [(3, 1000, 8, 128, 1, 256), (7, 33, 4, 64, 2, 64), (1, 4096, 80, 128, 1, 128)]:
         p = ssd.make_problem(nseq, T, H, 64, N, G, Q, ssd.SSD_BF16)
         kcap = -(-T // Q) + nseq
-        want = (_align(H * kcap * Q * 4) + _align(kcap * G * Q * Q * 2) + _align(kcap * G * N * Q * 2)
+        want = (_align(H * kcap * Q * 4) + _align(kcap * G * Q * Q * 2) + _align(2 * kcap * G * N * Q * 2)
                 + 2 * _align((nseq + 1) * 4))
         assert ssd.varlen_workspace_bytes(p) == want
     for kw in ({"dtype": ssd.SSD_F32}, {"P": 32}, {"N": 256}, {"N": 32}, {"Q": 32}):
