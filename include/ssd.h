@@ -26,9 +26,11 @@
  *     h0, hT [batch, nheads, headdim, dstate]        float32 (h0 NULL = 0; hT NULL = not written)
  * Head h reads B/C group floor(h * ngroups / nheads) (contiguous blocks of heads).
  *
- * Precision: decay sums, exponentials and states are float32; x, B, C (and the
- * masked scores and entering states fed to the matrix cores) are in the problem
- * dtype; accumulation is float32; y is rounded once to the problem dtype.
+ * Precision: decay sums, exponentials and the carried state are float32; x, B, C (and
+ * the masked scores and entering states fed to the matrix cores) are in the problem
+ * dtype, and so is each chunk's state S_c where the split schedule stores it (rounded
+ * once, then summed in float32); accumulation is float32; y is rounded once to the
+ * problem dtype.
  * Accuracy is stated for A <= 0 (decays in (0, 1]); NaN inputs propagate.
  *
  * Ownership and ordering: every pointer is a device pointer owned by the caller.
@@ -132,7 +134,7 @@ size_t ssd_workspace_bytes(const ssd_problem* p, int diag);
  *        not fit LDS (see ssd_diag_scan_fwd), [batch, nheads, nchunks, chunk, chunk] each
  *        head's decay-weighted block sum_n C_in B_jn exp(A_n (cdt_i - cdt_j)), D on the
  *        diagonal, zero above it
- *   states float32 [batch, nheads, nchunks, headdim, dstate]  chunk states S_c
+ *   states dtype [batch, nheads, nchunks, headdim, dstate]  chunk states S_c
  *   hin  dtype   [batch, nheads, nchunks, headdim, dstate]  state entering chunk c
  *   bt   dtype   [batch, nchunks, ngroups, dstate, chunk]  B of each chunk by token, then
  *        [batch, nchunks, ngroups, chunk, dstate] C of each chunk (fused schedule)

@@ -100,7 +100,7 @@ ssd_workspace_layout layout_of(const ssd_problem* p, int diag) {
                         : (size_t)(p->batch * nc * p->ngroups) * (size_t)(p->chunk * p->chunk) * es;
     off += align_up(L.cb_bytes);
     L.states_off = off;
-    L.states_bytes = fused ? 0 : bhc * (size_t)(p->headdim * p->dstate) * 4;
+    L.states_bytes = fused ? 0 : bhc * (size_t)(p->headdim * p->dstate) * es;
     off += align_up(L.states_bytes);
     L.hin_off = off;
     L.hin_bytes = fused ? 0 : bhc * (size_t)(p->headdim * p->dstate) * es;
@@ -192,7 +192,7 @@ int scan(const ssd_problem* p, int diag, const void* x, const float* dt, const f
     char* w = static_cast<char*>(ws);
     a.cdt = reinterpret_cast<float*>(w + L.cdt_off);
     a.cb = L.cb_bytes ? static_cast<void*>(w + L.cb_off) : nullptr;
-    a.states = L.states_bytes ? reinterpret_cast<float*>(w + L.states_off) : nullptr;
+    a.states = L.states_bytes ? static_cast<void*>(w + L.states_off) : nullptr;
     a.hin = L.hin_bytes ? static_cast<void*>(w + L.hin_off) : nullptr;
     a.bt = L.bt_bytes ? static_cast<void*>(w + L.bt_off) : nullptr;
     a.carry = L.carry_bytes ? reinterpret_cast<float*>(w + L.carry_off) : nullptr;

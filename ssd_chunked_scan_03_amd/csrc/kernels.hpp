@@ -708,12 +708,14 @@ struct StateTiling {
 // ADJ = true weights token j by its decay from the chunk start instead,
 // exp(A cdt_j): called with (dy, C) for (x, B) it gives the backward pass's adjoint
 // chunk input sum_{i in chunk} exp(A cdt_i) dy_i C_i^T.
+// ST is the type S_c is stored in: float32 for the backward; the forward stores it in the
+// input type (each S_c is rounded once, and the scan that sums them accumulates in float32).
 // ---------------------------------------------------------------------------
-template <typename T, int P, int N, bool DIAG, bool ADJ = false>
+template <typename T, int P, int N, bool DIAG, bool ADJ = false, typename ST = float>
 __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, const T* __restrict__ Bm,
                                                     const float* __restrict__ A,
                                                     const float* __restrict__ cdt,
-                                                    float* __restrict__ S, int64_t Tn, int H, int G,
+                                                    ST* __restrict__ S, int64_t Tn, int H, int G,
                                                     int Q, int nc) {
     typedef typename V8<T>::type v8;
     typedef StateTiling<P, N> TL;
@@ -820,12 +822,16 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
         __syncthreads();
     }
     if (wact) {
-        float* out = S + (bh * nc + c) * (int64_t)(P * N);
+        ST* out = S + (bh * nc + c) * (int64_t)(P * N);
 #pragma unroll
         for (int a = 0; a < TL::WN; ++a)
 #pragma unroll
-            for (int b = 0; b < TL::WP; ++b)
-                st4(out + ((wp0 + b) * 16 + l16) * N + (wn0 + a) * 16 + 4 * q, acc[a][b]);
+            for (int b = 0; b < TL::WP; ++b) {
+                typename V4<ST>::type o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = from_f<ST>(acc[a][b][r]);
+                st4(out + ((wp0 + b) * 16 + l16) * N + (wn0 + a) * 16 + 4 * q, o);
+            }
     }
 }
 
@@ -845,10 +851,11 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
 //           and the sum of its chunks' cdt totals                     (into `segsum`)
 //   k_scan_carry   in segment order: carry[s] <- H entering segment s
 //   MODE 2  each segment again from carry[s]: hin, and hT from the last segment
-// MODE 0 is the whole sequence in one segment (L = nc).
+// MODE 0 is the whole sequence in one segment (L = nc).  ST: the type the chunk states
+// are stored in (k_state's); the carried state is float32 throughout.
 // ---------------------------------------------------------------------------
-template <typename T, bool DIAG, int MODE>
-__global__ __launch_bounds__(kThreads) void k_scan(const float* __restrict__ S, T* __restrict__ hin,
+template <typename T, bool DIAG, int MODE, typename ST = float>
+__global__ __launch_bounds__(kThreads) void k_scan(const ST* __restrict__ S, T* __restrict__ hin,
                                                    float* __restrict__ hT, const float* __restrict__ h0,
                                                    const float* __restrict__ A,
                                                    const float* __restrict__ cdt, float* __restrict__ carry,
@@ -870,12 +877,12 @@ __global__ __launch_bounds__(kThreads) void k_scan(const float* __restrict__ S, 
     if (MODE == 2) st = ld4(carry + seg * BHPN + bh * PN + e0);
     else if (MODE == 0 && h0) st = ld4(h0 + bh * PN + e0);
     const float* cl = cdt + bh * (int64_t)nc * Q + (Q - 1);
-    const float* sp = S + bh * (int64_t)nc * PN + e0;
+    const ST* sp = S + bh * (int64_t)nc * PN + e0;
     T* hp = hin + bh * (int64_t)nc * PN + e0;
     constexpr int DEPTH = 8;
     float lsum = 0.f;  // the segment's log-decay per unit A (MODE 1)
     for (int c0 = cb; c0 < ce; c0 += DEPTH) {
-        f32x4 s[DEPTH];
+        typename V4<ST>::type s[DEPTH];
         float Lc[DEPTH];
 #pragma unroll
         for (int k = 0; k < DEPTH; ++k) {
@@ -894,7 +901,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(const float* __restrict__ S, 
                     st4(hp + (int64_t)(c0 + k) * PN, o);
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) st[r] = exp_f(a4[r] * Lc[k]) * st[r] + s[k][r];
+                for (int r = 0; r < 4; ++r) st[r] = exp_f(a4[r] * Lc[k]) * st[r] + to_f(s[k][r]);
                 if (MODE == 1) lsum += Lc[k];
             }
         }

@@ -22,7 +22,7 @@ struct RunArgs {
     float* hT;
     float* cdt;     // [b,H,nc,Q]
     void* cb;       // [b,nc,G,Q,Q] (scalar decay); [b,H,nc,Q,Q] (diagonal decay, table path)
-    float* states;  // [b,H,nc,P,N]
+    void* states;   // [b,H,nc,P,N] chunk states, in the input type
     void* hin;      // [b,H,nc,P,N]
     void* bt;       // [b,nc,G,N,Q]  (scalar decay only)
     // packed variable-length rows (nullptr: dense).  b rows share the token axis of T
@@ -187,11 +187,12 @@ int run(const RunArgs& a) {
             Bm, Cm, a.A, a.D, a.cdt, cb, a.T, H, G, Q, nc);
     }
     const dim3 g3((unsigned)(a.b * H * nc));
+    T* Sc = static_cast<T*>(a.states);
     if (!(st & 4)) {
     } else if (a.diag)
-        k_state<T, P, N, true><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
+        k_state<T, P, N, true, false, T><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, Sc, a.T, H, G, Q, nc);
     else
-        k_state<T, P, N, false><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, a.states, a.T, H, G, Q, nc);
+        k_state<T, P, N, false, false, T><<<g3, kThreads, 0, s>>>(x, Bm, a.A, a.cdt, Sc, a.T, H, G, Q, nc);
 
     const int per_head = (P * N / 4 + kThreads - 1) / kThreads;
     const int L = (int)scan_segment_len(a.b, H, P, N, nc);
@@ -202,22 +203,22 @@ int run(const RunArgs& a) {
     if (!(st & 8)) {
     } else if (nseg <= 1) {
         if (a.diag)
-            k_scan<T, true, 0><<<g4, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, nullptr, nullptr, H,
+            k_scan<T, true, 0, T><<<g4, kThreads, 0, s>>>(Sc, hin, a.hT, a.h0, a.A, a.cdt, nullptr, nullptr, H,
                                                       P * N, N, Q, nc, per_head, nc, BHPN);
         else
-            k_scan<T, false, 0><<<g4, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, nullptr, nullptr, H,
+            k_scan<T, false, 0, T><<<g4, kThreads, 0, s>>>(Sc, hin, a.hT, a.h0, a.A, a.cdt, nullptr, nullptr, H,
                                                        P * N, N, Q, nc, per_head, nc, BHPN);
     } else if (a.diag) {
-        k_scan<T, true, 1><<<g4s, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
+        k_scan<T, true, 1, T><<<g4s, kThreads, 0, s>>>(Sc, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
                                                     P * N, N, Q, nc, per_head, L, BHPN);
         k_scan_carry<true><<<g4, kThreads, 0, s>>>(a.h0, a.A, segsum, a.carry, H, P * N, N, per_head, nseg, BHPN);
-        k_scan<T, true, 2><<<g4s, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
+        k_scan<T, true, 2, T><<<g4s, kThreads, 0, s>>>(Sc, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
                                                     P * N, N, Q, nc, per_head, L, BHPN);
     } else {
-        k_scan<T, false, 1><<<g4s, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
+        k_scan<T, false, 1, T><<<g4s, kThreads, 0, s>>>(Sc, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
                                                      P * N, N, Q, nc, per_head, L, BHPN);
         k_scan_carry<false><<<g4, kThreads, 0, s>>>(a.h0, a.A, segsum, a.carry, H, P * N, N, per_head, nseg, BHPN);
-        k_scan<T, false, 2><<<g4s, kThreads, 0, s>>>(a.states, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
+        k_scan<T, false, 2, T><<<g4s, kThreads, 0, s>>>(Sc, hin, a.hT, a.h0, a.A, a.cdt, a.carry, segsum, H,
                                                      P * N, N, Q, nc, per_head, L, BHPN);
     }
 

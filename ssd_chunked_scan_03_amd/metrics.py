@@ -11,8 +11,8 @@ Bytes are per kernel of the split schedule, each operand that kernel must touch
 counted once (es = bytes of the x/B/C dtype):
   k_cumsum  dt read + cdt write
   k_cb      B + C read + C B^T blocks (64 x 64, on/below the diagonal) write
-  k_state   x + B + cdt read + fp32 chunk states write
-  k_scan    fp32 chunk states + chunk-end cdt + h0 read, entering states (es) + hT write
+  k_state   x + B + cdt read + chunk states (es) write
+  k_scan    chunk states (es) + chunk-end cdt + h0 read, entering states (es) + hT write
   k_out     x + C + cdt + C B^T blocks + entering states read, y write
   k_bt      B read + per-chunk transposed B write, C read + per-chunk C write (fused)
   k_fused   x + C + transposed B + cdt + C B^T blocks + h0 read, y + hT write
@@ -47,14 +47,13 @@ def kernel_bytes(b, T, H, P, N, G, Q, es, diag=False, h0=True) -> dict:
     dt = b * T * H * 4
     cdt = b * H * nc * Q * 4
     cbb = 0 if diag else b * nc * G * (nb * (nb + 1) // 2) * 64 * 64 * es
-    st32 = b * H * nc * P * N * 4
     stx = b * H * nc * P * N * es
     hstate = b * H * P * N * 4
     return {
         "k_cumsum": dt + cdt,
         "k_cb": 0 if diag else 2 * bc + cbb,
-        "k_state": x + bc + cdt + st32,
-        "k_scan": st32 + b * H * nc * 4 + (hstate if h0 else 0) + stx + hstate,
+        "k_state": x + bc + cdt + stx,
+        "k_scan": stx + b * H * nc * 4 + (hstate if h0 else 0) + stx + hstate,
         "k_out": x + bc * (2 if diag else 1) + cdt + cbb + stx + x,
         "k_bt": 0 if diag else 4 * bc,
         "k_fused": 2 * x + 2 * bc + cdt + cbb + (2 if h0 else 1) * hstate,

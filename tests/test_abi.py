@@ -53,7 +53,7 @@ def test_workspace_layout_arithmetic():
             lay = ssd.workspace_layout(p, diag)
             assert lay["cdt_bytes"] == 2 * 4 * nc * 128 * 4
             assert lay["cb_bytes"] == (0 if diag else 2 * nc * 2 * 128 * 128 * 2)
-            assert lay["states_bytes"] == (0 if fused else 2 * 4 * nc * 64 * 128 * 4)
+            assert lay["states_bytes"] == (0 if fused else 2 * 4 * nc * 64 * 128 * 2)  # in the input type
             assert lay["hin_bytes"] == (0 if fused else 2 * 4 * nc * 64 * 128 * 2)
             assert lay["bt_bytes"] == (2 * (2 * nc * 2 * 128 * 128 * 2) if fused else 0)  # B^T, then C
             assert lay["carry_bytes"] == 0  # 2 x 4 x 64 x 128 / 4 threads is not "few", and nc < 8
@@ -68,7 +68,7 @@ def test_workspace_layout_arithmetic():
 def test_workspace_follows_the_schedule_at_the_layer_shape():
     """The 2.7B layer shape (b8 T4096 H80 P64 N128 G1 Q256, bf16) runs the fused schedule
     by default: its workspace is cdt + C B^T + B^T and C per chunk (about 44 MB), none of
-    the split schedule's 503 MB of chunk states and entering states."""
+    the split schedule's 335 MB of chunk states and entering states."""
     b, T, H, P, N, G, Q = 8, 4096, 80, 64, 128, 1, 256
     nc = T // Q
     cdt, cb, bt = b * H * nc * Q * 4, b * nc * G * Q * Q * 2, 2 * b * nc * G * N * Q * 2
@@ -78,7 +78,7 @@ def test_workspace_follows_the_schedule_at_the_layer_shape():
     assert fused["total_bytes"] == cdt + cb + bt == 44_040_192
     split = ssd.workspace_layout(ssd.make_problem(b, T, H, P, N, G, Q, ssd.SSD_BF16, ssd.SCHEDULE_SPLIT))
     assert split["bt_bytes"] == 0
-    assert split["states_bytes"] == b * H * nc * P * N * 4 and split["hin_bytes"] == b * H * nc * P * N * 2
+    assert split["states_bytes"] == b * H * nc * P * N * 2 and split["hin_bytes"] == b * H * nc * P * N * 2
     assert split["total_bytes"] == cdt + cb + split["states_bytes"] + split["hin_bytes"]
 
 
@@ -177,7 +177,7 @@ def test_diag_table_path_workspace():
         tab = ssd.diag_uses_table(Q, P, N, dt)
         assert tab == ((Q * (P + 8) + 2 * Q * (N + 8)) * es + (2 * Q + N) * 4 > 160 * 1024)
         assert lay["cb_bytes"] == (2 * 4 * nc * Q * Q * es if tab else 0), (P, N, Q)
-        assert lay["states_bytes"] == 2 * 4 * nc * P * N * 4
+        assert lay["states_bytes"] == 2 * 4 * nc * P * N * es
     assert ssd.diag_uses_table(256, 64, 128, ssd.SSD_BF16) and not ssd.diag_uses_table(128, 64, 64, ssd.SSD_BF16)
 
 

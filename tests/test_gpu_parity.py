@@ -83,7 +83,7 @@ def test_stage_outputs_match_oracle_dumps(dtype, diag):
         return ws[off:off + nbytes].view(dt).reshape(shape).float().cpu().numpy()
     cdt = view(lay["cdt_off"], lay["cdt_bytes"], torch.float32, (b, H, nc, Q))
     np.testing.assert_allclose(cdt, st["cdt"], rtol=2e-6, atol=1e-6)
-    S = view(lay["states_off"], lay["states_bytes"], torch.float32, (b, H, nc, P, N))
+    S = view(lay["states_off"], lay["states_bytes"], td, (b, H, nc, P, N))  # stored in the input type
     Hc = view(lay["hin_off"], lay["hin_bytes"], td, (b, H, nc, P, N))
     tol = TOL[dtype]
     assert max_rel_err(S, st["S"], (0, 1, 2)) < tol
