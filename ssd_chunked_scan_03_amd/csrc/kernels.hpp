@@ -821,8 +821,30 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
         }
         __syncthreads();
     }
-    if (wact) {
-        ST* out = S + (bh * nc + c) * (int64_t)(P * N);
+    ST* out = S + (bh * nc + c) * (int64_t)(P * N);
+    // Where the state tile fits the B slab's LDS (stored in 16-bit types, P <= 64), it is
+    // staged there as rows and leaves in whole 16-byte row pieces; else each lane stores
+    // its 4 consecutive n straight from the accumulators (16 rows per store).
+    constexpr int LDS_ = N + 8;
+    if constexpr (sizeof(ST) == 2 && (size_t)P * LDS_ * sizeof(ST) <= (size_t)JB * LDB * sizeof(T)) {
+        ST* Ss = reinterpret_cast<ST*>(Bs);  // every wave is past its last read of Bs
+        if (wact) {
+#pragma unroll
+            for (int a = 0; a < TL::WN; ++a)
+#pragma unroll
+                for (int b = 0; b < TL::WP; ++b) {
+                    typename V4<ST>::type o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = from_f<ST>(acc[a][b][r]);
+                    st4(Ss + ((wp0 + b) * 16 + l16) * LDS_ + (wn0 + a) * 16 + 4 * q, o);
+                }
+        }
+        __syncthreads();
+        for (int v = tid; v < P * N / 8; v += kThreads) {
+            const int p = v / (N / 8), n0 = (v - p * (N / 8)) * 8;
+            st8(out + p * N + n0, ld8(Ss + p * LDS_ + n0));
+        }
+    } else if (wact) {
 #pragma unroll
         for (int a = 0; a < TL::WN; ++a)
 #pragma unroll
