@@ -68,6 +68,21 @@ struct Rows {
     }
 };
 
+// The (batch row, head, chunk) item of a one-dimensional grid of b * H * nc work-groups:
+// the heads of one (batch row, chunk) are adjacent, so the work-groups that read the same
+// per-chunk rows of B / C and the group's tables run together, and each XCD (blocks k,
+// k + 8, k + 16, ... are dispatched to one XCD) takes a contiguous range of items, so
+// those readers share its L2.  Returns b * H + h; c is the chunk.
+__device__ __forceinline__ int64_t chunk_item(int H, int nc, int& c) {
+    const int64_t nb = gridDim.x;
+    int64_t k = blockIdx.x;
+    if (nb % 8 == 0) k = (k % 8) * (nb / 8) + k / 8;
+    const int h = (int)(k % H);
+    const int64_t bc = k / H;
+    c = (int)(bc % nc);
+    return (bc / nc) * H + h;
+}
+
 // ---------------------------------------------------------------------------
 // k_rows: the packed-row map from the caller's cu_seqlens (nrows + 1 token offsets).
 // ts[r] = cu[r] clamped to [ts[r-1], T] (so every row lies inside the token axis, in
@@ -727,9 +742,8 @@ __global__ __launch_bounds__(kThreads) void k_state(const T* __restrict__ x, con
     __shared__ __attribute__((aligned(16))) T Bs[JB * LDB];
     __shared__ float cds[256];
     __shared__ float an2[DIAG ? N : 1];
-    const int64_t blk = blockIdx.x;
-    const int c = (int)(blk % nc);
-    const int64_t bh = blk / nc;
+    int c;
+    const int64_t bh = chunk_item(H, nc, c);
     const int h = (int)(bh % H);
     const int64_t bi = bh / H;
     const int g = h / (H / G);
@@ -1028,9 +1042,8 @@ __global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(cons
     float* u2 = cds + Q;       // scalar: exp(A (cdt_r(j) - cdt_j)), r(j) = j | 31
     float* an2 = u2 + Q;       // diagonal: A_n log2(e)
 
-    const int64_t blk = blockIdx.x;
-    const int c = (int)(blk % nc);
-    const int64_t bh = blk / nc;
+    int c;
+    const int64_t bh = chunk_item(H, nc, c);
     const int h = (int)(bh % H);
     const int64_t bi = bh / H;
     const int g = h / (H / G);
@@ -1348,9 +1361,8 @@ __global__ __launch_bounds__(kThreads, N <= 128 ? 3 : 2) void k_outs(const bf16*
     __shared__ __attribute__((aligned(16))) bf16 Hs[P * N];  // H_c (chunks swizzled by row)
     __shared__ float cds[Q], u2[Q];
 
-    const int64_t blk = blockIdx.x;
-    const int c = (int)(blk % nc);
-    const int64_t bh = blk / nc;
+    int c;
+    const int64_t bh = chunk_item(H, nc, c);
     const int h = (int)(bh % H);
     const int64_t bi = bh / H;
     const int g = h / (H / G);
@@ -1471,9 +1483,8 @@ __global__ __launch_bounds__(kThreads) void k_gtab(const T* __restrict__ Bm, con
     float* cj = ci + 64;                             // cdt of block J's rows
     float* an2 = cj + 64;                            // A_n log2(e)
 
-    const int64_t blk = blockIdx.x;
-    const int c = (int)(blk % nc);
-    const int64_t bh = blk / nc;
+    int c;
+    const int64_t bh = chunk_item(H, nc, c);
     const int h = (int)(bh % H);
     const int64_t bi = bh / H;
     const int g = h / (H / G);
