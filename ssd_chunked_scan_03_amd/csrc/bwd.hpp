@@ -1137,6 +1137,303 @@ __global__ __launch_bounds__(kBcThreads) void k_bwd_bc(const T* __restrict__ x, 
 }
 
 // ---------------------------------------------------------------------------
+// k_bwd_bcs: what k_bwd_bc computes, for bfloat16 at headdim 64 (n range NB = 64 or 128),
+// with each head's operands -- its dy rows [64 s, Q) and x rows [0, 64 s + 64), its H_c and
+// R_c tiles over the n range, its cdt row -- brought straight into LDS by direct transfers,
+// into one of two buffers: while the work-group computes one head from a buffer, the next
+// head's transfers land in the other.  (k_bwd_bc stages each head through registers one
+// head ahead, so it waits for every head's loads.)  The rows sit in xs_off's swizzled
+// layout; the H and R tiles in 64-column sub-tiles of the same layout (rows p), read as
+// transposed fragments.  The two buffers are separate arrays, so reads of one never wait
+// for the transfers into the other.
+// ---------------------------------------------------------------------------
+constexpr int kBcsThreads = 1024;  // k_bwd_bcs work-groups: 16 waves
+
+template <int Q, int NB>
+struct BcsCfg {
+    static constexpr int ROWS = Q + 64;                        // staged rows per head
+    static constexpr int RT = ROWS / 8;                        // 1 KB row transfers per head
+    static constexpr int NSUB = NB / 64;                       // 64-column sub-tiles of H (and of R)
+    static constexpr int ST = 2 * NSUB * 8;                    // state transfers per head
+    static constexpr int TPW = (RT + ST + 15) / 16;            // transfers per wave (16 waves)
+    static constexpr int BUF = ROWS * 64 + 2 * NSUB * 64 * 64; // bf16 elements of one buffer
+    static constexpr int LDC = Q + 8, LDW = 72;                // W rows of the slab, W columns of the slab
+    static_assert(64 * LDC <= BUF && Q * LDW <= BUF, "the W staging fits one buffer each");
+};
+
+template <int Q, int N, int NB>
+__global__ __launch_bounds__(kBcsThreads) void k_bwd_bcs(const bf16* __restrict__ x, const bf16* __restrict__ dy,
+                                                      const bf16* __restrict__ bt, const bf16* __restrict__ ct,
+                                                      const bf16* __restrict__ hin, const bf16* __restrict__ rin,
+                                                      const float* __restrict__ A, const float* __restrict__ cdt,
+                                                      bf16* __restrict__ dB, bf16* __restrict__ dC, int64_t Tn,
+                                                      int H, int G, int nc) {
+    typedef BcsCfg<Q, NB> CF;
+    constexpr int P = 64, ROWS = CF::ROWS, RT = CF::RT, NSUB = CF::NSUB, TPW = CF::TPW, BUF = CF::BUF;
+    constexpr int LDC = CF::LDC, LDW = CF::LDW, NBT = NB / 16, NR = N / NB, PN = P * N;
+    constexpr int NW = kBcsThreads / 64;                 // 16 waves
+    constexpr int nslab = Q / 64;
+    constexpr int NTMAX = 16 * nslab - 6;                // W tiles a slab needs
+    constexpr int NTW = (NTMAX + NW - 1) / NW;
+    constexpr int NSP = NW / 4;                          // n-tile splits of the state terms
+    constexpr int NBH = NBT >= NSP ? NBT / NSP : 1;
+    constexpr float LOG2E = 1.4426950408889634f;
+    __shared__ __attribute__((aligned(16))) bf16 buf0[BUF];
+    __shared__ __attribute__((aligned(16))) bf16 buf1[BUF];
+    __shared__ __attribute__((aligned(16))) float cdq0[Q];
+    __shared__ __attribute__((aligned(16))) float cdq1[Q];
+    __shared__ float cdh[Q], es[Q], ee[Q], sci[Q], scj[Q];
+
+    // work item (b, c, g, slab, n range); each XCD takes a contiguous range, so the slabs
+    // of one chunk, which stage the same heads' rows and tiles, share an L2
+    int64_t blk = blockIdx.x;
+    if (gridDim.x % 8 == 0) blk = (blk % 8) * (gridDim.x / 8) + blk / 8;
+    const int nr = (int)(blk % NR);
+    blk /= NR;
+    const int s = (int)(blk % nslab);
+    blk /= nslab;
+    const int g = (int)(blk % G);
+    blk /= G;
+    const int c = (int)(blk % nc);
+    const int64_t bi = blk / nc;
+    const int n0 = nr * NB;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), l16 = lane & 15, q = lane >> 4;
+    const int64_t tok0 = (int64_t)c * Q;
+    const int len = (int)((Tn - tok0) < Q ? (Tn - tok0) : Q);
+    const int hpg = H / G, hbeg = g * hpg, hend = hbeg + hpg;
+    const int s64 = 64 * s, NY = Q - s64;  // dy row i at tile row i - 64 s; x row j at tile row NY + j
+
+    // buffer resources based at this batch row: rows past T read as zero
+    const int XS = H * P * 2;
+    const uint32_t xbytes = (uint32_t)(Tn * H * P * 2);
+    const brsrc rx = make_rsrc(x + bi * Tn * H * P, xbytes);
+    const brsrc rdy = make_rsrc(dy + bi * Tn * H * P, xbytes);
+    const uint32_t sbytes = (uint32_t)((int64_t)H * nc * PN * 2);
+    const brsrc rh = make_rsrc(hin + bi * H * nc * PN, sbytes);
+    const brsrc rr = make_rsrc(rin + bi * H * nc * PN, sbytes);
+    const brsrc rcd = make_rsrc(cdt + bi * H * nc * Q, (uint32_t)((int64_t)H * nc * Q * 4));
+
+    // head hh's transfers into buffer bb and its cdt row into cq; the caller waits (vmcnt)
+    // and synchronises before reading them
+    auto issue = [&](int hh, bf16* bb, float* cq) {
+        int ln = lane_now();  // rebuilt per call, not kept live
+        const int hcol = hh * P * 2;
+        const int vr0 = xs_dma_lane(ln, 0, XS, hcol), vr1 = xs_dma_lane(ln, 1, XS, hcol);
+        const int vs0 = xs_dma_lane(ln, 0, N * 2, n0 * 2), vs1 = xs_dma_lane(ln, 1, N * 2, n0 * 2);
+        const int st0 = (hh * nc + c) * PN * 2;  // the head's state tile within the batch row, bytes
+#pragma unroll
+        for (int r = 0; r < TPW; ++r) {
+            const int m = w * TPW + r;
+            if (m >= RT + CF::ST) {
+            } else if (m < RT) {
+                // rows 8 m .. 8 m + 7 of the row tile: dy rows first, then x rows (NY is a
+                // multiple of 64, so no transfer mixes the two)
+                const bool isy = 8 * m < NY;
+                const int tok = isy ? s64 + 8 * m : 8 * m - NY;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(isy ? rdy : rx,
+                                                         (__attribute__((address_space(3))) void*)(bb + m * 512), 16,
+                                                         xs_dma_bit(m) ? vr1 : vr0,
+                                                         __builtin_amdgcn_readfirstlane((c * Q + tok) * XS), 0, 0);
+            } else {
+                // state transfer k: tensor k / (8 NSUB) (H, R), sub-tile (k / 8) % NSUB, rows 8 (k % 8) ..
+                const int k = m - RT, t = k / (8 * NSUB), sub = (k / 8) % NSUB, mm = k % 8;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    t ? rr : rh,
+                    (__attribute__((address_space(3))) void*)(bb + ROWS * 64 + (t * NSUB + sub) * 4096 + mm * 512), 16,
+                    (xs_dma_bit(mm) ? vs1 : vs0) + sub * 128,
+                    __builtin_amdgcn_readfirstlane(st0 + 8 * mm * N * 2), 0, 0);
+            }
+        }
+        if (w == 0 && ln * 4 < Q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rcd, (__attribute__((address_space(3))) void*)cq, 16, ln * 16,
+                                                     __builtin_amdgcn_readfirstlane((hh * nc + c) * Q * 4), 0, 0);
+    };
+    // the head's decay tables from its cdt row
+    auto tables = [&](int hh, const float* cq) {
+        if (tid < Q) {
+            const float ah2 = A[hh] * LOG2E;
+            const float cv = cq[tid], c0v = cq[tid & ~15], c15v = cq[tid | 15], clv = cq[Q - 1];
+            cdh[tid] = cv;
+            es[tid] = exp2f_fast(ah2 * (cv - c0v));
+            ee[tid] = exp2f_fast(ah2 * (c15v - cv));
+            sci[tid] = exp2f_fast(ah2 * cv);
+            scj[tid] = exp2f_fast(ah2 * (clv - cv));
+        }
+    };
+
+    // tile u -> (I, J): first the rows of the slab (J <= I), then the columns of the slab
+    // below it
+    auto tile_ij = [&](int u, int& I, int& J) {
+        const int nA = 16 * s + 10;
+        if (u < nA) {
+            int a = 0, base = 0;
+            while (a < 3 && u >= base + 4 * s + a + 1) {
+                base += 4 * s + a + 1;
+                ++a;
+            }
+            I = 4 * s + a;
+            J = u - base;
+        } else {
+            const int v = u - nA;
+            I = 4 * s + 4 + v / 4;
+            J = 4 * s + (v & 3);
+        }
+    };
+
+    f32x4 accW[NTW], accC[NBH], accB[NBH];
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) accW[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NBH; ++nt) accC[nt] = accB[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int rt = w & 3, nh = w >> 2;  // row tile of the slab, n-tile split
+    const bool sact = nh < NBT / NBH;   // (fewer n tiles than splits: the rest idle)
+    const int nb0 = nh * NBH;           // first n tile of this wave
+    const int iw = s64 + rt * 16 + l16; // this wave's row (dC) and column (dB) token
+
+    // this wave's W tiles (the same for every head; wave-uniform)
+    int tI[NTW], tJ[NTW];
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) {
+        tI[m] = tJ[m] = 0;
+        if (w + NW * m < NTMAX) tile_ij(w + NW * m, tI[m], tJ[m]);
+    }
+
+    // one head from buffer bb: W tiles, decay-masked, into accW; the state terms
+    auto compute = [&](int hh, const bf16* bb) {
+        const float ah2 = A[hh] * LOG2E;
+        const bf16* Ys = bb;                 // the staged rows
+        const bf16* Hs = bb + ROWS * 64;     // H sub-tiles, then R sub-tiles
+        const bf16* Rs = Hs + NSUB * 4096;
+#pragma unroll
+        for (int m = 0; m < NTW; ++m) {
+            const int u = w + NW * m;
+            if (u < NTMAX) {
+                const int I = tI[m], J = tJ[m];
+                const int i = I * 16 + l16, j = J * 16 + l16;
+                f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p0 = 0; p0 < P; p0 += 32)
+                    t = mma(t, ld8(Ys + xs_off(i - s64, p0 + 8 * q)), ld8(Ys + xs_off(NY + j, p0 + 8 * q)));
+                // lane: W[I*16 + 4q + r][J*16 + l16]
+                if (I > J) {
+                    const float f = exp2f_fast(ah2 * (cdh[I * 16] - cdh[J * 16 + 15])) * ee[J * 16 + l16];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) accW[m][r] += t[r] * (es[I * 16 + 4 * q + r] * f);
+                } else {
+                    const float cj = cdh[J * 16 + l16];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int ii = I * 16 + 4 * q + r;
+                        const float L = exp2f_fast(fminf(ah2 * (cdh[ii] - cj), 0.f));
+                        accW[m][r] += (ii >= J * 16 + l16) ? t[r] * L : 0.f;
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one tile's fragments in flight at a time
+        }
+        // state terms: this wave's 16 tokens, its share of the n tiles of the range
+        if (sact) {
+            const float si = sci[iw], sj = scj[iw];
+#pragma unroll
+            for (int p0 = 0; p0 < P; p0 += 32) {
+                bf16x8 yb = ld8(Ys + xs_off(iw - s64, p0 + 8 * q));
+                bf16x8 xb8 = ld8(Ys + xs_off(NY + iw, p0 + 8 * q));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    yb[e] = (bf16)((float)yb[e] * si);
+                    xb8[e] = (bf16)((float)xb8[e] * sj);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NBH; ++nt) {
+                    const int nn = (nb0 + nt) * 16, sub = nn / 64, cc = nn % 64;
+                    accC[nt] = mma(accC[nt], frag_xs(Hs + sub * 4096, p0, cc, lane), yb);
+                    accB[nt] = mma(accB[nt], frag_xs(Rs + sub * 4096, p0, cc, lane), xb8);
+                }
+            }
+        }
+    };
+
+    issue(hbeg, buf0, cdq0);
+    for (int hh = hbeg; hh < hend; hh += 2) {
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's transfers of head hh
+        __syncthreads();                    // ... every wave's; every wave is done with head hh - 1
+        tables(hh, cdq0);
+        __syncthreads();
+        if (hh + 1 < hend) issue(hh + 1, buf1, cdq1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(hh, buf0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (hh + 1 < hend) {
+            __builtin_amdgcn_s_waitcnt(0xF70);
+            __syncthreads();
+            tables(hh + 1, cdq1);
+            __syncthreads();
+            if (hh + 2 < hend) issue(hh + 2, buf0, cdq0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(hh + 1, buf1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // ---- once per group: W through LDS (W rows of the slab in buf0, W columns of the slab
+    //      in buf1), then the products with B^T and C^T ----
+    bf16* Wc = buf0;  // [64][Q + 8]  W rows i of the slab, all j
+    bf16* Wb = buf1;  // [Q][72]      W rows i >= slab start, columns of the slab
+    __syncthreads();  // every wave is done with the last head's buffer
+    for (int v = tid; v < 64 * LDC / 8; v += kBcsThreads) reinterpret_cast<u32x4v*>(Wc)[v] = u32x4v{0u, 0u, 0u, 0u};
+    for (int v = tid; v < Q * LDW / 8; v += kBcsThreads) reinterpret_cast<u32x4v*>(Wb)[v] = u32x4v{0u, 0u, 0u, 0u};
+    __syncthreads();
+    const int NT = NTMAX;
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) {
+        const int u = w + NW * m;
+        if (u < NT) {
+            int I, J;
+            tile_ij(u, I, J);
+            const int j = J * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = I * 16 + 4 * q + r;
+                const bf16 v = (bf16)accW[m][r];
+                if (I >= 4 * s && I < 4 * s + 4) Wc[(i - s64) * LDC + j] = v;
+                if (J >= 4 * s && J < 4 * s + 4) Wb[(i - s64) * LDW + (j - s64)] = v;
+            }
+        }
+    }
+    __syncthreads();
+    const bf16* btb = bt + ((bi * nc + c) * G + g) * (int64_t)N * Q;  // [n][j], fragment order
+    const bf16* ctb = ct + ((bi * nc + c) * G + g) * (int64_t)N * Q;
+    if (!sact) return;
+    for (int j0 = 0; j0 < s64 + 64; j0 += 32) {
+        const bf16x8 wf = ld8(&Wc[(iw - s64) * LDC + j0 + 8 * q]);
+#pragma unroll
+        for (int nt = 0; nt < NBH; ++nt)
+            accC[nt] = mma(accC[nt], ld8(btb + tfrag(n0 + (nb0 + nt) * 16 + l16, j0 + 8 * q, Q)), wf);
+    }
+    for (int i0 = s64; i0 < Q; i0 += 32) {
+        const bf16x8 wf = frag_rows(Wb, LDW, i0 - s64, rt * 16, lane);
+#pragma unroll
+        for (int nt = 0; nt < NBH; ++nt)
+            accB[nt] = mma(accB[nt], ld8(ctb + tfrag(n0 + (nb0 + nt) * 16 + l16, i0 + 8 * q, Q)), wf);
+    }
+    if (iw < len) {
+        bf16* dCr = dC + ((bi * Tn + tok0 + iw) * G + g) * N + n0;
+        bf16* dBr = dB + ((bi * Tn + tok0 + iw) * G + g) * N + n0;
+#pragma unroll
+        for (int nt = 0; nt < NBH; ++nt) {
+            bf16x4 oc, ob;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                oc[r] = (bf16)accC[nt][r];
+                ob[r] = (bf16)accB[nt][r];
+            }
+            st4(dCr + (nb0 + nt) * 16 + 4 * q, oc);
+            st4(dBr + (nb0 + nt) * 16 + 4 * q, ob);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // k_bwd_dt: dl_t = dL/d(dt_t A) = sum_{u >= t} ds_u + <dhT, hT>, ddt_t = A dl_t, and
 // partials sum_t dt_t dl_t of dA.
 // The running sum restarts at every chunk: at the first token of chunk c + 1, dl equals

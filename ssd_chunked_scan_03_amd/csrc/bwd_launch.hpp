@@ -180,10 +180,35 @@ int run_bwd(const BwdArgs& a) {
         k_bwd_x<T, P, N><<<g3, kThreads, sx, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
                                                   static_cast<T*>(a.dx), a.ds, a.dDp, a.T, H, G, Q, nc);
     }
-    (void)hipFuncSetAttribute((const void*)k_bwd_bc<T, P, N, NB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sbc);
-    const dim3 g7((unsigned)(a.b * nc * G * (Q / 64) * (N / NB)));
-    k_bwd_bc<T, P, N, NB><<<g7, kBcThreads, sbc, s>>>(x, dy, bt, ct, hin, rin, a.A, a.cdt, static_cast<T*>(a.dB),
-                                                    static_cast<T*>(a.dC), a.T, H, G, Q, nc);
+    bool bc_done = false;
+    if constexpr (std::is_same<T, bf16>::value && P == 64 && (N == 64 || N == 128)) {
+        // the double-buffered variant: buffer offsets of a batch row within 32 bits
+        const int64_t lim = (int64_t)1 << 31;
+        if (a.T * H * P * 2 < lim && H * a.nc * P * N * 2 < lim && H * a.nc * Q * 4 < lim) {
+            const dim3 g7((unsigned)(a.b * nc * G * (Q / 64)));
+            const bf16* xb = x;
+            switch (Q) {
+                case 64: k_bwd_bcs<64, N, N><<<g7, kBcsThreads, 0, s>>>(xb, dy, bt, ct, hin, rin, a.A, a.cdt,
+                                                                      static_cast<T*>(a.dB), static_cast<T*>(a.dC),
+                                                                      a.T, H, G, nc); break;
+                case 128: k_bwd_bcs<128, N, N><<<g7, kBcsThreads, 0, s>>>(xb, dy, bt, ct, hin, rin, a.A, a.cdt,
+                                                                        static_cast<T*>(a.dB), static_cast<T*>(a.dC),
+                                                                        a.T, H, G, nc); break;
+                case 256: k_bwd_bcs<256, N, N><<<g7, kBcsThreads, 0, s>>>(xb, dy, bt, ct, hin, rin, a.A, a.cdt,
+                                                                        static_cast<T*>(a.dB), static_cast<T*>(a.dC),
+                                                                        a.T, H, G, nc); break;
+                default: return 3;
+            }
+            bc_done = true;
+        }
+    }
+    if (!bc_done) {
+        (void)hipFuncSetAttribute((const void*)k_bwd_bc<T, P, N, NB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)sbc);
+        const dim3 g7((unsigned)(a.b * nc * G * (Q / 64) * (N / NB)));
+        k_bwd_bc<T, P, N, NB><<<g7, kBcThreads, sbc, s>>>(x, dy, bt, ct, hin, rin, a.A, a.cdt, static_cast<T*>(a.dB),
+                                                        static_cast<T*>(a.dC), a.T, H, G, Q, nc);
+    }
     k_bwd_dt<128><<<(unsigned)(a.b * nc), 128, 0, s>>>(a.ds, a.dt, a.A, a.kpart, a.ddt, a.dAp, a.T, H, Q, nc,
                                                        nslot, nvalid);
     k_bwd_reduce<kThreads><<<(unsigned)H, kThreads, 0, s>>>(a.dAp, a.dDp, a.dA, a.dD, a.b, H, nc);
