@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_x(const T* __restrict__ x, con
 // register holds them in flight; each wave then takes its row tiles one at a time (one
 // tile's accumulators live, not four), its state term from the LDS state tile and its
 // diagonal block from the C B^T (or transposed) table in L2, and dx leaves in whole rows.
-// That fits three work-groups per CU.  Per row tile, phase 1 keeps only dy_i . yhat_i (a
+// Its LDS fits three work-groups per CU.  Per row tile, phase 1 keeps only dy_i . yhat_i (a
 // scalar per row) for phase 2's decay term.
 // ---------------------------------------------------------------------------
 template <int Q, int N>
@@ -613,8 +613,11 @@ struct BxsCfg {
     static constexpr int NF = N / 32;           // 32-wide n-steps of the state term
 };
 
+// Registers: at chunk 256 two work-groups per CU (226 registers, no spills; within the 168
+// that a third allows it spilled 49 per lane, which measured 150 us slower at the 2.7B layer
+// shape); smaller chunks fit three.
 template <int Q, int N>
-__global__ __launch_bounds__(kThreads, 3) void k_bwd_xs(const bf16* __restrict__ x, const bf16* __restrict__ dy,
+__global__ __launch_bounds__(kThreads, Q >= 256 ? 2 : 3) void k_bwd_xs(const bf16* __restrict__ x, const bf16* __restrict__ dy,
                                                      const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
                                                      const bf16* __restrict__ cb, const bf16* __restrict__ cbt,
                                                      const bf16* __restrict__ hin, const bf16* __restrict__ rin,
