@@ -397,8 +397,9 @@ int step(const ssd_problem* p, int diag, const void* x, const float* dt, const f
 
 // ---- backward pass (ssd_scan_bwd) ----
 struct BwdLayout {
-    size_t cdt, cb, cbt, bt, ct, states, hin, rin, hTf, ds, dDp, dAp, kpart, zh, yh, dxp, ddtp, total;
-    bool has_states;  // (the chunk walks need no chunk-state region)
+    size_t cdt, cb, cbt, bt, ct, bcp, ccp, states, hin, rin, hTf, ds, dDp, dAp, kpart, zh, yh, dxp, ddtp, total;
+    bool has_states;
+    bool has_copies;  // B and C per chunk by token (k_bwd_xs)  // (the chunk walks need no chunk-state region)
 };
 
 // Scalar decay: C B^T tables, per-token decay terms and boundary partials, and the chunk
@@ -441,6 +442,11 @@ BwdLayout bwd_layout_of(const ssd_problem* p, int diag) {
     take(L.cbt, bgc * (size_t)(Q * Q) * es);
     take(L.bt, bgc * (size_t)(N * Q) * es);
     take(L.ct, bgc * (size_t)(N * Q) * es);
+    L.has_copies = ssd::xs_applies(p->dtype == SSD_BF16, T, H, P, N, G, Q);
+    if (L.has_copies) {
+        take(L.bcp, bgc * (size_t)(N * Q) * es);
+        take(L.ccp, bgc * (size_t)(N * Q) * es);
+    }
     // chunk states (and the adjoint's chunk inputs) only where the chunk walks do not run
     L.has_states = !ssd::walks_apply(p->dtype == SSD_BF16, b, T, H, P, N, G, Q);
     if (L.has_states) take(L.states, bhc * (size_t)(P * N) * 4);
@@ -546,6 +552,8 @@ int scan_bwd(const ssd_problem* p, int diag, const void* x, const float* dt, con
     a.cbt = w + L.cbt;
     a.bt = w + L.bt;
     a.ct = w + L.ct;
+    a.bcp = L.has_copies ? static_cast<void*>(w + L.bcp) : nullptr;
+    a.ccp = L.has_copies ? static_cast<void*>(w + L.ccp) : nullptr;
     a.states = L.has_states ? reinterpret_cast<float*>(w + L.states) : nullptr;
     a.hin = w + L.hin;
     a.rin = w + L.rin;

@@ -618,7 +618,7 @@ struct BxsCfg {
 // shape); smaller chunks fit three.
 template <int Q, int N>
 __global__ __launch_bounds__(kThreads, Q >= 256 ? 2 : 3) void k_bwd_xs(const bf16* __restrict__ x, const bf16* __restrict__ dy,
-                                                     const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
+                                                     const bf16* __restrict__ Bf, const bf16* __restrict__ Cf,
                                                      const bf16* __restrict__ cb, const bf16* __restrict__ cbt,
                                                      const bf16* __restrict__ hin, const bf16* __restrict__ rin,
                                                      const float* __restrict__ A, const float* __restrict__ D,
@@ -645,13 +645,15 @@ __global__ __launch_bounds__(kThreads, Q >= 256 ? 2 : 3) void k_bwd_xs(const bf1
 
     // buffer resources based at this batch row (rows past T read as zero, stores dropped),
     // the group's tables and this chain's states
-    const int XS = H * P * 2, CS = G * N * 2;  // row strides in bytes
+    const int XS = H * P * 2;  // x / dy / dx row stride in bytes
     const uint32_t xbytes = (uint32_t)(Tn * H * P * 2);
     const brsrc rx = make_rsrc(x + bi * Tn * H * P, xbytes);
     const brsrc rdy = make_rsrc(dy + bi * Tn * H * P, xbytes);
     const brsrc rdx = make_rsrc(dx + bi * Tn * H * P, xbytes);
-    const brsrc rc = make_rsrc(Cm + bi * Tn * G * N, (uint32_t)(Tn * G * N * 2));
-    const brsrc rb = make_rsrc(Bm + bi * Tn * G * N, (uint32_t)(Tn * G * N * 2));
+    // B and C per chunk by token, in fragment order (tokens past T hold zeros)
+    const uint32_t fbytes = (uint32_t)((int64_t)nc * G * Q * N * 2);
+    const brsrc rc = make_rsrc(Cf + bi * nc * G * Q * N, fbytes);
+    const brsrc rb = make_rsrc(Bf + bi * nc * G * Q * N, fbytes);
     const uint32_t tbytes = (uint32_t)((int64_t)nc * G * Q * Q * 2);
     const brsrc rcb = make_rsrc(cb + bi * nc * G * Q * Q, tbytes);
     const brsrc rcbt = make_rsrc(cbt + bi * nc * G * Q * Q, tbytes);
@@ -660,19 +662,19 @@ __global__ __launch_bounds__(kThreads, Q >= 256 ? 2 : 3) void k_bwd_xs(const bf1
     const brsrc rr = make_rsrc(rin + bh * nc * PN, sbytes);
     const int hcol = h * P * 2;
     const int tab0 = (c * G + g) * Q * Q * 2;                    // this chunk's table, bytes
-    const int vc = l16 * CS + 8 * q * 2;                         // C / B row l16 of a tile, n-group q
 
     // the chunk's rows (x or dy) and a state tile (H_c or R_c) into LDS, this wave's share
     auto stage = [&](brsrc rrows, brsrc rstate) {
         dma_rows_state<Q, N>(Ts, Hs, rrows, c * Q * XS, XS, hcol, rstate, c * PN * 2, w);
     };
     auto row_tile = [&](int k) { return (RPW == 1) ? w : ((k & 1) ? 8 * (k >> 1) + 7 - w : 8 * (k >> 1) + w); };
-    // state term of one row tile: acc^T[p][t] = sum_n S[p][n] V_t[n] (S in Hs, V = C or B rows)
+    // state term of one row tile: acc^T[p][t] = sum_n S[p][n] V_t[n] (S in Hs, V = C or B
+    // rows; each 16 x 32 fragment one contiguous 1 KB run)
     auto state_term = [&](f32x4* acc, brsrc rv, int rt) {
         bf16x8 vf[NF];
-        const int sv = __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * CS + g * N * 2);
+        const int sv = __builtin_amdgcn_readfirstlane(((c * G + g) * Q * N + rt * (N / 32) * 512) * 2);
 #pragma unroll
-        for (int n = 0; n < NF; ++n) vf[n] = bload8(rv, vc, sv + n * 64);
+        for (int n = 0; n < NF; ++n) vf[n] = bload8(rv, lane * 16, sv + n * 1024);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -702,6 +704,13 @@ __global__ __launch_bounds__(kThreads, Q >= 256 ? 2 : 3) void k_bwd_xs(const bf1
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             if (ks < nks) gf[ks] = bload8(rcb, lane * 16, __builtin_amdgcn_readfirstlane(tab0 + (rt * (Q / 32) + ks) * 1024));
+        // the tile's dy rows for dy_i . yhat_i, requested with the tile's other operands
+        const int sy = __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * XS);
+        bf16x4 dv[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+            dv[pt] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                    rdy, l16 * XS + hcol + (pt * 16 + 4 * q) * 2, sy, 0));
         f32x4 acc[4];
         state_term(acc, rc, rt);
         const float ci = cds[i];
@@ -731,17 +740,14 @@ __global__ __launch_bounds__(kThreads, Q >= 256 ? 2 : 3) void k_bwd_xs(const bf1
             }
         }
         // dy_i . yhat_i (lane (i, q) holds p = 16 pt + 4 q + r), and dy . x for dD
-        const int sy = __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * XS);
         float s = 0.f;
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-            const bf16x4 dv = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
-                                                             rdy, l16 * XS + hcol + (pt * 16 + 4 * q) * 2, sy, 0));
             const bf16x4 xv = ld4(Ts + xs_off(i, pt * 16 + 4 * q));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                s += (float)dv[r] * acc[pt][r];
-                dd += (float)dv[r] * (float)xv[r];
+                s += (float)dv[pt][r] * acc[pt][r];
+                dd += (float)dv[pt][r] * (float)xv[r];
             }
         }
         p1[k] = sum_q(s);
@@ -765,6 +771,13 @@ __global__ __launch_bounds__(kThreads, Q >= 256 ? 2 : 3) void k_bwd_xs(const bf1
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             if (ks >= kd) gf[ks] = bload8(rcbt, lane * 16, __builtin_amdgcn_readfirstlane(tab0 + (rt * (Q / 32) + ks) * 1024));
+        // the tile's x rows for x_j . dxhat_j, requested with the tile's other operands
+        const int sx = __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * XS);
+        bf16x4 xv[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+            xv[pt] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                                    rx, l16 * XS + hcol + (pt * 16 + 4 * q) * 2, sx, 0));
         f32x4 acc[4];
         state_term(acc, rb, rt);
         const float cj = cds[j];
@@ -794,16 +807,13 @@ __global__ __launch_bounds__(kThreads, Q >= 256 ? 2 : 3) void k_bwd_xs(const bf1
             }
         }
         // ds_j = dy_j . yhat_j - x_j . dxhat_j; dx = dxhat + D dy
-        const int sx = __builtin_amdgcn_readfirstlane((c * Q + rt * 16) * XS);
         float s = 0.f;
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-            const bf16x4 xv = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
-                                                             rx, l16 * XS + hcol + (pt * 16 + 4 * q) * 2, sx, 0));
             const bf16x4 dv = ld4(Ts + xs_off(j, pt * 16 + 4 * q));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                s += (float)xv[r] * acc[pt][r];
+                s += (float)xv[pt][r] * acc[pt][r];
                 acc[pt][r] += Dh * (float)dv[r];
             }
         }

@@ -34,6 +34,8 @@ struct BwdArgs {
     void* cbt;      // [b,nc,G,Q,Q]  its transpose, cbt[j][i] = B_j . C_i
     void* bt;       // [b,nc,G,N,Q]  B per chunk, tokens contiguous
     void* ct;       // [b,nc,G,N,Q]  C per chunk, tokens contiguous
+    void* bcp;      // [b,nc,G,Q,N]  B per chunk by token (k_bwd_xs's state-term operand), or null
+    void* ccp;      // [b,nc,G,Q,N]  C per chunk by token, or null
     float* states;  // [b,H,nc,P,N]  chunk states, then adjoint chunk inputs
     void* hin;      // [b,H,nc,P,N]  forward state entering each chunk
     void* rin;      // [b,H,nc,P,N]  adjoint arriving at each chunk's last token
@@ -54,6 +56,15 @@ struct BwdArgs {
 // (batch, head) chains to occupy every CU and the shape is theirs: bfloat16, headdim 64,
 // dstate 64 or 128, and buffer offsets of a batch row within 32 bits.  (The workspace
 // layout takes the same decision: the walks need no chunk-state region.)
+// Whether the backward's dx runs k_bwd_xs (bfloat16, headdim 64, dstate 64 or 128, buffer
+// offsets of a batch row within 32 bits); it then reads B and C per chunk by token in
+// fragment order (two more workspace regions).
+inline bool xs_applies(bool bf16_dtype, int64_t T, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
+    const int64_t lim = (int64_t)1 << 31, nc = (T + Q - 1) / Q;
+    return bf16_dtype && P == 64 && (N == 64 || N == 128) && T * H * P * 2 < lim && nc * G * N * Q * 2 < lim &&
+           nc * G * Q * Q * 2 < lim && nc * P * N * 2 < lim;
+}
+
 inline bool walks_apply(bool bf16_dtype, int64_t b, int64_t T, int64_t H, int64_t P, int64_t N, int64_t G,
                         int64_t Q) {
     const int64_t lim = (int64_t)1 << 31, nc = (T + Q - 1) / Q;
@@ -117,8 +128,9 @@ int run_bwd(const BwdArgs& a) {
     k_cb<T, N, false><<<g2, kThreads, 0, s>>>(Bm, Cm, cb, rows, G, Q);
     k_cb<T, N, true><<<g2, kThreads, 0, s>>>(Bm, Cm, cbt, rows, G, Q);
     const dim3 g6(kc * (unsigned)(Q / 64), (unsigned)G);
-    k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, bt, nullptr, nullptr, rows, G, Q);
-    k_bt<T, N><<<g6, kThreads, 0, s>>>(Cm, ct, nullptr, nullptr, rows, G, Q);
+    // B^T and C^T per chunk; with a.bcp / a.ccp also B and C per chunk by token
+    k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, bt, a.bcp ? Bm : nullptr, static_cast<T*>(a.bcp), rows, G, Q);
+    k_bt<T, N><<<g6, kThreads, 0, s>>>(Cm, ct, a.ccp ? Cm : nullptr, static_cast<T*>(a.ccp), rows, G, Q);
     const dim3 g3((unsigned)(a.b * H * nc));
     const int per_head = (int)((a.P * a.N / 4 + kThreads - 1) / kThreads);
     int nvalid = (int)(a.P * a.N / 4 / 64);  // partials of <R_c, H_{c+1}> per chunk
@@ -160,15 +172,16 @@ int run_bwd(const BwdArgs& a) {
     // gradients: dx and the per-token decay term (LDS-staged kernel where it applies)
     bool xs_done = false;
     if constexpr (std::is_same<T, bf16>::value && P == 64 && (N == 64 || N == 128)) {
-        const int64_t lim = (int64_t)1 << 31;
-        if (a.T * H * P * 2 < lim && a.T * G * N * 2 < lim && a.nc * G * Q * Q * 2 < lim && a.nc * P * N * 2 < lim) {
+        if (a.bcp && a.ccp) {  // (the workspace has the copies exactly where xs_applies)
             bf16* dxp = static_cast<bf16*>(a.dx);
+            const bf16* Bf = static_cast<const bf16*>(a.bcp);
+            const bf16* Cf = static_cast<const bf16*>(a.ccp);
             switch (Q) {
-                case 64: k_bwd_xs<64, N><<<g3, kThreads, 0, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
+                case 64: k_bwd_xs<64, N><<<g3, kThreads, 0, s>>>(x, dy, Bf, Cf, cb, cbt, hin, rin, a.A, a.D, a.cdt,
                                                                  dxp, a.ds, a.dDp, a.T, H, G, nc); break;
-                case 128: k_bwd_xs<128, N><<<g3, kThreads, 0, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
+                case 128: k_bwd_xs<128, N><<<g3, kThreads, 0, s>>>(x, dy, Bf, Cf, cb, cbt, hin, rin, a.A, a.D, a.cdt,
                                                                    dxp, a.ds, a.dDp, a.T, H, G, nc); break;
-                case 256: k_bwd_xs<256, N><<<g3, kThreads, 0, s>>>(x, dy, Bm, Cm, cb, cbt, hin, rin, a.A, a.D, a.cdt,
+                case 256: k_bwd_xs<256, N><<<g3, kThreads, 0, s>>>(x, dy, Bf, Cf, cb, cbt, hin, rin, a.A, a.D, a.cdt,
                                                                    dxp, a.ds, a.dDp, a.T, H, G, nc); break;
                 default: return 3;
             }

@@ -364,7 +364,10 @@ def test_bwd_workspace_arithmetic():
     p = prob()  # b2 T300 H4 P64 N128 G2 Q128 bf16: 3 chunks
     b, H, P, N, G, Q, nc = 2, 4, 64, 128, 2, 128, 3
     a = lambda n: (n + 255) // 256 * 256
+    # cdt, C B^T both ways, B^T and C^T per chunk, B and C per chunk by token (bf16, headdim
+    # 64), chunk states (few chains: no walks), H_c and R_c, hT, ds, dD / dA partials, kpart
     want = (a(b * H * nc * Q * 4) + 2 * a(b * nc * G * Q * Q * 2) + 2 * a(b * nc * G * N * Q * 2)
+            + 2 * a(b * nc * G * N * Q * 2)
             + a(b * H * nc * P * N * 4) + 2 * a(b * H * nc * P * N * 2) + a(b * H * P * N * 4)
             + a(b * H * nc * Q * 4) + a(b * H * nc * 4) + a(b * H * nc * 4)
             + a(b * H * nc * 4 * ((P * N // 4 + 255) // 256) * 4))
@@ -379,12 +382,15 @@ def test_bwd_workspace_arithmetic():
 def test_bwd_workspace_without_chunk_states_when_the_walks_run():
     """With 512 or more (batch, head) chains at bfloat16, headdim 64 and dstate 64 / 128 the
     chunk walks carry both recurrences on chip: no float32 chunk-state region (335 MB at the
-    2.7B layer shape); float32, other headdims and fewer chains keep it."""
+    2.7B layer shape); float32, other headdims and fewer chains keep it.  At bfloat16,
+    headdim 64 and dstate 64 / 128 (k_bwd_xs) B and C are also copied per chunk by token."""
     a = lambda n: (n + 255) // 256 * 256
 
     def want(b, T, H, P, N, G, Q, es, states):
         nc = -(-T // Q)
+        copies = es == 2 and P == 64 and N in (64, 128)
         return (a(b * H * nc * Q * 4) + 2 * a(b * nc * G * Q * Q * es) + 2 * a(b * nc * G * N * Q * es)
+                + (2 * a(b * nc * G * N * Q * es) if copies else 0)
                 + (a(b * H * nc * P * N * 4) if states else 0) + 2 * a(b * H * nc * P * N * es)
                 + a(b * H * P * N * 4) + a(b * H * nc * Q * 4) + 2 * a(b * H * nc * 4)
                 + a(b * H * nc * 4 * ((P * N // 4 + 255) // 256) * 4))
