@@ -120,6 +120,11 @@ CASES = [  # b, T, H, P, N, G, Q, dtype
     (4, 130, 128, 64, 128, 1, 64, "bf16"),
     (8, 257, 64, 64, 128, 1, 256, "bf16"),
     (1, 100, 515, 64, 64, 5, 64, "bf16"),
+    # bfloat16, headdim 64, fewer chains: k_bwd_xs and k_bwd_bcs at every (chunk, dstate)
+    # pair, ragged last chunks, an odd head count per group
+    (2, 600, 6, 64, 64, 2, 256, "bf16"),
+    (2, 300, 4, 64, 128, 2, 128, "bf16"),
+    (1, 333, 3, 64, 128, 1, 64, "bf16"),
 ]
 
 
