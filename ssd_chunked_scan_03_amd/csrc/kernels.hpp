@@ -672,8 +672,6 @@ __device__ __forceinline__ void dma_rows_state(bf16* Ts, bf16* Hs, brsrc rrows, 
 
 // Element offsets of a chunk's x rows in LDS: the swizzled 64-element rows for bfloat16
 // at headdim 64 (no bank conflicts in the transpose reads), else rows padded by 8.
-// (The diagonal-decay output kernel keeps the padded rows: its split-row fragments would
-// need more address registers than its occupancy allows.)
 template <typename T, int P, bool ALLOW = true>
 struct XRows {
     static constexpr bool SWZ = ALLOW && sizeof(T) == 2 && P == 64;
@@ -999,11 +997,29 @@ __global__ __launch_bounds__(kThreads) void k_scan_carry(const float* __restrict
 // Each wave owns Q/64 row tiles of 16 rows, paired (k, 7-k) within every 128 rows so
 // the causal work is balanced.  y is staged through LDS (aliasing x) for row stores.
 // ---------------------------------------------------------------------------
-template <typename T, int P, int N, bool DIAG, bool TAB = false>
+// SWZR (diagonal decay): the x rows and the rescaled C / B rows in swizzled unpadded
+// layouts (a smaller tile, chosen where it fits one more work-group per CU) instead of
+// rows padded by 8.
+template <typename T, int P, int N, bool DIAG, bool TAB = false, bool SWZR = false>
 struct OutSmem {
     static constexpr bool RESCALED = DIAG && !TAB;  // rescaled C / B rows in LDS
-    static constexpr int LDX = XRows<T, P, !RESCALED>::LD;  // x (then y) rows
-    static constexpr int LDN = N + 8;  // rescaled C / B rows (diagonal decay)
+    static constexpr bool XSWZ = !RESCALED || SWZR;   // x rows swizzled where XRows allows
+    static constexpr int LDX = XRows<T, P, XSWZ>::LD;  // x (then y) rows
+    // rescaled C / B rows: with SWZR and a 16-bit type unpadded, their 16-byte chunks
+    // XOR-swizzled by row (rc_off); else padded by 8
+    static constexpr bool RSWZ = SWZR && sizeof(T) == 2;
+    static constexpr int LDN = RSWZ ? N : N + 8;
+    // element offset of (row r, column n) of a rescaled C / B tile, n a multiple of 8 plus
+    // e < 8: the 16 rows a fragment reads land in distinct banks
+    __device__ static int rc_off(int r, int n) {
+        if constexpr (RSWZ) {
+            constexpr int RPB = (128 / N) > 1 ? 128 / N : 1;       // rows per 64-bank cycle
+            constexpr int NCH = (N / 8) < 16 ? N / 8 : 16;         // chunks the swizzle spans
+            return r * N + ((((n >> 3) ^ ((r / RPB) & (NCH - 1)))) << 3) + (n & 7);
+        } else {
+            return r * LDN + n;
+        }
+    }
     __host__ __device__ static int xs(int Q) { return Q * LDX; }
     __host__ __device__ static int diag_elems(int Q) { return RESCALED ? 2 * Q * LDN : 0; }
     __host__ __device__ static int floats(int Q) { return 2 * Q + (RESCALED ? N : 0); }
@@ -1018,7 +1034,7 @@ struct OutSmem {
 template <typename T, int P>
 constexpr int out_min_blocks() { return (sizeof(T) == 2 && P <= 64) ? 3 : 1; }
 
-template <typename T, int P, int N, bool DIAG, bool TAB = false>
+template <typename T, int P, int N, bool DIAG, bool TAB = false, bool SWZR = false>
 __global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(const T* __restrict__ x, const T* __restrict__ Bm,
                                                   const T* __restrict__ Cm, const T* __restrict__ cb,
                                                   const T* __restrict__ hin, const float* __restrict__ A,
@@ -1027,8 +1043,8 @@ __global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(cons
                                                   int64_t Tn, int H, int G, int Q, int nc) {
     typedef typename V8<T>::type v8;
     typedef typename V4<T>::type v4;
-    typedef OutSmem<T, P, N, DIAG, TAB> SM;
-    typedef XRows<T, P, !SM::RESCALED> XL;
+    typedef OutSmem<T, P, N, DIAG, TAB, SWZR> SM;
+    typedef XRows<T, P, SM::XSWZ> XL;
     constexpr bool SCAL = !DIAG || TAB;  // diagonal block from a table of query-key products
     constexpr int LDN = SM::LDN;
     constexpr int PT = P / 16;
@@ -1164,8 +1180,8 @@ __global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(cons
                     bv[e] = from_f<T>(to_f(br[e]) * exp2f_fast(an2[n0 + e] * dce));
                 }
             }
-            st8(&Ct[ii * LDN + n0], cv);
-            st8(&Bt[ii * LDN + n0], bv);
+            st8(&Ct[SM::rc_off(ii, n0)], cv);
+            st8(&Bt[SM::rc_off(ii, n0)], bv);
         }
     }
     __syncthreads();
@@ -1212,7 +1228,7 @@ __global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(cons
                         }
 #pragma unroll
                         for (int pt = 0; pt < PT; ++pt) {
-                            const v8 xf = frag_x<T, P, !SM::RESCALED>(Xs, ks * 32, pt * 16, lane);
+                            const v8 xf = frag_x<T, P, SM::XSWZ>(Xs, ks * 32, pt * 16, lane);
                             acc[k][pt] = mma(acc[k][pt], xf, mf);
                         }
                     }
@@ -1246,11 +1262,11 @@ __global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(cons
                                 const bool nv = (N % 32 == 0) || (nn < N);
                                 v8 a = zero8<T>(), b = zero8<T>();
                                 if (nv) {
-                                    a = ld8(&Bt[(J * 16 + l16) * LDN + nn]);
+                                    a = ld8(&Bt[SM::rc_off(J * 16 + l16, nn)]);
 #pragma unroll
                                     for (int e = 0; e < 8; ++e)
                                         a[e] = from_f<T>(to_f(a[e]) * exp2f_fast(an2[nn + e] * dm));
-                                    b = ld8(&Ct[(sI + l16) * LDN + nn]);
+                                    b = ld8(&Ct[SM::rc_off(sI + l16, nn)]);
                                 }
                                 gt[s2] = mma(gt[s2], a, b);
                             }
@@ -1287,7 +1303,7 @@ __global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(cons
                     }
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) {
-                        const v8 xf = frag_x_split<T, P, !SM::RESCALED>(Xs, 32 * u + 4 * q, 32 * u + 16 + 4 * q, pt * 16, lane);
+                        const v8 xf = frag_x_split<T, P, SM::XSWZ>(Xs, 32 * u + 4 * q, 32 * u + 16 + 4 * q, pt * 16, lane);
                         acc[k][pt] = mma(acc[k][pt], xf, mf);
                     }
                 }
@@ -1300,7 +1316,7 @@ __global__ __launch_bounds__(kThreads, (out_min_blocks<T, P>())) void k_out(cons
                     const bool nv = (N % 32 == 0) || (nn < N);
                     v8 cf = zero8<T>();
                     if (nv) {
-                        cf = ld8(&Ct[i * LDN + nn]);
+                        cf = ld8(&Ct[SM::rc_off(i, nn)]);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) cf[e] = from_f<T>(to_f(cf[e]) * exp2f_fast(an2[nn + e] * csI));
                     }

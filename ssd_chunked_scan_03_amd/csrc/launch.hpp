@@ -145,8 +145,14 @@ int run(const RunArgs& a) {
 
     // the output kernel's LDS must fit one CU (160 KiB); checked before any launch
     const bool tab = a.diag && diag_uses_table(Q, P, N, sizeof(T));
+    // the diagonal decay's swizzled tiles where they fit one more work-group per CU (the
+    // kernel's registers allow at most 3)
+    const auto per_cu = [](size_t bytes) { const size_t n = (160 * 1024) / bytes; return n < 3 ? n : (size_t)3; };
+    const bool swzr = a.diag && !tab && sizeof(T) == 2 &&
+                      per_cu(OutSmem<T, P, N, true, false, true>::bytes(Q)) > per_cu(OutSmem<T, P, N, true>::bytes(Q));
     const size_t smem = !a.diag ? OutSmem<T, P, N, false>::bytes(Q)
                         : tab   ? OutSmem<T, P, N, true, true>::bytes(Q)
+                        : swzr  ? OutSmem<T, P, N, true, false, true>::bytes(Q)
                                 : OutSmem<T, P, N, true>::bytes(Q);
     if (smem > 160 * 1024) return 3;
 
@@ -228,8 +234,17 @@ int run(const RunArgs& a) {
                             (int)smem);
         k_out<T, P, N, true, true><<<g3, kThreads, smem, s>>>(x, Bm, Cm, cb, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);
     } else if (a.diag) {
-        hipFuncSetAttribute((const void*)k_out<T, P, N, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        k_out<T, P, N, true><<<g3, kThreads, smem, s>>>(x, Bm, Cm, nullptr, hin, a.A, a.D, a.cdt, y, a.T, H, G, Q, nc);
+        if (swzr) {
+            hipFuncSetAttribute((const void*)k_out<T, P, N, true, false, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+            k_out<T, P, N, true, false, true><<<g3, kThreads, smem, s>>>(x, Bm, Cm, nullptr, hin, a.A, a.D, a.cdt, y,
+                                                                         a.T, H, G, Q, nc);
+        } else {
+            hipFuncSetAttribute((const void*)k_out<T, P, N, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)smem);
+            k_out<T, P, N, true><<<g3, kThreads, smem, s>>>(x, Bm, Cm, nullptr, hin, a.A, a.D, a.cdt, y, a.T, H, G,
+                                                            Q, nc);
+        }
     } else if (launch_outs<T, P, N>(a, g3, s, x, Cm, cb, hin, y)) {
     } else {
         hipFuncSetAttribute((const void*)k_out<T, P, N, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
