@@ -181,8 +181,45 @@ def other_workloads(torch, ssd, stream, dev, headline, reps=10):
                         "decay": "diagonal" if w.diag else "scalar"}
             print(f"[bench] {key}: {ms:.4f} ms/step", file=sys.stderr, flush=True)
             del y, hT, ws
+        if w0.name == configs.LONG.name:
+            out[f"{w0.name}_seqlen_scaling"] = seqlen_scaling(torch, ssd, stream, dev, w0, d, reps)
         del d
     return out
+
+
+def seqlen_scaling(torch, ssd, stream, dev, w, d, reps):
+    """The long workload (batch 1) at its own chunk size over the first T tokens of the same
+    resident inputs, T = 8K .. the whole sequence: the forward's cost against T ("still
+    linear in T").  Each point: 3 untimed forwards, then `reps` timed one by one (warm)."""
+    b, H, P, N, G, Q = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    dcode = ssd.SSD_BF16 if w.dtype == "bf16" else ssd.SSD_F32
+    pts = {}
+    T = 8192
+    while T <= w.seqlen:
+        sl = {k: (d[k][:, :T] if d[k] is not None and k in ("x", "dt", "B", "C") else d[k]) for k in d}
+        assert all(v is None or v.is_contiguous() for v in sl.values())  # batch 1: leading slices
+        prob = ssd.make_problem(b, T, H, P, N, G, Q, dcode)
+        y = torch.empty_like(sl["x"])
+        hT = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(ssd.workspace_bytes(prob, w.diag), 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            ssd.scan_fwd_into(prob, w.diag, sl["x"], sl["dt"], sl["A"], sl["B"], sl["C"], sl["D"], sl["h0"], y, hT,
+                              ws, stream.cuda_stream)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        ms = stats(time_each(torch, stream, step, reps))["median_ms"]
+        pts[str(T)] = {"ms_per_step": ms, "tokens_per_s": round(b * T / (ms * 1e-3), 1)}
+        print(f"[bench] {w.name} T={T}: {ms:.4f} ms/step", file=sys.stderr, flush=True)
+        del y, hT, ws
+        T *= 2
+    ts = sorted(int(t) for t in pts)
+    lo, hi = ts[0], ts[-1]
+    return {"chunk": Q, "schedule": ssd.schedule_of(ssd.make_problem(b, hi, H, P, N, G, Q, dcode), w.diag),
+            "points": pts,
+            "time_ratio_last_over_first": round(pts[str(hi)]["ms_per_step"] / pts[str(lo)]["ms_per_step"], 3),
+            "token_ratio_last_over_first": hi // lo}
 
 
 def main():

@@ -346,8 +346,11 @@ __device__ __forceinline__ void cb_body(const T* __restrict__ Bm, const T* __res
     }
 }
 
+// dstate from which k_prep takes a whole 64-row block row of C B^T per work-group
+constexpr int kPrepRowN = 128;
+
 // One 64-row block row I of a chunk's C B^T (tiles J = 0 .. I, I < 4) for bfloat16 with
-// dstate >= kCbStageN: the block row's C rows are staged in LDS once and serve every
+// dstate >= kPrepRowN: the block row's C rows are staged in LDS once and serve every
 // tile; each tile's B rows are in flight while the previous tile computes.  Same
 // output as cb_body on each tile (the same products in the same order).  (Taking the
 // tiles in pairs, so that each C fragment read from LDS feeds two matrix-core steps,
@@ -356,7 +359,7 @@ template <int N>
 __device__ __forceinline__ void cb_row_body(const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
                                             bf16* __restrict__ cb, Rows rows, int G, int Q, int kg, int I, int g,
                                             bf16* __restrict__ cs) {
-    static_assert(N % 32 == 0 && N >= kCbStageN, "staged block rows");
+    static_assert(N % 32 == 0 && N >= kPrepRowN, "staged block rows");
     if (kg >= rows.total_chunks()) return;
     const int rr = rows.row_of(kg);
     const int c = kg - rows.kbase(rr);
@@ -415,9 +418,9 @@ __device__ __forceinline__ void cb_row_body(const bf16* __restrict__ Bm, const b
 }
 
 // C B^T work items of one chunk and group in k_prep: a block row per work-group where
-// the staged path applies (bfloat16, dstate >= kCbStageN), else one 64 x 64 tile each
+// the staged path applies (bfloat16, dstate >= kPrepRowN), else one 64 x 64 tile each
 template <typename T, int N>
-__host__ __device__ constexpr bool prep_cb_rows() { return sizeof(T) == 2 && N >= kCbStageN && N % 32 == 0; }
+__host__ __device__ constexpr bool prep_cb_rows() { return sizeof(T) == 2 && N >= kPrepRowN && N % 32 == 0; }
 template <typename T, int N>
 __host__ __device__ constexpr int prep_cb_tasks(int nb) { return prep_cb_rows<T, N>() ? nb : nb * (nb + 1) / 2; }
 
@@ -500,7 +503,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ dt,
                                                    T* __restrict__ cb, T* __restrict__ Bt, Rows rows, int G) {
     constexpr int nb = Q / 64, nslab = Q / 64;
     // one LDS buffer for whichever task the work-group runs
-    constexpr size_t s1 = cumsum_smem<Q>(), s2 = cb_smem<T, N>(), s3 = BT ? bt_smem<T, N>() : 0;
+    constexpr size_t s1 = cumsum_smem<Q>(), s3 = BT ? bt_smem<T, N>() : 0;
+    constexpr size_t s2 = prep_cb_rows<T, N>() ? (size_t)64 * (N + 8) * 2 : cb_smem<T, N>();
     constexpr size_t SB = s1 > s2 ? (s1 > s3 ? s1 : s3) : (s2 > s3 ? s2 : s3);
     __shared__ __attribute__((aligned(16))) unsigned char smem[SB];
     const int nh = (rows.H + kCumsumHeads - 1) / kCumsumHeads;
