@@ -10,8 +10,10 @@ read that flushes the caches (cold: the headline `value`); K back-to-back forwar
 timed the same way (warm, reported beside it).  The JSON line also carries the roofline
 of the dominant kernel (timed live inside a staged forward), its matrix-core rate, the
 HBM and matrix-core peaks measured on this GPU (a streaming copy and a dense matrix-core
-loop), per-kernel times, the other workloads timed briefly, the decode step and the
-backward pass at the same shape, and the fp64 oracle timed on this host's cores.
+loop), per-kernel times, the other workloads timed briefly (with the long workload's
+cost against sequence length over the first 8K..64K tokens of its inputs), the decode
+step and the backward pass at the same shape, and the fp64 oracle timed on this host's
+cores.
 """
 from __future__ import annotations
 
