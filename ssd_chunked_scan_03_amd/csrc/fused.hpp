@@ -22,11 +22,13 @@
 // 16-lane group hit disjoint banks), H_c 64 x N (chunks swizzled by row), three
 // per-chunk float tables.  Blocks are numbered so that the heads of one batch row
 // share an XCD (and its L2 copy of the per-chunk tables).
-// Wave priorities: the C B^T fragment loops of the output passes run at priority 2, the
-// state update at 1, the state terms and the chunk-boundary work (tables, barriers,
-// transfers) at 0.  With two or three work-groups per CU, a SIMD then issues first for
-// the wave that is in its fragment loop, and the other work-groups' state terms and
-// chunk boundaries fill the gaps: 302 -> 283 us at the 2.7B layer shape, bit-identical.
+// Wave priorities: the work between a chunk's closing barrier and the next chunk's top
+// barrier (the next x transfer and the next chunk's tables and H_c, which every wave of the
+// work-group waits for) runs at priority 3, the C B^T fragment loops of the output passes
+// at 2, the state update at 1 and the state terms at 0.  With two or three work-groups per
+// CU, a SIMD then issues first for the wave that gates its work-group's next barrier, then
+// for the one in its fragment loop, and the state terms fill the gaps: 302 -> 272 us at
+// the 2.7B layer shape, bit-identical.
 #pragma once
 
 #include "kernels.hpp"
@@ -216,6 +218,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
     for (int c = 0; c < nc; ++c) {
         const int64_t t0 = (int64_t)c * Q;
         __syncthreads();  // the chunk's tables and Hs are in place
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int a = 0; a < SN; ++a)
 #pragma unroll
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_fused(const bf16* __restrict__ 
         __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): the next cdt row has landed
         if (c + 1 < nc) issue_front(fr, c + 1, 0);
         __syncthreads();  // every wave is done with Xs, Hs and the tables of this chunk
-        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_s_setprio(3);  // the chunk boundary (see the header)
         if (c + 1 < nc) {
             dma_x(c + 1);
             stage_tables();
