@@ -75,7 +75,9 @@ typedef enum {
 
 /* Problem descriptor.  Supported: chunk in {64, 128, 256}; headdim in {16, 32, 64, 128};
  * dstate in {16, 32, 64, 128, 256}; any seqlen >= 0 (a ragged last chunk is allowed);
- * batch >= 0; nheads >= 1; ngroups >= 1 dividing nheads. */
+ * batch >= 0; nheads >= 1; ngroups >= 1 dividing nheads; launch-grid limits: batch and
+ * batch * ngroups at most 65535, ceil(nheads / 16) + 28 * ngroups at most 65535, nheads
+ * at most 2^20, batch * nheads * nchunks under 2^31 (else SSD_ERR_UNSUPPORTED). */
 typedef struct {
     int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
     int32_t dtype;  /* ssd_dtype */

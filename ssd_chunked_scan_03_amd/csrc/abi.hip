@@ -58,6 +58,9 @@ int check_problem(const ssd_problem* p) {
     // launch-grid limits: blocks per launch and the batch / group grid dimensions
     const int64_t nc = (p->seqlen + p->chunk - 1) / p->chunk;
     if (p->batch > 65535 || p->batch * p->ngroups > 65535) return SSD_ERR_UNSUPPORTED;
+    // the preparation launches' second grid dimension: ceil(nheads / 16) cumsum tasks plus
+    // at most 28 table tasks per group (the backward's, at chunk 256)
+    if ((p->nheads + 15) / 16 + 28 * p->ngroups > 65535) return SSD_ERR_UNSUPPORTED;
     if (p->nheads > (int64_t)1 << 20 || nc > (int64_t)1 << 24) return SSD_ERR_UNSUPPORTED;
     if (p->batch * p->nheads * (nc > 0 ? nc : 1) > 0x7fffffffLL) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;

@@ -33,9 +33,10 @@
 // k_bwd_x forms the per-token term from the fp32 accumulators of y - D x (recomputed)
 // and dx - D dy; k_bwd_dt takes the reverse running sum.
 //
-// Kernels, in launch order after the forward's k_cumsum, k_cb (both orientations), k_bt
-// (B and C), and the entering states H_c and final state hT (k_state + k_scan, or with
-// many (b, h) chains k_states walking each chain's chunks with the state in registers):
+// Kernels, in launch order after k_bprep (the forward's cumsum, C B^T in both
+// orientations, B^T and C^T per chunk, in one launch) and the entering states H_c and
+// final state hT (k_state + k_scan, or with many (b, h) chains k_states walking each
+// chain's chunks with the state in registers):
 //   k_state<ADJ>  adjoint chunk inputs S'_c                        -> states (reused)
 //   k_scan_rev    R_c per chunk, dh0, partials of <R_c, H_{c+1}>     -> rin, dh0, kpart
 //   k_bwd_x       dx, per-token decay term, D partial sums, per (b, h, c)
@@ -48,6 +49,52 @@
 #include "kernels.hpp"
 
 namespace ssd {
+
+// ---------------------------------------------------------------------------
+// k_bprep: the tables a backward pass rebuilds, in one launch (the forward's k_prep does
+// the same for its three).  They do not depend on one another, so one grid (chunks,
+// tasks) runs them side by side, each task the work one block of the separate kernel
+// does (the same arithmetic, so the same tables bit for bit):
+//   y in [0, nh)                          k_cumsum's work for heads 16 y .. 16 y + 15
+//   y in [nh, + npair G)                  k_cb's work, C B^T, block pair y % npair, group y / npair
+//   y in [nh + npair G, + npair G)        the same transposed (B C^T, the input gradient's operand)
+//   y in [nh + 2 npair G, + nslab G)      k_bt's work for B: B^T per chunk, and B by token if bcp
+//   y in [nh + 2 npair G + nslab G, ...)  the same for C: C^T, and C by token if ccp
+// (nh = ceil(H / 16), npair = nb (nb + 1) / 2 with nb = Q / 64, nslab = Q / 64.)
+// ---------------------------------------------------------------------------
+template <typename T, int N, int Q>
+__global__ __launch_bounds__(kThreads) void k_bprep(const float* __restrict__ dt, float* __restrict__ cdt,
+                                                    const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                                    T* __restrict__ cb, T* __restrict__ cbt, T* __restrict__ bt,
+                                                    T* __restrict__ ct, T* __restrict__ bcp, T* __restrict__ ccp,
+                                                    Rows rows, int G) {
+    constexpr int nb = Q / 64, npair = nb * (nb + 1) / 2, nslab = Q / 64;
+    constexpr size_t s1 = cumsum_smem<Q>(), s2 = cb_smem<T, N>(), s3 = bt_smem<T, N>();
+    constexpr size_t SB = s1 > s2 ? (s1 > s3 ? s1 : s3) : (s2 > s3 ? s2 : s3);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SB];
+    const int nh = (rows.H + kCumsumHeads - 1) / kCumsumHeads;
+    const int k = blockIdx.x;
+    int y = blockIdx.y;
+    if (y < nh) {
+        cumsum_body<Q>(dt, cdt, rows, k, y, reinterpret_cast<float(*)[Q + 1]>(smem));
+        return;
+    }
+    y -= nh;
+    if (y < 2 * npair * G) {
+        const bool tr = y >= npair * G;
+        const int t = tr ? y - npair * G : y;
+        if (tr) cb_body<T, N, true>(Bm, Cm, cbt, rows, G, Q, k, t % npair, t / npair, reinterpret_cast<T*>(smem));
+        else cb_body<T, N, false>(Bm, Cm, cb, rows, G, Q, k, t % npair, t / npair, reinterpret_cast<T*>(smem));
+        return;
+    }
+    y -= 2 * npair * G;
+    const bool isc = y >= nslab * G;
+    const int t = isc ? y - nslab * G : y;
+    T* cp = isc ? ccp : bcp;
+    const T* src = isc ? Cm : Bm;
+    bt_body<T, N>(src, isc ? ct : bt, cp ? src : nullptr, cp, rows, G, Q, k, (t % nslab) * 64, t / nslab,
+                  reinterpret_cast<T*>(smem));
+}
 
 // sum over the four lanes l16, l16 + 16, l16 + 32, l16 + 48 (one matrix-core column)
 __device__ __forceinline__ float sum_q(float v) {

@@ -115,22 +115,18 @@ int run_bwd(const BwdArgs& a) {
     rows.kcap = (int)(a.b * a.nc);
     const unsigned kc = (unsigned)rows.kcap;
 
-    // the forward's tables and entering states
-    const dim3 g1(kc, 1, (H + 15) / 16);
+    // the forward's tables (cdt, C B^T in both orientations, B^T and C^T per chunk; with
+    // a.bcp / a.ccp also B and C per chunk by token) in one launch, then the entering states
+    const int nb = Q / 64;
+    const dim3 gp(kc, (unsigned)((H + 15) / 16 + 2 * (nb * (nb + 1) / 2) * G + 2 * nb * G));
+    T* bcp = static_cast<T*>(a.bcp);
+    T* ccp = static_cast<T*>(a.ccp);
     switch (Q) {
-        case 64: k_cumsum<64><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
-        case 128: k_cumsum<128><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
-        case 256: k_cumsum<256><<<g1, kThreads, 0, s>>>(a.dt, a.cdt, rows); break;
+        case 64: k_bprep<T, N, 64><<<gp, kThreads, 0, s>>>(a.dt, a.cdt, Bm, Cm, cb, cbt, bt, ct, bcp, ccp, rows, G); break;
+        case 128: k_bprep<T, N, 128><<<gp, kThreads, 0, s>>>(a.dt, a.cdt, Bm, Cm, cb, cbt, bt, ct, bcp, ccp, rows, G); break;
+        case 256: k_bprep<T, N, 256><<<gp, kThreads, 0, s>>>(a.dt, a.cdt, Bm, Cm, cb, cbt, bt, ct, bcp, ccp, rows, G); break;
         default: return 3;
     }
-    const int nb = Q / 64;
-    const dim3 g2(kc, nb * (nb + 1) / 2, (unsigned)G);
-    k_cb<T, N, false><<<g2, kThreads, 0, s>>>(Bm, Cm, cb, rows, G, Q);
-    k_cb<T, N, true><<<g2, kThreads, 0, s>>>(Bm, Cm, cbt, rows, G, Q);
-    const dim3 g6(kc * (unsigned)(Q / 64), (unsigned)G);
-    // B^T and C^T per chunk; with a.bcp / a.ccp also B and C per chunk by token
-    k_bt<T, N><<<g6, kThreads, 0, s>>>(Bm, bt, a.bcp ? Bm : nullptr, static_cast<T*>(a.bcp), rows, G, Q);
-    k_bt<T, N><<<g6, kThreads, 0, s>>>(Cm, ct, a.ccp ? Cm : nullptr, static_cast<T*>(a.ccp), rows, G, Q);
     const dim3 g3((unsigned)(a.b * H * nc));
     const int per_head = (int)((a.P * a.N / 4 + kThreads - 1) / kThreads);
     int nvalid = (int)(a.P * a.N / 4 / 64);  // partials of <R_c, H_{c+1}> per chunk

@@ -181,6 +181,17 @@ def test_diag_table_path_workspace():
     assert ssd.diag_uses_table(256, 64, 128, ssd.SSD_BF16) and not ssd.diag_uses_table(128, 64, 64, ssd.SSD_BF16)
 
 
+def test_grid_limits_refused_on_the_host():
+    """Shapes whose preparation launch would exceed a grid dimension are refused before any
+    HIP call: ceil(nheads / 16) + 28 ngroups <= 65535 (the backward's table tasks at chunk
+    256), batch * ngroups <= 65535."""
+    ok = ssd.make_problem(1, 256, 2300, 64, 64, 2300, 256, ssd.SSD_BF16)  # 144 + 64400 tasks
+    assert ssd.workspace_bytes(ok) > 0 and ssd.bwd_workspace_bytes(ok) > 0
+    big = ssd.make_problem(1, 256, 2341 * 4, 64, 64, 2341, 256, ssd.SSD_BF16)  # 586 + 65548
+    assert ssd.workspace_bytes(big) == 0 and ssd.bwd_workspace_bytes(big) == 0
+    assert ssd.workspace_bytes(ssd.make_problem(2, 256, 65536, 64, 64, 32768, 64, ssd.SSD_BF16)) == 0
+
+
 def test_schedule_flags_validated():
     p = prob()
     p.flags = ssd.SCHEDULE_SPLIT | ssd.SCHEDULE_FUSED
