@@ -68,15 +68,36 @@ def trace_rows(path):
     return rows, res
 
 
+def dispatch_medians(path):
+    """Median duration (us) of each kernel's dispatches, from the per-dispatch rows of the
+    trace database's kernels view (duration column, else end - start, in ns); {} if the
+    view has neither."""
+    con = sqlite3.connect(_db(path))
+    cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
+    if "duration" in cols:
+        q = "select name, duration from kernels"
+    elif "start" in cols and "end" in cols:
+        q = 'select name, "end" - "start" from kernels'
+    else:
+        return {}
+    per = {}
+    for name, d in con.execute(q):
+        if d is not None:
+            per.setdefault(name, []).append(float(d))
+    return {name: statistics.median(v) / 1e3 for name, v in per.items()}
+
+
 def cmd_trace(args):
     rows, res = trace_rows(args.dir)
     print(f"Command (from the repository root on one MI355X):\n\n    {args.command}\n")
     print(f"Kernel sources hash: `{kernel_source_hash()}`\n")
-    print("| kernel | calls | avg us | total us | share | grid x | LDS B | VGPR | AGPR | SGPR | scratch B |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    med = dispatch_medians(args.dir)
+    print("| kernel | calls | avg us | median us | total us | share | grid x | LDS B | VGPR | AGPR | SGPR | scratch B |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
     for short, full, calls, total, avg, pct in rows:
         g = res.get(full, ("", "", "", "", "", ""))
-        print(f"| {short} | {calls} | {avg:.2f} | {total:.1f} | {pct:.1f}% | {g[0]} | {g[1]} | {g[2]} | {g[3]} | "
+        m = f"{med[full]:.2f}" if full in med else "—"
+        print(f"| {short} | {calls} | {avg:.2f} | {m} | {total:.1f} | {pct:.1f}% | {g[0]} | {g[1]} | {g[2]} | {g[3]} | "
               f"{g[4]} | {g[5]} |")
 
 
